@@ -1,0 +1,114 @@
+"""Python handle on the plain CPU oracle (``oracle/oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: the tests, the package smoke check and the
+benchmark's CPU-baseline leg are the only callers. The GPU path neither
+imports nor links anything here, and nothing here touches the GPU path.
+
+The oracle is the sort-based definition of top-k / top-p that the Qrita
+summary says its output matches ("Resultados"; "Contribuciones Clave" 1):
+stable descending order by value with ties by ascending index, top-k prefix,
+then the minimal rank prefix whose float64 softmax mass reaches p.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile ``oracle.c`` into ``liboracle.so`` with gcc; returns the path."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread",
+                               "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB):
+                build(force=True)
+            lib = ctypes.CDLL(_LIB)
+            vp, i64, i32p = ctypes.c_void_p, ctypes.c_int64, ctypes.POINTER(ctypes.c_int32)
+            lib.oracle_select.restype = ctypes.c_int
+            lib.oracle_select.argtypes = [vp, i64, i64, ctypes.c_int, vp, vp, vp, vp, i64, vp,
+                                          vp, vp, ctypes.c_int, ctypes.POINTER(i64),
+                                          ctypes.POINTER(i64)]
+            lib.oracle_hardware_threads.restype = ctypes.c_int
+            _lib = lib
+        return _lib
+
+
+def hardware_threads() -> int:
+    return int(_load().oracle_hardware_threads())
+
+
+class OracleInputError(ValueError):
+    pass
+
+
+@dataclass
+class OracleResult:
+    mask: np.ndarray      # uint8 [B, V]
+    idx: np.ndarray       # int32 [B, idx_cap]; entries past min(count, idx_cap) are -1
+    count: np.ndarray     # int32 [B]
+    band_lo: np.ndarray   # int32 [B]
+    band_hi: np.ndarray   # int32 [B]
+
+    @property
+    def band_rows(self) -> np.ndarray:
+        return np.nonzero(self.band_lo != self.band_hi)[0]
+
+
+def select(logits: np.ndarray, dtype: str, k: Optional[np.ndarray], p: Optional[np.ndarray],
+           idx_cap: int, nthreads: int = 0, want_mask: bool = True) -> OracleResult:
+    """Run the oracle on host arrays.
+
+    logits: [B, V] float32 (dtype "f32") or uint16 bf16 bits (dtype "bf16").
+    k: int32 [B] or None (top-k off); p: float32 [B] or None (top-p off).
+    """
+    lib = _load()
+    if dtype == "f32":
+        x = np.ascontiguousarray(logits, dtype=np.float32)
+        dt = 0
+    elif dtype == "bf16":
+        x = np.ascontiguousarray(logits, dtype=np.uint16)
+        dt = 1
+    else:
+        raise ValueError(f"unknown dtype {dtype!r}")
+    B, V = x.shape
+    kk = None if k is None else np.ascontiguousarray(k, dtype=np.int32)
+    pp = None if p is None else np.ascontiguousarray(p, dtype=np.float32)
+    mask = np.empty((B, V), np.uint8) if want_mask else None
+    idx = np.full((B, max(idx_cap, 0)), -1, np.int32)
+    count = np.empty(B, np.int32)
+    lo = np.empty(B, np.int32)
+    hi = np.empty(B, np.int32)
+    bad_r, bad_c = ctypes.c_int64(-1), ctypes.c_int64(-1)
+
+    def ptr(a):
+        return None if a is None else a.ctypes.data
+
+    rc = lib.oracle_select(ptr(x), B, V, dt, ptr(kk), ptr(pp), ptr(mask),
+                           ptr(idx) if idx_cap > 0 else None, int(idx_cap), ptr(count), ptr(lo),
+                           ptr(hi), int(nthreads), ctypes.byref(bad_r), ctypes.byref(bad_c))
+    if rc == 2:
+        raise OracleInputError(f"NaN or +inf logit at row {bad_r.value}, column {bad_c.value}")
+    if rc != 0:
+        raise RuntimeError(f"oracle_select failed with status {rc}")
+    return OracleResult(mask, idx, count, lo, hi)

@@ -1,0 +1,224 @@
+/*
+ * Plain CPU oracle for exact top-k / top-p candidate-set selection.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing in the product path may include, link,
+ * load or call this file; only the tests, the package smoke check and the
+ * benchmark's CPU-baseline leg use it. It shares no code with the GPU path.
+ *
+ * What it computes. The Qrita summary (gist.science, "Qrita - Top-k y Top-p de
+ * alto rendimiento..." / its Korean translation) states that the method
+ * returns the full candidate set with the exact semantics of sort-based top-k
+ * and top-p ("Declaración del Problema"; "Contribuciones Clave" 1), that the
+ * pivot keeps exactly k elements at or above it ("Metodología" §2), that the
+ * number of retained boundary duplicates is fixed deterministically (§2,
+ * "Condición de Terminación"), and that the output matches sort-based
+ * algorithms ("Resultados"). The oracle is therefore that sort-based
+ * definition written out, not the pivot algorithm:
+ *
+ *   1. decode each logit exactly to double (bf16: bits << 16 as float);
+ *      NaN and +inf are rejected, -inf is an ordinary value;
+ *   2. order the indices by value descending, equal values by ascending
+ *      index (-0.0 and +0.0 are equal values);
+ *   3. top-k: K = V if k <= 0 or k >= V, else k; keep ranks 0..K-1;
+ *   4. top-p (only when p < 1, p taken as the float the caller passes):
+ *      p <= 0 keeps 1; otherwise with m the rank-0 value,
+ *      e_r = exp(z_r - m) for r < K, S = sum e_r (sequential, rank order),
+ *      cum_r = sum_{s<=r} e_s / S (sequential); keep 1 + min{r: cum_r >= p}
+ *      ranks (K if no r qualifies); an all -inf row keeps 1;
+ *   5. mask[i] = rank(i) < L; idx[j] = index of rank j, j < min(L, idx_cap);
+ *      count = L.
+ *
+ * Boundary band (top-p rows): L_lo / L_hi are the cuts for p - 1e-5 and
+ * p + 1e-5 (same rule, clamped to [1, K]). A row is a band row iff they
+ * differ; there a GPU result must be a rank prefix with length in
+ * [L_lo, L_hi]. For other rows band_lo = band_hi = L.
+ *
+ * Top-k before top-p, with top-p renormalised over the top-k set, is the
+ * composition of the sort-based samplers Qrita replaces; the pages do not
+ * spell it out.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <unistd.h>
+
+typedef struct {
+    double v;
+    int64_t i;
+} oracle_item;
+
+/* value descending, then index ascending: a total order, so the sorted
+ * sequence is unique whatever sort routine produces it. */
+static int cmp_desc(const void *pa, const void *pb) {
+    const oracle_item *a = (const oracle_item *)pa;
+    const oracle_item *b = (const oracle_item *)pb;
+    if (a->v > b->v) return -1;
+    if (a->v < b->v) return 1;
+    return (a->i < b->i) ? -1 : (a->i > b->i);
+}
+
+static double decode(const void *logits, int dtype, int64_t off) {
+    if (dtype == 0) {
+        return (double)((const float *)logits)[off];
+    }
+    uint32_t u = ((uint32_t)((const uint16_t *)logits)[off]) << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* smallest L in [1, K] with cum_{L-1} >= target, else K */
+static int64_t prefix_cut(const double *cum, int64_t K, double target) {
+    for (int64_t r = 0; r < K; ++r)
+        if (cum[r] >= target) return r + 1;
+    return K;
+}
+
+typedef struct {
+    const void *logits;
+    int64_t batch, vocab;
+    int dtype;
+    const int32_t *k;
+    const float *p;
+    uint8_t *mask;
+    int32_t *idx;
+    int64_t idx_cap;
+    int32_t *count;
+    int32_t *band_lo, *band_hi;
+    int64_t row_begin, row_end;
+    int status;
+    int64_t bad_row, bad_col;
+} oracle_job;
+
+static void *run_rows(void *arg) {
+    oracle_job *J = (oracle_job *)arg;
+    const int64_t V = J->vocab;
+    oracle_item *items = (oracle_item *)malloc((size_t)V * sizeof(oracle_item));
+    double *cum = (double *)malloc((size_t)V * sizeof(double));
+    double *e = (double *)malloc((size_t)V * sizeof(double));
+    if (!items || !cum || !e) {
+        J->status = 3;
+        free(items); free(cum); free(e);
+        return NULL;
+    }
+    for (int64_t b = J->row_begin; b < J->row_end; ++b) {
+        /* 1. decode */
+        for (int64_t i = 0; i < V; ++i) {
+            double x = decode(J->logits, J->dtype, b * V + i);
+            if (isnan(x) || x == INFINITY) {
+                J->status = 2;
+                J->bad_row = b;
+                J->bad_col = i;
+                goto done;
+            }
+            items[i].v = x;
+            items[i].i = i;
+        }
+        /* 2. order */
+        qsort(items, (size_t)V, sizeof(oracle_item), cmp_desc);
+        /* 3. top-k */
+        int64_t kb = J->k ? (int64_t)J->k[b] : 0;
+        int64_t K = (kb <= 0 || kb >= V) ? V : kb;
+        int64_t L = K, L_lo = K, L_hi = K;
+        /* 4. top-p */
+        double p = J->p ? (double)J->p[b] : 1.0;
+        if (p < 1.0) {
+            if (p <= 0.0) {
+                L = L_lo = L_hi = 1;
+            } else if (items[0].v == -INFINITY) {
+                L = L_lo = L_hi = 1;
+            } else {
+                const double m = items[0].v;
+                double S = 0.0;
+                for (int64_t r = 0; r < K; ++r) {
+                    e[r] = exp(items[r].v - m);
+                    S += e[r];
+                }
+                double c = 0.0;
+                for (int64_t r = 0; r < K; ++r) {
+                    c += e[r] / S;
+                    cum[r] = c;
+                }
+                L = prefix_cut(cum, K, p);
+                L_lo = prefix_cut(cum, K, p - 1e-5);
+                L_hi = prefix_cut(cum, K, p + 1e-5);
+            }
+        }
+        /* 5. outputs */
+        if (J->mask) {
+            uint8_t *mrow = J->mask + b * V;
+            memset(mrow, 0, (size_t)V);
+            for (int64_t r = 0; r < L; ++r) mrow[items[r].i] = 1;
+        }
+        if (J->idx) {
+            int64_t n = L < J->idx_cap ? L : J->idx_cap;
+            for (int64_t r = 0; r < n; ++r) J->idx[b * J->idx_cap + r] = (int32_t)items[r].i;
+        }
+        if (J->count) J->count[b] = (int32_t)L;
+        if (J->band_lo) J->band_lo[b] = (int32_t)L_lo;
+        if (J->band_hi) J->band_hi[b] = (int32_t)L_hi;
+    }
+done:
+    free(items);
+    free(cum);
+    free(e);
+    return NULL;
+}
+
+int oracle_hardware_threads(void) {
+    long n = sysconf(_SC_NPROCESSORS_ONLN);
+    return n > 0 ? (int)n : 1;
+}
+
+/*
+ * Select over `batch` rows of `vocab` logits (dtype 0 = float32, 1 = bf16 bits).
+ * k, p: per-row controls (either may be NULL: that control is off).
+ * mask [batch][vocab] uint8, idx [batch][idx_cap] int32, count [batch],
+ * band_lo / band_hi [batch]: outputs, each may be NULL.
+ * nthreads <= 0 uses every online core; rows are split in contiguous blocks.
+ * Returns 0 on success, 1 for bad arguments, 2 if a NaN or +inf logit was
+ * found (its row/column in *bad_row / *bad_col), 3 on allocation failure.
+ */
+int oracle_select(const void *logits, int64_t batch, int64_t vocab, int dtype,
+                  const int32_t *k, const float *p, uint8_t *mask, int32_t *idx,
+                  int64_t idx_cap, int32_t *count, int32_t *band_lo, int32_t *band_hi,
+                  int nthreads, int64_t *bad_row, int64_t *bad_col) {
+    if (!logits || batch < 0 || vocab <= 0 || vocab > INT32_MAX || (dtype != 0 && dtype != 1) ||
+        idx_cap < 0)
+        return 1;
+    if (batch == 0) return 0;
+    if (nthreads <= 0) nthreads = oracle_hardware_threads();
+    if (nthreads > batch) nthreads = (int)batch;
+    oracle_job *jobs = (oracle_job *)calloc((size_t)nthreads, sizeof(oracle_job));
+    pthread_t *th = (pthread_t *)calloc((size_t)nthreads, sizeof(pthread_t));
+    if (!jobs || !th) {
+        free(jobs); free(th);
+        return 3;
+    }
+    for (int t = 0; t < nthreads; ++t) {
+        oracle_job *J = &jobs[t];
+        J->logits = logits; J->batch = batch; J->vocab = vocab; J->dtype = dtype;
+        J->k = k; J->p = p; J->mask = mask; J->idx = idx; J->idx_cap = idx_cap;
+        J->count = count; J->band_lo = band_lo; J->band_hi = band_hi;
+        J->row_begin = batch * t / nthreads;
+        J->row_end = batch * (t + 1) / nthreads;
+        J->status = 0;
+        J->bad_row = J->bad_col = -1;
+    }
+    for (int t = 1; t < nthreads; ++t) pthread_create(&th[t], NULL, run_rows, &jobs[t]);
+    run_rows(&jobs[0]);
+    for (int t = 1; t < nthreads; ++t) pthread_join(th[t], NULL);
+    int status = 0;
+    for (int t = 0; t < nthreads && status == 0; ++t) {
+        if (jobs[t].status) {
+            status = jobs[t].status;
+            if (bad_row) *bad_row = jobs[t].bad_row;
+            if (bad_col) *bad_col = jobs[t].bad_col;
+        }
+    }
+    free(jobs);
+    free(th);
+    return status;
+}
