@@ -1,0 +1,246 @@
+"""Benchmark: exact top-k / top-p candidate-set selection on one MI355X.
+
+One step = one qrita_select call over one batch of a named synthetic workload
+(both kernels of the path: the streaming truncation pass and the per-row
+tail). The headline line is the 64 x 128256 bf16 workload; the other
+bandwidth workloads are reported in "per_config".
+
+Timing: W warmup steps, then K steps between two HIP events on the stream the
+library launches on, after a device synchronize. Inputs rotate over enough
+buffer sets to keep the footprint above 1 GiB so the 256 MiB Infinity Cache
+cannot serve them. A second loop with an event between the two kernels gives
+each kernel's average duration (the roofline numbers). The outputs of the
+last timed call are checked against the CPU oracle, which is then timed on a
+bounded sample of the same workload as the CPU baseline.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+METRIC = "rows/sec and effective HBM GB/s (% of peak) for exact top-k/top-p masks"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def to_device(x, dev):
+    import torch
+
+    if x.dtype == "bf16":
+        return torch.from_numpy(x.logits.view(np.int16)).to(dev).view(torch.bfloat16)
+    return torch.from_numpy(x.logits).to(dev)
+
+
+def bench_config(index, steps, warmup, rotate_bytes):
+    import torch
+
+    import top_selection_sigma_amd as q
+    import workloads as w
+
+    dev = torch.device("cuda", 0)
+    t0 = time.time()
+    x = w.make_config(index)
+    log(f"[bench] workload {index} {x.name}: generated in {time.time() - t0:.1f}s")
+    B, V = x.batch, x.vocab
+    es = 2 if x.dtype == "bf16" else 4
+    idx_cap = int(max(64, x.k.max()))
+    logits0 = to_device(x, dev)
+    k = torch.from_numpy(x.k).to(dev)
+    p = torch.from_numpy(x.p).to(dev)
+    set_bytes = B * V * (es + 1) + B * idx_cap * 4
+    nsets = max(2, math.ceil(rotate_bytes / set_bytes))
+    sets = []
+    for i in range(nsets):
+        lg = logits0 if i == 0 else logits0.clone()
+        sets.append((lg, torch.empty((B, V), dtype=torch.uint8, device=dev),
+                     torch.empty((B, idx_cap), dtype=torch.int32, device=dev),
+                     torch.empty(B, dtype=torch.int32, device=dev)))
+    ws = q.workspace_for(B, V, q.dtype_code(logits0), idx_cap, dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i, opts=None):
+        lg, m, ix, c = sets[i % nsets]
+        q.qrita_select_ex(lg, k, p, m, ix, c, idx_cap, ws, stream, opts)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(steps):
+        step(warmup + i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = ev0.elapsed_time(ev1)
+    last = (warmup + steps - 1) % nsets
+
+    # per-kernel durations: an event between the two launches of every call
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    mids = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for e in mids:
+        e.record(stream)  # create the underlying hipEvent before handing it over
+    torch.cuda.synchronize()
+    for i in range(steps):
+        starts[i].record(stream)
+        step(i, q.Options(mid_event=mids[i]))
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    pass1_ms = float(np.mean([s.elapsed_time(m) for s, m in zip(starts, mids)]))
+    tail_ms = float(np.mean([m.elapsed_time(e) for m, e in zip(mids, ends)]))
+
+    res = dict(index=index, name=x.name, batch=B, vocab=V, dtype=x.dtype, steps=steps,
+               warmup=warmup, rotation_sets=nsets, ms_per_step=total_ms / steps,
+               pass1_ms=pass1_ms, tail_ms=tail_ms)
+    lg, m, ix, c = sets[last]
+    count = c.cpu().numpy()
+    kept_idx = np.minimum(count, idx_cap).astype(np.int64).sum()
+    eff_bytes = B * V * es + B * V + 4 * kept_idx + 4 * B
+    sec = res["ms_per_step"] * 1e-3
+    res["rows_per_s"] = B / sec
+    res["effective_gbps"] = eff_bytes / sec / 1e9
+    res["pct_peak_hbm"] = 100.0 * res["effective_gbps"] / PEAK_HBM_GBS
+    res["pass1_alg_bytes"] = B * V * (es + 1)
+    res["pass1_gbps"] = res["pass1_alg_bytes"] / (pass1_ms * 1e-3) / 1e9
+    res["mean_count"] = float(count.mean())
+    res["_inputs"] = x
+    res["_gpu"] = (m.cpu().numpy(), ix.cpu().numpy(), count, idx_cap)
+    return res
+
+
+def oracle_leg(res):
+    """CPU oracle on the same host arrays: checks the last timed call's outputs."""
+    import oracle
+
+    x = res["_inputs"]
+    mask, idx, count, idx_cap = res["_gpu"]
+    t1 = time.time()
+    ref = oracle.select(x.logits, x.dtype, x.k, x.p, idx_cap)
+    band = ref.band_lo != ref.band_hi
+    bad = np.zeros(x.batch, bool)
+    bad |= ~band & (count != ref.count)
+    bad |= ~band & np.any(mask != ref.mask, axis=1)
+    for b in range(x.batch):
+        n = min(int(count[b]), idx_cap)
+        if not band[b] and not np.array_equal(idx[b, :n], ref.idx[b, :n]):
+            bad[b] = True
+        if band[b] and not (ref.band_lo[b] <= count[b] <= ref.band_hi[b]):
+            bad[b] = True
+    res["parity"] = dict(mismatch_rows=int(bad.sum()), band_rows=int(band.sum()),
+                         oracle_s=round(time.time() - t1, 2))
+    log(f"[bench] {x.name}: parity mismatches {int(bad.sum())}, band rows {int(band.sum())}")
+
+
+def cpu_baseline(x, idx_cap, target_s=10.0):
+    """The oracle, as it stands, on all host cores over whole batches of the
+    headline workload until about target_s seconds of work."""
+    import oracle
+
+    threads = oracle.hardware_threads()
+    rows = 0
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        oracle.select(x.logits, x.dtype, x.k, x.p, idx_cap, nthreads=threads)
+        rows += x.batch
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= target_s or reps >= 1000:
+            break
+    return dict(value=rows / el, unit="rows/s", cores=threads, kind="oracle",
+                sample=f"{reps} passes over the full {x.batch}-row batch ({el:.1f}s wall)")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=1)
+    ap.add_argument("--others", default="2,3,4", help="extra workloads for per_config ('' = none)")
+    ap.add_argument("--rotate-gib", type=float, default=1.0)
+    ap.add_argument("--no-check", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(--gpus must be 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import top_selection_sigma_amd as q
+
+    q.lib()
+    torch.cuda.init()
+    rot = int(args.rotate_gib * (1 << 30))
+    head = bench_config(args.config, args.steps, args.warmup, rot)
+    others = []
+    for s in [t for t in args.others.split(",") if t.strip()]:
+        i = int(s)
+        if i != args.config:
+            others.append(bench_config(i, args.steps, args.warmup, rot))
+    # oracle leg: parity of every timed workload, then the CPU baseline
+    per = {}
+    for r in [head] + others:
+        if not args.no_check:
+            oracle_leg(r)
+    for r in others:
+        r.pop("_inputs")
+        r.pop("_gpu")
+        per[r["name"]] = {kk: (round(v, 4) if isinstance(v, float) else v) for kk, v in r.items()}
+    x = head.pop("_inputs")
+    head.pop("_gpu")
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(x, int(max(64, x.k.max())), args.cpu_seconds)
+    dev_name = torch.cuda.get_device_name(0)
+    line = {
+        "metric": METRIC,
+        "value": round(head["rows_per_s"], 1),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": head["dtype"],
+        "data": "synthetic",
+        "config": {"workload": head["name"], "batch": head["batch"], "vocab": head["vocab"],
+                   "logits": head["dtype"], "k": "per-row U{1..1024}", "p": "per-row U[0.5,1)",
+                   "outputs": "uint8 mask + int32 indices + counts"},
+        "effective_gbps": round(head["effective_gbps"], 1),
+        "pct_peak_hbm": round(head["pct_peak_hbm"], 2),
+        "roofline": {
+            "kernel": "pass1_kernel (sample stats, single-pass truncation, mask fill)",
+            "bound": "hbm",
+            "achieved": round(head["pass1_gbps"], 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(head["pass1_gbps"] / PEAK_HBM_GBS, 4),
+            "traffic": None,
+            "pass1_us": round(head["pass1_ms"] * 1e3, 3),
+            "tail_us": round(head["tail_ms"] * 1e3, 3),
+            "alg_bytes_per_launch": head["pass1_alg_bytes"],
+        },
+        "cpu_baseline": cpu,
+        "parity": head.get("parity"),
+        "per_config": per,
+        "device": dev_name,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

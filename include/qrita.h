@@ -1,0 +1,164 @@
+/*
+ * qrita.h - exact, deterministic top-k / top-p candidate-set selection over
+ * large-vocabulary logits on AMD MI355X (gfx950).
+ *
+ * The operation is the one the Qrita summary (gist.science paper 2602.01518,
+ * Spanish and Korean pages) describes for an LLM sampler: for every row of
+ * logits, return the full top-k / top-p candidate set with the exact
+ * semantics of sort-based top-k and top-p ("Declaración del Problema";
+ * "Contribuciones Clave" 1 and 4), computed by Gaussian sigma-truncation
+ * ("Metodología" §1), a quaternary pivot search with duplicate tracking
+ * (§2) and a duplicate-handling mask ("Detalles de Implementación",
+ * Pipeline).
+ *
+ * Semantics per row b (V = vocab):
+ *   - Order: value descending; equal values (including -0.0 == +0.0 and
+ *     -inf == -inf) by ascending vocabulary index. This is the order a stable
+ *     descending sort produces, and it fixes which boundary duplicates are
+ *     kept (the pages require a deterministic count, §2).
+ *   - Top-k: K = k[b] if 0 < k[b] < V, otherwise top-k is off (K = V).
+ *     Exactly K tokens are kept (§2: exactly k elements at or above the
+ *     pivot).
+ *   - Top-p: on iff p[b] < 1 (NaN means off). p[b] <= 0 keeps one token.
+ *     Otherwise the kept set is the shortest rank prefix of the top-k set
+ *     whose softmax mass, renormalised over the top-k set, is >= p[b].
+ *     Masses are formed in float64 fixed point on the GPU; on rows whose
+ *     cumulative mass at the cut lies within 1e-5 of p the cut may differ from
+ *     an exact float64 computation by the ranks inside that band.
+ *   - An all -inf row keeps one token when top-p is on.
+ *   Logits must be finite or -inf; NaN and +inf give unspecified (but
+ *   memory-safe) output.
+ *
+ * All pointers are device pointers owned by the caller. Calls are
+ * asynchronous on `stream` (a hipStream_t; NULL is the default stream),
+ * allocate nothing, do not synchronise, and launch two kernels in stream
+ * order: the single streaming pass over the logits and a per-row tail.
+ * Argument errors are reported before anything is launched or written.
+ */
+#ifndef QRITA_H
+#define QRITA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of the logits. */
+typedef enum {
+    QRITA_F32 = 0,  /* IEEE float32 */
+    QRITA_BF16 = 1  /* bfloat16 (upper half of a float32) */
+} qrita_dtype_t;
+
+/* Return codes. */
+typedef enum {
+    QRITA_OK = 0,
+    QRITA_EINVAL = 1,      /* bad argument: nothing launched, nothing written */
+    QRITA_EWORKSPACE = 2,  /* workspace NULL or smaller than qrita_workspace_bytes() */
+    QRITA_ELAUNCH = 3,     /* the HIP runtime reported an error at launch */
+    QRITA_EUNSUPPORTED = 4 /* the current device cannot run this library */
+} qrita_status_t;
+
+/*
+ * Bytes of device workspace qrita_select needs for this shape. The workspace
+ * holds a 64-byte header per row and a per-row overflow list of candidates
+ * (at most min(vocab, 16384) entries of 8 bytes): O(batch) memory, against the
+ * O(batch * vocab) value+index buffers a full sort needs (the summary reports
+ * about 50 % lower memory than sort-based selection, "Resultados").
+ * Returns 0 for an invalid shape.
+ */
+size_t qrita_workspace_bytes(int64_t batch, int64_t vocab, int dtype, int64_t idx_cap);
+
+/*
+ * Zero-fill `bytes` of workspace on `stream`. A workspace must be zero-filled
+ * once before its first use; every completed qrita_select call leaves it
+ * zero-filled again, so it can be reused by later calls of any shape that
+ * fits. Two calls sharing one workspace must not overlap in time.
+ * Returns QRITA_EINVAL for a NULL pointer, QRITA_ELAUNCH on launch failure.
+ */
+int qrita_workspace_init(void* workspace, size_t bytes, void* stream);
+
+/*
+ * Select the top-k / top-p candidate set of every row.
+ *
+ * logits     device, [batch][vocab] contiguous rows of `dtype`; 16-byte aligned.
+ * batch      rows (>= 0; 0 is a no-op).
+ * vocab      logits per row, 1 .. 2^31 - 1.
+ * dtype      QRITA_F32 or QRITA_BF16.
+ * k          device int32 [batch], or NULL (top-k off for all rows).
+ * p          device float32 [batch], or NULL (top-p off for all rows).
+ * out_mask   device uint8 [batch][vocab]: 1 = kept, 0 = dropped; or NULL.
+ *            16-byte aligned.
+ * out_idx    device int32 [batch][idx_cap]: the first min(count, idx_cap)
+ *            kept indices in rank order (value descending, index ascending);
+ *            later entries of each row are left untouched. Or NULL.
+ * out_count  device int32 [batch]: number of kept tokens. Required when
+ *            out_idx is given; may be NULL otherwise.
+ * idx_cap    row stride of out_idx (>= 0).
+ * workspace  device scratch of at least qrita_workspace_bytes(...) bytes,
+ *            zero-filled before first use (see qrita_workspace_init).
+ * stream     hipStream_t to launch on (NULL = default stream).
+ *
+ * At least one of out_mask, out_idx, out_count must be non-NULL.
+ * Returns QRITA_OK, QRITA_EINVAL, QRITA_EWORKSPACE or QRITA_ELAUNCH.
+ */
+int qrita_select(const void* logits, int64_t batch, int64_t vocab, int dtype,
+                 const int32_t* k, const float* p,
+                 uint8_t* out_mask, int32_t* out_idx, int32_t* out_count, int64_t idx_cap,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Options for qrita_select_ex: ablation and test controls. None of them can
+ * change a selection result; they only change how it is reached.
+ *   force_miss   nonzero: no truncation survivors, every row takes the
+ *                full-row fallback (the summary's truncation miss, §1).
+ *   delta_scale  multiplies the table delta (0 means 1).
+ *   pivot_mode   0: pivots at 25/50/75 % of the key range (§2);
+ *                1: the same fractions of the value range.
+ *   slices       workgroups per row (0 = automatic tier).
+ *   lds_cap      candidate capacity in LDS per workgroup (0 = automatic;
+ *                otherwise clamped to [64, automatic]).
+ *   list_cap     per-row overflow-list capacity (0 = automatic; otherwise
+ *                clamped to [1, automatic]).
+ *   diag         device int32 [batch][QRITA_DIAG_FIELDS] or NULL: per-row
+ *                diagnostics, see QRITA_DIAG_* below.
+ *   mid_event    a hipEvent_t or NULL: recorded on the stream between the
+ *                streaming pass and the per-row tail, for per-stage timing.
+ */
+typedef struct {
+    int32_t force_miss;
+    float delta_scale;
+    int32_t pivot_mode;
+    int32_t slices;
+    int32_t lds_cap;
+    int32_t list_cap;
+    int32_t* diag;
+    void* mid_event;
+} qrita_options;
+
+#define QRITA_DIAG_FIELDS 8
+#define QRITA_DIAG_T 0          /* Gaussian threshold mu + delta*sigma (float bits) */
+#define QRITA_DIAG_TC 1         /* threshold used for collection (float bits) */
+#define QRITA_DIAG_NT 2         /* #{z >= Gaussian threshold}, or -1 if unknown */
+#define QRITA_DIAG_NCAND 3      /* candidates collected in the single pass */
+#define QRITA_DIAG_PATH 4       /* 0 LDS, 1 overflow list, 2 list after re-collection, 3 full row */
+#define QRITA_DIAG_HIT 5        /* 1 if the Gaussian threshold alone was a truncation hit */
+#define QRITA_DIAG_ITERS 6      /* pivot-search iterations spent on the row */
+#define QRITA_DIAG_PREDICTED 7  /* 1 if the sample predicted a miss and lowered the threshold */
+
+/* qrita_select with options (opt may be NULL: same as qrita_select). */
+int qrita_select_ex(const void* logits, int64_t batch, int64_t vocab, int dtype,
+                    const int32_t* k, const float* p,
+                    uint8_t* out_mask, int32_t* out_idx, int32_t* out_count, int64_t idx_cap,
+                    void* workspace, size_t workspace_bytes, void* stream,
+                    const qrita_options* opt);
+
+/* Static description of a status code. */
+const char* qrita_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QRITA_H */

@@ -1,0 +1,151 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Small shapes span several pass-1 tiles (256 threads x 16 logits) and ragged
+tails; the named workloads run at their full sizes with every row checked.
+"""
+import numpy as np
+import pytest
+
+import workloads as w
+from parity import check, oracle_for, run_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+KINDS = ["gauss", "gauss_outliers", "ties16", "uniform", "heavy", "equal", "twolevel", "smallint",
+         "neginf", "allneginf", "zeros", "ascending", "descending", "spike", "flat"]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("V", [1, 2, 17, 63, 64, 65, 1000, 4097, 12345, 40000])
+def test_small_shapes_all_kinds(dtype, V):
+    for i, kind in enumerate(KINDS):
+        B = 3 if V > 10000 else 9
+        x = w.make_rows(B, V, dtype, kind, seed=100 + V * 31 + i)
+        cap = min(V, 300)
+        _say(f"case {kind} V={V} {dtype}")
+        g = run_gpu(x, cap)
+        check(x, g, oracle_for(x, cap), cap, f"{kind} V={V} {dtype}")
+
+
+@pytest.mark.parametrize("B", [1, 3, 130])
+def test_batch_shapes(B):
+    x = w.make_rows(B, 5000, "bf16", "gauss_outliers", seed=B)
+    g = run_gpu(x, 128)
+    check(x, g, oracle_for(x, 128), 128, f"B={B}")
+
+
+@pytest.mark.parametrize("index", [0, 1, 2, 3, 4])
+def test_named_workload_full_size(index):
+    x = w.make_config(index)
+    cap = int(max(64, x.k.max()))
+    _say(f"workload {index} {x.name} B={x.batch} V={x.vocab} cap={cap}")
+    g = run_gpu(x, cap)
+    ref = oracle_for(x, cap)
+    band = check(x, g, ref, cap, x.name)
+    _say(f"  band rows {len(band)}; paths {np.bincount(g.diag[:, 4], minlength=4).tolist()}")
+
+
+def test_uniform_rows_take_the_fallback_and_match():
+    """U(-1,1) rows defeat the Gaussian threshold (a truncation miss)."""
+    x = w.make_config(3, rows=range(16))
+    g = run_gpu(x, 4096)
+    check(x, g, oracle_for(x, 4096), 4096, "uniform")
+    miss = g.diag[:, 5] == 0
+    assert miss.sum() >= 12            # the Gaussian threshold alone misses on most rows
+    assert np.all(g.diag[miss, 7] == 1)  # and the sample predicted every miss
+    assert np.all(g.diag[:, 4] <= 1)     # served from the single pass, no re-read
+
+
+@pytest.mark.parametrize("kind", ["gauss_outliers", "ties16", "heavy", "uniform"])
+def test_forced_miss_takes_full_row_fallback(kind):
+    import top_selection_sigma_amd as q
+
+    x = w.make_rows(6, 20000, "bf16", kind, seed=7)
+    g = run_gpu(x, 256, options=q.Options(force_miss=True))
+    check(x, g, oracle_for(x, 256), 256, f"force_miss {kind}")
+    assert np.all(g.diag[:, 4] >= 2)
+
+
+@pytest.mark.parametrize("scale", [0.25, 0.5, 2.0, 4.0, -1.0])
+def test_delta_scale_does_not_change_results(scale):
+    import top_selection_sigma_amd as q
+
+    x = w.make_rows(8, 30000, "f32", "gauss_outliers", seed=11)
+    base = run_gpu(x, 200)
+    g = run_gpu(x, 200, options=q.Options(delta_scale=scale))
+    assert np.array_equal(g.mask, base.mask) and np.array_equal(g.count, base.count)
+    check(x, g, oracle_for(x, 200), 200, f"delta {scale}")
+
+
+def test_value_space_pivots_match_key_space():
+    import top_selection_sigma_amd as q
+
+    x = w.make_rows(8, 30000, "bf16", "ties16", seed=12)
+    a = run_gpu(x, 100)
+    b = run_gpu(x, 100, options=q.Options(pivot_mode=1))
+    assert np.array_equal(a.mask, b.mask) and np.array_equal(a.count, b.count)
+    assert np.array_equal(a.idx, b.idx)
+
+
+@pytest.mark.parametrize("slices", [1, 2, 3, 7, 16])
+def test_tiers_match_oracle(slices):
+    import top_selection_sigma_amd as q
+
+    x = w.make_rows(5, 50000, "bf16", "gauss_outliers", seed=13)
+    g = run_gpu(x, 300, options=q.Options(slices=slices))
+    check(x, g, oracle_for(x, 300), 300, f"slices {slices}")
+
+
+@pytest.mark.parametrize("lds_cap,list_cap", [(64, 0), (64, 100), (300, 50), (0, 1)])
+def test_small_capacities_reach_every_path(lds_cap, list_cap):
+    import top_selection_sigma_amd as q
+
+    x = w.make_rows(6, 9000, "f32", "gauss_outliers", seed=14)
+    g = run_gpu(x, 9000, options=q.Options(lds_cap=lds_cap, list_cap=list_cap))
+    check(x, g, oracle_for(x, 9000), 9000, f"caps {lds_cap}/{list_cap}")
+
+
+def test_keep_all_rows_full_order():
+    x = w.make_rows(4, 6000, "bf16", "ties16", seed=15, k=0, p=1.0)
+    g = run_gpu(x, 6000)
+    ref = oracle_for(x, 6000)
+    check(x, g, ref, 6000, "keep-all")
+    assert np.all(g.mask == 1) and np.all(g.count == 6000)
+
+
+@pytest.mark.parametrize("cap", [0, 1, 7, 1000])
+def test_idx_cap_variants(cap):
+    x = w.make_rows(6, 3000, "f32", "smallint", seed=16)
+    g = run_gpu(x, cap, want_idx=cap > 0)
+    check(x, g, oracle_for(x, cap), cap, f"cap {cap}")
+
+
+def test_count_only_and_mask_only():
+    x = w.make_rows(6, 3000, "bf16", "gauss", seed=17)
+    ref = oracle_for(x, 0)
+    g = run_gpu(x, 0, want_mask=False, want_idx=False)
+    assert np.array_equal(g.count[ref.band_lo == ref.band_hi], ref.count[ref.band_lo == ref.band_hi])
+
+
+def test_repeated_calls_are_bitwise_identical():
+    x = w.make_rows(32, 70000, "bf16", "ties16", seed=18)
+    first = run_gpu(x, 500)
+    for _ in range(4):
+        g = run_gpu(x, 500)
+        assert np.array_equal(g.mask, first.mask)
+        assert np.array_equal(g.idx, first.idx)
+        assert np.array_equal(g.count, first.count)
+
+
+def test_workspace_reuse_across_shapes():
+    """Each call leaves the workspace zeroed, so shapes can change between calls."""
+    for i, (B, V, dt) in enumerate([(40, 9000, "f32"), (3, 70000, "bf16"), (64, 128256, "bf16"),
+                                    (1, 5, "f32"), (40, 9000, "f32")]):
+        x = w.make_rows(B, V, dt, "gauss_outliers", seed=40 + i)
+        g = run_gpu(x, 64)
+        check(x, g, oracle_for(x, 64), 64, f"reuse {B}x{V}")
