@@ -63,7 +63,7 @@ typedef enum {
 /*
  * Bytes of device workspace qrita_select needs for this shape. The workspace
  * holds a 64-byte header per row and a per-row overflow list of candidates
- * (at most min(vocab, 16384) entries of 8 bytes): O(batch) memory, against the
+ * (at most min(vocab, 32768) entries of 8 bytes): O(batch) memory, against the
  * O(batch * vocab) value+index buffers a full sort needs (the summary reports
  * about 50 % lower memory than sort-based selection, "Resultados").
  * Returns 0 for an invalid shape.

@@ -1,5 +1,5 @@
 // Device helpers shared by the selection kernels: order-preserving keys,
-// candidate encoding, fixed-point softmax mass, and wave/block reductions.
+// candidate encoding, fixed-point softmax mass, and DPP wave reductions.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -19,7 +19,7 @@ constexpr int kMaxWaves = 16;
 // to +0.0 first so the two zeros are one value (the pages count equal logits
 // as duplicates, "Metodología" §2). bf16 logits use the key of their exact
 // float32 widening, so one search handles both dtypes. -inf has the smallest
-// key of any non-NaN value.
+// key of any non-NaN value, and every non-NaN key is nonzero.
 // ---------------------------------------------------------------------------
 QRITA_DEV uint32_t f32_key(uint32_t bits) {
     bits = (bits == 0x80000000u) ? 0u : bits;
@@ -61,53 +61,108 @@ QRITA_DEV uint64_t fx_from_unit_f32(float e) {
     return ((uint64_t)hi << 32) | lo;
 }
 
-QRITA_DEV uint64_t fx_from_unit_f64(double e) {
-    return (uint64_t)(e * 0x1p44);
+// exp(z - m) for a candidate key against the row maximum m, as a float.
+// y = (z - m) * log2(e) is formed in float64 (z - m is exact there) and split
+// into an integer i <= 0 and a fraction f in [0, 1); the hardware exp2 gives
+// 2^f to about one float ulp and ldexp applies 2^i exactly. Relative error
+// about 1e-7. The value is a deterministic function of (key, m).
+QRITA_DEV float mass_f32(uint32_t key, float m) {
+    const float z = key_value(key);
+    if (z == -__builtin_inff()) return 0.0f;
+    const double y = ((double)z - (double)m) * 1.4426950408889634;
+    const double fl = floor(y);
+    if (fl < -160.0) return 0.0f;
+    return ldexpf(__builtin_amdgcn_exp2f((float)(y - fl)), (int)fl);
 }
 
-// exp(z - m) in float64 for a candidate key against the row maximum m.
-QRITA_DEV uint64_t mass_fx(uint32_t key, float m) {
-    float z = key_value(key);
-    if (z == -__builtin_inff()) return 0;
-    double d = (double)z - (double)m;  // exact: both operands are floats
-    return fx_from_unit_f64(exp(d));
-}
+// Fixed-point softmax mass of a candidate key, floor(exp(z - m) * 2^44).
+QRITA_DEV uint64_t mass_fx(uint32_t key, float m) { return fx_from_unit_f32(mass_f32(key, m)); }
 
 // ---------------------------------------------------------------------------
-// Wave reductions (wave64). Integer reductions are exact, so the shuffle order
-// is immaterial; the float sum uses a fixed butterfly so every lane ends with
-// the same bits.
+// Wave reductions (wave64) with DPP: row shifts within each 16-lane row, then
+// row broadcasts across rows; lane 63 ends with the whole wave's value. No
+// LDS traffic and no dependence on lane order for these exact integer ops.
 // ---------------------------------------------------------------------------
-QRITA_DEV uint32_t wave_sum_u32(uint32_t x) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) x += (uint32_t)__shfl_xor((int)x, o);
-    return x;
+template <int CTRL, int ROWMASK>
+QRITA_DEV uint32_t dpp_mov(uint32_t old, uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)x, CTRL, ROWMASK, 0xF, false);
 }
+constexpr int kShr1 = 0x111, kShr2 = 0x112, kShr4 = 0x114, kShr8 = 0x118;
+constexpr int kBcast15 = 0x142, kBcast31 = 0x143;
+
+QRITA_DEV uint32_t readlane(uint32_t x, int lane) {
+    return (uint32_t)__builtin_amdgcn_readlane((int)x, lane);
+}
+
+#define QRITA_ROW_STEPS(OP, ID)                         \
+    x = OP(x, dpp_mov<kShr1, 0xF>(ID, x));              \
+    x = OP(x, dpp_mov<kShr2, 0xF>(ID, x));              \
+    x = OP(x, dpp_mov<kShr4, 0xF>(ID, x));              \
+    x = OP(x, dpp_mov<kShr8, 0xF>(ID, x));
+#define QRITA_WAVE_STEPS(OP, ID)                        \
+    QRITA_ROW_STEPS(OP, ID)                             \
+    x = OP(x, dpp_mov<kBcast15, 0xA>(ID, x));           \
+    x = OP(x, dpp_mov<kBcast31, 0xC>(ID, x));
+
+QRITA_DEV uint32_t op_min(uint32_t a, uint32_t b) { return a < b ? a : b; }
+QRITA_DEV uint32_t op_max(uint32_t a, uint32_t b) { return a > b ? a : b; }
+QRITA_DEV uint32_t op_add(uint32_t a, uint32_t b) { return a + b; }
+
+// Whole-wave reductions; the result is wave-uniform.
 QRITA_DEV uint32_t wave_min_u32(uint32_t x) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        uint32_t y = (uint32_t)__shfl_xor((int)x, o);
-        x = y < x ? y : x;
-    }
-    return x;
+    QRITA_WAVE_STEPS(op_min, 0xFFFFFFFFu)
+    return readlane(x, 63);
 }
 QRITA_DEV uint32_t wave_max_u32(uint32_t x) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        uint32_t y = (uint32_t)__shfl_xor((int)x, o);
-        x = y > x ? y : x;
-    }
-    return x;
+    QRITA_WAVE_STEPS(op_max, 0u)
+    return readlane(x, 63);
+}
+QRITA_DEV uint32_t wave_sum_u32(uint32_t x) {
+    QRITA_WAVE_STEPS(op_add, 0u)
+    return readlane(x, 63);
+}
+// Reductions over lanes 0..15 only (lane 15 holds the result).
+QRITA_DEV uint32_t row_min_u32(uint32_t x) {
+    QRITA_ROW_STEPS(op_min, 0xFFFFFFFFu)
+    return readlane(x, 15);
+}
+QRITA_DEV uint32_t row_max_u32(uint32_t x) {
+    QRITA_ROW_STEPS(op_max, 0u)
+    return readlane(x, 15);
+}
+QRITA_DEV uint32_t row_sum_u32(uint32_t x) {
+    QRITA_ROW_STEPS(op_add, 0u)
+    return readlane(x, 15);
+}
+
+template <int CTRL, int ROWMASK>
+QRITA_DEV void add64_step(uint32_t& lo, uint32_t& hi) {
+    const uint32_t blo = dpp_mov<CTRL, ROWMASK>(0u, lo);
+    const uint32_t bhi = dpp_mov<CTRL, ROWMASK>(0u, hi);
+    const uint32_t nlo = lo + blo;
+    hi = hi + bhi + (nlo < lo ? 1u : 0u);
+    lo = nlo;
 }
 QRITA_DEV uint64_t wave_sum_u64(uint64_t x) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)x, o);
-        uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(x >> 32), o);
-        x += ((uint64_t)hi << 32) | lo;
-    }
-    return x;
+    uint32_t lo = (uint32_t)x, hi = (uint32_t)(x >> 32);
+    add64_step<kShr1, 0xF>(lo, hi);
+    add64_step<kShr2, 0xF>(lo, hi);
+    add64_step<kShr4, 0xF>(lo, hi);
+    add64_step<kShr8, 0xF>(lo, hi);
+    add64_step<kBcast15, 0xA>(lo, hi);
+    add64_step<kBcast31, 0xC>(lo, hi);
+    return ((uint64_t)readlane(hi, 63) << 32) | readlane(lo, 63);
 }
+QRITA_DEV uint64_t row_sum_u64(uint64_t x) {
+    uint32_t lo = (uint32_t)x, hi = (uint32_t)(x >> 32);
+    add64_step<kShr1, 0xF>(lo, hi);
+    add64_step<kShr2, 0xF>(lo, hi);
+    add64_step<kShr4, 0xF>(lo, hi);
+    add64_step<kShr8, 0xF>(lo, hi);
+    return ((uint64_t)readlane(hi, 15) << 32) | readlane(lo, 15);
+}
+
+// Float sum with a fixed butterfly (every lane ends with the same bits).
 QRITA_DEV float wave_sum_f32(float x) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
@@ -119,7 +174,5 @@ QRITA_DEV uint32_t lanes_below(uint64_t mask) {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
                                      __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
-
-QRITA_DEV uint32_t lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
 
 }  // namespace qrita

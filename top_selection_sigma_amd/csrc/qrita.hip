@@ -13,7 +13,10 @@ namespace {
 using qrita::Params;
 
 constexpr int64_t kHeaderBytes = qrita::H_WORDS * 4;
-constexpr int64_t kListMax = 16384;
+constexpr int64_t kListMax = 32768;
+// tail workgroup: one wave per SIMD, with the row's candidates in 128 KiB of LDS
+constexpr int kTailThreads = 256;
+constexpr int kTailLdsEntries = 16384;
 
 int64_t list_stride_for(int64_t vocab) { return std::min<int64_t>(vocab, kListMax); }
 
@@ -56,16 +59,16 @@ Tier choose_tier(int64_t B, int64_t V, const qrita_options* o) {
     t.slices = (int)S;
     t.slice_len = (int)L;
     int stage = 2048;
-    int tail = 8192;
+    int tail = kTailLdsEntries;
     if (o && o->lds_cap > 0) {
         stage = std::max(64, std::min(stage, (int)o->lds_cap));
         tail = std::max(64, std::min(tail, (int)o->lds_cap));
     }
     t.stage_cap = stage;
     t.stage_alloc = std::max(stage, qrita::kSampleN);
-    t.tail_threads = 512;
+    t.tail_threads = kTailThreads;
     t.tail_cap = tail;
-    t.tail_alloc = (int)next_pow2(std::max(tail, qrita::kSampleN));
+    t.tail_alloc = kTailLdsEntries;
     int64_t lc = list_stride_for(V);
     if (o && o->list_cap > 0) lc = std::max<int64_t>(1, std::min<int64_t>(lc, o->list_cap));
     t.list_cap = (int)lc;
@@ -73,8 +76,8 @@ Tier choose_tier(int64_t B, int64_t V, const qrita_options* o) {
 }
 
 // Dynamic LDS above 64 KiB must be enabled per kernel; the largest request is
-// the tail's 8192-entry candidate store (64 KiB) next to its static LDS.
-constexpr int kMaxDynLds = 96 * 1024;
+// the tail's 16384-entry candidate store (128 KiB) next to its static LDS.
+constexpr int kMaxDynLds = 128 * 1024;
 
 template <class Kern>
 hipError_t allow_lds(Kern kern, std::once_flag& once, hipError_t& err) {
@@ -164,7 +167,7 @@ int select_impl(const void* logits, int64_t batch, int64_t vocab, int dtype, con
     if (opt && opt->mid_event) {
         if (hipEventRecord((hipEvent_t)opt->mid_event, s) != hipSuccess) return QRITA_ELAUNCH;
     }
-    err = bf16 ? launch_tail<512, true>(P, t, s) : launch_tail<512, false>(P, t, s);
+    err = bf16 ? launch_tail<kTailThreads, true>(P, t, s) : launch_tail<kTailThreads, false>(P, t, s);
     return err == hipSuccess ? QRITA_OK : QRITA_ELAUNCH;
 }
 
