@@ -153,6 +153,27 @@ QRITA_DEV uint64_t wave_sum_u64(uint64_t x) {
     add64_step<kBcast31, 0xC>(lo, hi);
     return ((uint64_t)readlane(hi, 63) << 32) | readlane(lo, 63);
 }
+// Wave total of the fixed-point masses hi * 2^22 + lo held per lane as
+// 32-bit half sums (each below 2^27): 16-lane row sums stay within 32 bits,
+// the cross-row steps run in 64 bits.
+QRITA_DEV uint64_t wave_sum_split(uint32_t hi, uint32_t lo) {
+    {
+        uint32_t x = hi;
+        QRITA_ROW_STEPS(op_add, 0u)
+        hi = x;
+    }
+    {
+        uint32_t x = lo;
+        QRITA_ROW_STEPS(op_add, 0u)
+        lo = x;
+    }
+    const uint64_t v = ((uint64_t)hi << 22) + lo;
+    uint32_t vl = (uint32_t)v, vh = (uint32_t)(v >> 32);
+    add64_step<kBcast15, 0xA>(vl, vh);
+    add64_step<kBcast31, 0xC>(vl, vh);
+    return ((uint64_t)readlane(vh, 63) << 32) | readlane(vl, 63);
+}
+
 QRITA_DEV uint64_t row_sum_u64(uint64_t x) {
     uint32_t lo = (uint32_t)x, hi = (uint32_t)(x >> 32);
     add64_step<kShr1, 0xF>(lo, hi);
@@ -167,6 +188,53 @@ QRITA_DEV float wave_sum_f32(float x) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
     return x;
+}
+
+// 1 if f > p, else 0, in vector ALU operations only (a saturating subtract
+// and a minimum; the minimum is kept as written so the compiler does not turn
+// it back into a compare and a lane-mask select).
+QRITA_DEV uint32_t gt01(uint32_t f, uint32_t p) {
+    uint32_t d = __builtin_elementwise_sub_sat(f, p);
+    asm("v_min_u32 %0, 1, %0" : "+v"(d));
+    return d;
+}
+QRITA_DEV uint32_t ne01(uint32_t a, uint32_t b) {
+    uint32_t d = a ^ b;
+    asm("v_min_u32 %0, 1, %0" : "+v"(d));
+    return d;
+}
+
+// A softmax mass e in [0, 1] as floor(e * 2^44) = hi * 2^22 + lo with
+// hi, lo < 2^22 + 1 (both exact; the same value as fx_from_unit_f32). Sums of
+// up to 512 such halves fit 32 bits.
+QRITA_DEV void fx_split(float e, uint32_t& hi, uint32_t& lo) {
+    hi = (uint32_t)(e * 0x1p22f);
+    lo = (uint32_t)fmaf((float)hi, -0x1p22f, e * 0x1p44f);
+}
+
+// threadIdx.x behind an optimisation barrier: address and mask arithmetic
+// derived from it is recomputed where it is used, instead of being hoisted to
+// kernel entry and held in registers for the whole kernel.
+QRITA_DEV uint32_t tid_here() {
+    uint32_t t = threadIdx.x;
+    asm volatile("" : "+v"(t));
+    return t;
+}
+// first thread of this thread's wave, as a wave-uniform (scalar) value
+QRITA_DEV uint32_t wave_base_here() { return __builtin_amdgcn_readfirstlane(tid_here() & ~(uint32_t)(kWave - 1)); }
+
+// Barrier over the NT threads that run a step: the workgroup barrier, or for
+// a step run by one wave alone a fence that completes its LDS accesses (the
+// lanes of a wave run in lockstep, and other waves are not waiting).
+template <int NT>
+QRITA_DEV void block_sync() {
+    if (NT > kWave) {
+        __syncthreads();
+    } else {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    }
 }
 
 // Number of set bits of `mask` in lanes below this lane.

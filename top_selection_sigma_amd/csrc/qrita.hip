@@ -14,9 +14,12 @@ using qrita::Params;
 
 constexpr int64_t kHeaderBytes = qrita::H_WORDS * 4;
 constexpr int64_t kListMax = 32768;
-// tail workgroup: one wave per SIMD, with the row's candidates in 128 KiB of LDS
-constexpr int kTailThreads = 256;
-constexpr int kTailLdsEntries = 16384;
+// tail workgroup: two waves per SIMD; up to 32 candidate keys per thread in
+// registers (16384 per row) with their indices in LDS, and an LDS buffer of
+// 8192 candidates for sorting (larger kept sets are sorted in windows)
+constexpr int kTailThreads = 512;
+constexpr int kTailRegCap = kTailThreads * qrita::kTailR;
+constexpr int kTailLdsEntries = 8192;
 
 int64_t list_stride_for(int64_t vocab) { return std::min<int64_t>(vocab, kListMax); }
 
@@ -27,8 +30,8 @@ struct Tier {
     int stage_cap;    // pass 1 LDS candidate stage
     int stage_alloc;  // pass 1 LDS entries (>= the 2048-entry sample)
     int tail_threads;
-    int tail_cap;     // tail: candidates kept in LDS
-    int tail_alloc;   // tail LDS entries (power of two)
+    int tail_cap;     // tail: largest list searched in registers
+    int tail_alloc;   // tail LDS entries for sorting (power of two)
     int list_cap;
 };
 
@@ -59,7 +62,7 @@ Tier choose_tier(int64_t B, int64_t V, const qrita_options* o) {
     t.slices = (int)S;
     t.slice_len = (int)L;
     int stage = 2048;
-    int tail = kTailLdsEntries;
+    int tail = kTailRegCap;
     if (o && o->lds_cap > 0) {
         stage = std::max(64, std::min(stage, (int)o->lds_cap));
         tail = std::max(64, std::min(tail, (int)o->lds_cap));
@@ -76,7 +79,7 @@ Tier choose_tier(int64_t B, int64_t V, const qrita_options* o) {
 }
 
 // Dynamic LDS above 64 KiB must be enabled per kernel; the largest request is
-// the tail's 16384-entry candidate store (128 KiB) next to its static LDS.
+// the tail's sort buffer and index store (128 KiB) next to its static LDS.
 constexpr int kMaxDynLds = 128 * 1024;
 
 template <class Kern>
@@ -106,7 +109,7 @@ hipError_t launch_tail(const Params& P, const Tier& t, hipStream_t stream) {
     static std::once_flag once;
     static hipError_t attr = hipSuccess;
     if (allow_lds(kern, once, attr) != hipSuccess) return attr;
-    const size_t lds = (size_t)t.tail_alloc * sizeof(uint64_t);
+    const size_t lds = (size_t)t.tail_alloc * sizeof(uint64_t) + (size_t)kTailRegCap * sizeof(uint32_t);
     hipLaunchKernelGGL(kern, dim3((unsigned)P.batch), dim3(THREADS), lds, stream, P);
     return hipGetLastError();
 }
