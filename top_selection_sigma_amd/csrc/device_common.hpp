@@ -183,6 +183,31 @@ QRITA_DEV uint64_t row_sum_u64(uint64_t x) {
     return ((uint64_t)readlane(hi, 15) << 32) | readlane(lo, 15);
 }
 
+// Float wave sum with DPP steps in a fixed order (the result is the same on
+// every call for the same lane values).
+QRITA_DEV float wave_sum_f32_dpp(float v) {
+    uint32_t x = __float_as_uint(v);
+#define QRITA_FADD(CTRL, RM)                                                                         \
+    x = __float_as_uint(__uint_as_float(x) + __uint_as_float(dpp_mov<CTRL, RM>(0u, x)));
+    QRITA_FADD(kShr1, 0xF)
+    QRITA_FADD(kShr2, 0xF)
+    QRITA_FADD(kShr4, 0xF)
+    QRITA_FADD(kShr8, 0xF)
+    QRITA_FADD(kBcast15, 0xA)
+    QRITA_FADD(kBcast31, 0xC)
+#undef QRITA_FADD
+    return __uint_as_float(readlane(x, 63));
+}
+
+// Exclusive suffix sum over lanes: lane l gets the sum of lanes l+1 .. 63.
+QRITA_DEV uint32_t wave_suffix_sum_excl(uint32_t v) {
+    // inclusive prefix sum of the lanes in reverse order
+    const uint32_t tot = wave_sum_u32(v);
+    uint32_t x = v;
+    QRITA_WAVE_STEPS(op_add, 0u)
+    return tot - x;  // x = inclusive prefix sum up to this lane
+}
+
 // Float sum with a fixed butterfly (every lane ends with the same bits).
 QRITA_DEV float wave_sum_f32(float x) {
 #pragma unroll

@@ -53,7 +53,8 @@ Tier choose_tier(int64_t B, int64_t V, const qrita_options* o) {
     S = std::min<int64_t>(S, 64);
     S = std::min<int64_t>(S, std::max<int64_t>(1, (V + 8191) / 8192));
     if (o && o->slices > 0) S = std::min<int64_t>(o->slices, std::max<int64_t>(1, V));
-    t.threads = (S == 1 && V >= 65536) ? 512 : 256;
+    // 256-thread workgroups: 1024 of them stay resident together on 256 CUs
+    t.threads = 256;
     const int64_t TB = (int64_t)t.threads * 16;
     int64_t L = (V + S - 1) / S;
     L = ((L + TB - 1) / TB) * TB;

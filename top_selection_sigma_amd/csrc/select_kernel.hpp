@@ -82,10 +82,16 @@ constexpr int kTieDirect = 256;  // tie groups up to this size are ranked direct
 constexpr int kTailR = 32;       // tail: candidates per thread held in registers
 constexpr int kWaveR = 32;       // tail, one-wave mode: candidates per lane (2048 per row)
 
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kHistBins = 256;  // pass 1: sample histogram for the miss prediction
+
 struct Shared {
     alignas(16) uint32_t slot[2][kMaxWaves][16];  // per-wave partial records, double-buffered
     uint32_t ties[kTieDirect];
-    float fred[kMaxWaves];
+    uint32_t hist[kHistBins];
+    float fred[2 * kMaxWaves];
     uint32_t ncand;
     uint32_t flags;
     uint32_t gather_n;
@@ -1081,14 +1087,38 @@ QRITA_DEV int lut_k_index(float ratio) {
 }
 
 // Load the row's sample into registers: 8 chunks of 256 consecutive logits at
-// evenly spaced offsets (the whole row when it has at most 2048 logits).
+// evenly spaced offsets (the whole row when it has at most 2048 logits). A
+// thread's 8 logits are consecutive; away from the row's ends each run is
+// moved down to a 16-byte boundary and read with vector loads.
 template <bool BF16>
 QRITA_DEV void load_sample(const void* rowp, int32_t V, float x[8], bool in[8]) {
     const int tid = threadIdx.x;
     const bool whole = V <= kSampleN;
-    const int64_t pos0 =
+    int64_t pos0 =
         whole ? (int64_t)tid * 8
               : ((int64_t)(tid >> 5) * (int64_t)(V - kSampleChunk)) / (kSampleChunks - 1) + (int64_t)(tid & 31) * 8;
+    constexpr int64_t ES = BF16 ? 2 : 4;
+    const int64_t mis = (int64_t)(((uintptr_t)rowp / ES + (uint64_t)pos0) & (BF16 ? 7 : 3));
+    if (!whole && tid < kSampleN / 8 && pos0 >= mis && pos0 - mis + 8 <= V) {
+        pos0 -= mis;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) in[i] = true;
+        if (BF16) {
+            const u32x4_t w = *(const u32x4_t*)((const uint16_t*)rowp + pos0);
+            const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                x[2 * r] = __uint_as_float(ws[r] << 16);
+                x[2 * r + 1] = __uint_as_float(ws[r] & 0xFFFF0000u);
+            }
+        } else {
+            const f32x4_t a = *(const f32x4_t*)((const float*)rowp + pos0);
+            const f32x4_t b = *(const f32x4_t*)((const float*)rowp + pos0 + 4);
+            x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+            x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int64_t e = pos0 + i;
@@ -1128,48 +1158,53 @@ QRITA_DEV Thresh compute_threshold(const Params& P, const RowMode& md, const voi
     if (!md.need_cand) return th;
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int32_t V = P.vocab;
+    for (int i = threadIdx.x; i < kHistBins; i += THREADS) sh.hist[i] = 0u;
     float x[8];
     bool in[8];
     load_sample<BF16>(rowp, V, x, in);
-    // mean over finite sample values, fixed reduction order
-    float sum = 0.0f;
-    uint32_t nf = 0;
+    // mean, variance and range of the finite sample values in one reduction
+    // (moments about the row's first logit, fixed reduction order)
+    float c0 = load_value<BF16>(rowp, 0);
+    c0 = __builtin_isfinite(c0) ? c0 : 0.0f;
+    float s1 = 0.0f, s2 = 0.0f;
+    uint32_t nf = 0, kmn = 0xFFFFFFFFu, kmx = 0u;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const bool ok = in[i] && __builtin_isfinite(x[i]);
-        sum += ok ? x[i] : 0.0f;
+        const float d = ok ? x[i] - c0 : 0.0f;
+        s1 += d;
+        s2 += d * d;
         nf += ok ? 1u : 0u;
+        const uint32_t k = f32_key(__float_as_uint(x[i]));
+        kmn = ok && k < kmn ? k : kmn;
+        kmx = ok && k > kmx ? k : kmx;
     }
-    sum = wave_sum_f32(sum);
+    s1 = wave_sum_f32_dpp(s1);
+    s2 = wave_sum_f32_dpp(s2);
     nf = wave_sum_u32(nf);
-    if (lane == 0) {
-        sh.fred[wave] = sum;
-        sh.slot[rb][wave][0] = nf;
-    }
+    kmn = wave_min_u32(kmn);
+    kmx = wave_max_u32(kmx);
+    if (lane == 0) *(uint4*)sh.slot[rb][wave] = make_uint4(__float_as_uint(s1), __float_as_uint(s2), nf, 0u);
+    if (lane == 0) *(uint2*)&sh.slot[rb][wave][4] = make_uint2(kmn, kmx);
     __syncthreads();
-    float tot = 0.0f;
+    float t1 = 0.0f, t2 = 0.0f;
     uint32_t n = 0;
+    kmn = 0xFFFFFFFFu;
+    kmx = 0u;
     for (int w = 0; w < NW; ++w) {
-        tot += sh.fred[w];
-        n += sh.slot[rb][w][0];
+        const uint4 q = *(const uint4*)sh.slot[rb][w];
+        const uint2 r = *(const uint2*)&sh.slot[rb][w][4];
+        t1 += __uint_as_float(q.x);
+        t2 += __uint_as_float(q.y);
+        n += q.z;
+        kmn = r.x < kmn ? r.x : kmn;
+        kmx = r.y > kmx ? r.y : kmx;
     }
     rb ^= 1;
-    __syncthreads();
-    const float mu = n ? tot / (float)n : 0.0f;
-    float d2 = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const bool ok = in[i] && __builtin_isfinite(x[i]);
-        const float d = x[i] - mu;
-        d2 += ok ? d * d : 0.0f;
-    }
-    d2 = wave_sum_f32(d2);
-    if (lane == 0) sh.fred[wave] = d2;
-    __syncthreads();
-    float var = 0.0f;
-    for (int w = 0; w < NW; ++w) var += sh.fred[w];
-    __syncthreads();
-    const float sigma = n ? sqrtf(var / (float)n) : 0.0f;
+    const float m1 = n ? t1 / (float)n : 0.0f;
+    const float mu = c0 + m1;
+    const float var = n ? fmaxf(t2 / (float)n - m1 * m1, 0.0f) : 0.0f;
+    const float sigma = sqrtf(var);
     const uint32_t ns = (uint32_t)min(V, kSampleN);
     th.n_s = ns;
     float t;
@@ -1196,24 +1231,50 @@ QRITA_DEV Thresh compute_threshold(const Params& P, const RowMode& md, const voi
     // values at or above the K_t-th largest logit of the row, and with the
     // table's factor-2 target about 2 * lambda values >= t. Fewer than
     // 1.25 * lambda + 2 suggests t lies above that logit (a truncation miss);
-    // then collect down to a sample order statistic instead, so the miss is
-    // served from the same single pass.
+    // then collect down to about the r-th largest sample value instead
+    // (r = lambda + 5 sqrt(lambda) + 5), so the miss is served from the same
+    // single pass. That value is read off a 256-bin histogram of the sample
+    // over its range: the lower edge of the bin where the count from the top
+    // reaches r, less half a bin, is at or below the r-th largest value.
     if (md.K_t > 0 && n >= 2 && __builtin_isfinite(t)) {
+        const float lo = key_value(kmn), hi = key_value(kmx);
+        const float w = (hi - lo) * (1.0f / kHistBins);
+        const float inv = w > 0.0f ? 1.0f / w : 0.0f;
         uint32_t c = 0;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) c += (in[i] && x[i] >= t) ? 1u : 0u;
+        for (int i = 0; i < 8; ++i) {
+            const bool ok = in[i] && __builtin_isfinite(x[i]);
+            c += (ok && x[i] >= t) ? 1u : 0u;
+            if (ok) {
+                const int b = (int)fminf(fmaxf((x[i] - lo) * inv, 0.0f), (float)(kHistBins - 1));
+                atomicAdd(&sh.hist[b], 1u);
+            }
+        }
         c = wave_sum_u32(c);
         if (lane == 0) sh.slot[rb][wave][0] = c;
         __syncthreads();
         uint32_t ct = 0;
-        for (int w = 0; w < NW; ++w) ct += sh.slot[rb][w][0];
+        for (int v = 0; v < NW; ++v) ct += sh.slot[rb][v][0];
         rb ^= 1;
-        __syncthreads();
         const float lam = (float)ns * (float)md.K_t / (float)V;
         th.lambda = lam;
         if (lam >= 4.0f && (float)ct < 1.25f * lam + 2.0f) {
             const uint32_t r = min((uint32_t)ceilf(lam + 5.0f * sqrtf(lam) + 5.0f), ns);
-            const float tfb = sample_rank_value<THREADS, BF16>(rowp, V, r, sh, rb);
+            // every wave scans the histogram from the top: lane l holds bins
+            // 4l .. 4l+3, and the suffix counts come from a DPP scan
+            const uint32_t b0 = sh.hist[4 * lane], b1 = sh.hist[4 * lane + 1], b2 = sh.hist[4 * lane + 2],
+                           b3 = sh.hist[4 * lane + 3];
+            const uint32_t own = b0 + b1 + b2 + b3;
+            const uint32_t above = wave_suffix_sum_excl(own);  // bins of higher lanes
+            // highest bin whose count from the top reaches r
+            int bin = -1;
+            const uint32_t c3 = above + b3, c2 = c3 + b2, c1 = c2 + b1, cz = c1 + b0;
+            bin = c3 >= r ? 4 * lane + 3 : (c2 >= r ? 4 * lane + 2 : (c1 >= r ? 4 * lane + 1 : (cz >= r ? 4 * lane : -1)));
+            const uint64_t has = __ballot(bin >= 0);
+            // the reaching bin sits in the highest lane that has one
+            const int src = has ? 63 - (int)__builtin_clzll(has) : 0;
+            const int best = __shfl(bin, src);
+            const float tfb = best >= 0 ? lo + ((float)best - 0.5f) * w : -kInf;
             th.tc = fminf(t, tfb);
             th.predicted = true;
         }
@@ -1229,34 +1290,52 @@ QRITA_DEV Thresh compute_threshold(const Params& P, const RowMode& md, const voi
 // Compact the survivors (f >= tc) of 16 logits per lane into the candidate
 // stage: wavefront ballots count them, one LDS atomic per wave reserves
 // space, mbcnt gives each lane its slot. Logit j of this lane has vocabulary
-// index idx0 + (j / VE) * vstride + (j % VE). Survivors past the stage go
-// straight to the row list (with their key, for the list's max).
+// index idx0 + (j / VE) * vstride + (j % VE); bit j of `valid` marks it as
+// present. Survivors past the stage go straight to the row list (with their
+// key, for the list's max). For top-p-only rows (REST) the dropped logits'
+// masses exp(f - tc) are summed per lane in float over the 16 and added to
+// the fixed-point `rest` once, so the total does not depend on lane order.
 template <int THREADS, bool BF16, bool REST, int VE>
 QRITA_DEV void consume16(const Params& P, int64_t row, const float f[16], uint32_t valid, uint32_t idx0,
                          uint32_t vstride, float tc, Shared& sh, uint64_t& rest, uint32_t& spill_kmax) {
     const uint32_t lane = threadIdx.x & (kWave - 1);
     uint32_t tot = 0;
+    float dropped = 0.0f;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
         const bool v = (valid >> j) & 1u;
         const bool s = v && f[j] >= tc;
         tot += (uint32_t)__popcll(__ballot(s));
-        if (REST && v && !s) rest += fx_from_unit_f32(__expf(f[j] - tc));
+        if (REST) dropped += (v && !s) ? __expf(f[j] - tc) : 0.0f;
     }
+    if (REST) rest += fx_from_unit_f32(fminf(dropped * 0x1p-5f, 1.0f)) << 5;
     if (tot == 0) return;
     uint32_t base = 0;
     if (lane == 0) base = atomicAdd(&sh.ncand, tot);
     base = readlane(base, 0);
     const uint32_t cap = (uint32_t)P.stage_cap;
-    const uint32_t spill_from = base > cap ? base : cap;
-    uint32_t gbase = 0;
-    if (base + tot > cap) {
-        const uint32_t nover = base + tot - spill_from;
-        if (lane == 0) gbase = atomicAdd(&P.hdr[row * H_WORDS + H_LIST], nover);
-        gbase = readlane(gbase, 0);
-    }
     uint64_t* a = lds_cands();
     uint32_t run = base;
+    if (base + tot <= cap) {
+        // the whole group fits the stage
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const bool s = ((valid >> j) & 1u) && f[j] >= tc;
+            const uint64_t b = __ballot(s);
+            if (b) {
+                if (s)
+                    a[run + lanes_below(b)] = ((uint64_t)__float_as_uint(f[j]) << 32) |
+                                              (idx0 + (uint32_t)(j / VE) * vstride + (uint32_t)(j % VE));
+                run += (uint32_t)__popcll(b);
+            }
+        }
+        return;
+    }
+    const uint32_t spill_from = base > cap ? base : cap;
+    const uint32_t nover = base + tot - spill_from;
+    uint32_t gbase = 0;
+    if (lane == 0) gbase = atomicAdd(&P.hdr[row * H_WORDS + H_LIST], nover);
+    gbase = readlane(gbase, 0);
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
         const bool s = ((valid >> j) & 1u) && f[j] >= tc;
@@ -1283,16 +1362,67 @@ QRITA_DEV void consume16(const Params& P, int64_t row, const float f[16], uint32
     }
 }
 
+// One tile (THREADS * 16 logits from `tile`, all inside the slice): vector
+// loads marked non-temporal (the logits are read once) into f.
+template <int THREADS, bool BF16>
+QRITA_DEV void load_tile(const void* rowp, int64_t tile, float f[16]) {
+    constexpr int VE = BF16 ? 8 : 4;
+    constexpr int NV = 16 / VE;
+#pragma unroll
+    for (int q = 0; q < NV; ++q) {
+        const int64_t e = tile + (int64_t)q * THREADS * VE + (int64_t)threadIdx.x * VE;
+        if (BF16) {
+            const u32x4_t w = __builtin_nontemporal_load((const u32x4_t*)((const uint16_t*)rowp + e));
+            const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                f[q * 8 + 2 * r] = __uint_as_float(ws[r] << 16);
+                f[q * 8 + 2 * r + 1] = __uint_as_float(ws[r] & 0xFFFF0000u);
+            }
+        } else {
+            const f32x4_t w = __builtin_nontemporal_load((const f32x4_t*)((const float*)rowp + e));
+            f[q * 4 + 0] = w.x;
+            f[q * 4 + 1] = w.y;
+            f[q * 4 + 2] = w.z;
+            f[q * 4 + 3] = w.w;
+        }
+    }
+}
+
+// The mask bytes of one full tile (this lane's 16 entries).
+template <int THREADS, bool BF16>
+QRITA_DEV void fill_tile(uint8_t* mrow, int64_t tile, uint8_t fill) {
+    constexpr int VE = BF16 ? 8 : 4;
+    constexpr int NV = 16 / VE;
+    const uint64_t fill8 = 0x0101010101010101ull * fill;
+#pragma unroll
+    for (int q = 0; q < NV; ++q) {
+        const int64_t e = tile + (int64_t)q * THREADS * VE + (int64_t)threadIdx.x * VE;
+        if (BF16)
+            __builtin_nontemporal_store(fill8, (uint64_t*)(mrow + e));
+        else
+            __builtin_nontemporal_store((uint32_t)fill8, (uint32_t*)(mrow + e));
+    }
+}
+
+// First 16-element-aligned position of the slice [e0, e1) of a row starting
+// at element roff of the batch.
+QRITA_DEV int64_t aligned_start(int64_t roff, int64_t e0, int64_t e1) {
+    const int64_t a = e0 + ((16 - ((roff + e0) & 15)) & 15);
+    return a > e1 ? e1 : a;
+}
+
+// The streaming pass over [e0, e1); f0 holds the slice's first full tile
+// (loaded before the threshold was known) when there is one.
 template <int THREADS, bool BF16, bool REST>
 QRITA_DEV void stream_slice(const Params& P, int64_t row, int64_t e0, int64_t e1, float tc, uint8_t fill,
-                            Shared& sh, uint64_t& rest, uint32_t& spill_kmax) {
+                            const float (&f0)[16], Shared& sh, uint64_t& rest, uint32_t& spill_kmax) {
     const int64_t roff = row * (int64_t)P.vocab;
     const void* rowp = row_ptr<BF16>(P, row);
     uint8_t* mrow = P.mask ? P.mask + roff : nullptr;
     const int tid = threadIdx.x;
     // head: up to 15 logits before the first 16-element-aligned position
-    int64_t a = e0 + ((16 - ((roff + e0) & 15)) & 15);
-    if (a > e1) a = e1;
+    const int64_t a = aligned_start(roff, e0, e1);
     if (a > e0) {
         float f[16];
         uint32_t valid = 0;
@@ -1310,47 +1440,36 @@ QRITA_DEV void stream_slice(const Params& P, int64_t row, int64_t e0, int64_t e1
     constexpr int VE = BF16 ? 8 : 4;  // logits per 16-byte vector
     constexpr int NV = 16 / VE;       // vectors per thread per tile
     constexpr int TB = THREADS * 16;  // logits per tile
-    const uint64_t fill8 = 0x0101010101010101ull * fill;
-    for (int64_t tile = a; tile < e1; tile += TB) {
-        float f[16];
+    // full tiles: the next tile's loads are issued before this one is consumed
+    const int64_t nfull = (e1 - a) / TB;
+    float f[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) f[j] = f0[j];
+    for (int64_t i = 0; i < nfull; ++i) {
+        const int64_t tile = a + i * TB;
+        float g[16];
+        if (i + 1 < nfull) load_tile<THREADS, BF16>(rowp, tile + TB, g);
+        if (mrow) fill_tile<THREADS, BF16>(mrow, tile, fill);
+        consume16<THREADS, BF16, REST, VE>(P, row, f, 0xFFFFu, (uint32_t)(tile + (int64_t)tid * VE),
+                                           (uint32_t)(THREADS * VE), tc, sh, rest, spill_kmax);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) f[j] = g[j];
+    }
+    // ragged last tile, element by element
+    const int64_t tile = a + nfull * TB;
+    if (tile < e1) {
         uint32_t valid = 0;
 #pragma unroll
         for (int q = 0; q < NV; ++q) {
-            const int64_t e = tile + (int64_t)q * THREADS * VE + (int64_t)tid * VE;
-            if (e + VE <= e1) {
-                if (BF16) {
-                    const uint4 w = *(const uint4*)((const uint16_t*)rowp + e);
-                    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        f[q * 8 + 2 * r] = __uint_as_float(ws[r] << 16);
-                        f[q * 8 + 2 * r + 1] = __uint_as_float(ws[r] & 0xFFFF0000u);
-                    }
+            for (int r = 0; r < VE; ++r) {
+                const int64_t er = tile + (int64_t)q * THREADS * VE + (int64_t)tid * VE + r;
+                if (er < e1) {
+                    f[q * VE + r] = load_value<BF16>(rowp, er);
+                    valid |= 1u << (q * VE + r);
+                    if (mrow) mrow[er] = fill;
                 } else {
-                    const float4 w = *(const float4*)((const float*)rowp + e);
-                    f[q * 4 + 0] = w.x;
-                    f[q * 4 + 1] = w.y;
-                    f[q * 4 + 2] = w.z;
-                    f[q * 4 + 3] = w.w;
-                }
-                valid |= ((1u << VE) - 1u) << (q * VE);
-                if (mrow) {
-                    if (BF16)
-                        *(uint64_t*)(mrow + e) = fill8;
-                    else
-                        *(uint32_t*)(mrow + e) = (uint32_t)fill8;
-                }
-            } else {
-#pragma unroll
-                for (int r = 0; r < VE; ++r) {
-                    const int64_t er = e + r;
-                    if (er < e1) {
-                        f[q * VE + r] = load_value<BF16>(rowp, er);
-                        valid |= 1u << (q * VE + r);
-                        if (mrow) mrow[er] = fill;
-                    } else {
-                        f[q * VE + r] = 0.0f;
-                    }
+                    f[q * VE + r] = 0.0f;
                 }
             }
         }
@@ -1380,6 +1499,18 @@ __global__ __launch_bounds__(THREADS) void pass1_kernel(Params P) {
         sh.ncand = 0;
         sh.flags = 0;
     }
+    // this workgroup's slice; slices after the first start 16-aligned
+    const int64_t A = (16 - (roff & 15)) & 15;
+    int64_t e0 = slice == 0 ? 0 : A + (int64_t)slice * P.slice_len;
+    int64_t e1 = A + (int64_t)(slice + 1) * P.slice_len;
+    if (slice + 1 == (uint32_t)P.slices || e1 > V) e1 = V;
+    if (e0 > V) e0 = V;
+    // the first full tile is loaded before the threshold is known
+    float f0[16];
+    {
+        const int64_t a = aligned_start(roff, e0, e1);
+        if (e1 - a >= (int64_t)THREADS * 16) load_tile<THREADS, BF16>(rowp, a, f0);
+    }
     // a2: every slice computes the same threshold from the same sample
     const Thresh th = compute_threshold<THREADS, BF16>(P, md, rowp, sh, rb);
     if (slice == 0 && threadIdx.x == 0) {
@@ -1390,41 +1521,49 @@ __global__ __launch_bounds__(THREADS) void pass1_kernel(Params P) {
         hdr[H_NS] = th.n_s;
     }
     __syncthreads();
-    // a3: this workgroup's slice; slices after the first start 16-aligned
-    const int64_t A = (16 - (roff & 15)) & 15;
-    int64_t e0 = slice == 0 ? 0 : A + (int64_t)slice * P.slice_len;
-    int64_t e1 = A + (int64_t)(slice + 1) * P.slice_len;
-    if (slice + 1 == (uint32_t)P.slices || e1 > V) e1 = V;
-    if (e0 > V) e0 = V;
+    // a3: the single streaming pass over the slice
     const uint8_t fill = md.keep_all ? 1 : 0;
     const bool rest_on = md.topp && !md.topk;
     uint64_t rest = 0;
     uint32_t kmax = 0;
     if (rest_on)
-        stream_slice<THREADS, BF16, true>(P, row, e0, e1, th.tc, fill, sh, rest, kmax);
+        stream_slice<THREADS, BF16, true>(P, row, e0, e1, th.tc, fill, f0, sh, rest, kmax);
     else
-        stream_slice<THREADS, BF16, false>(P, row, e0, e1, th.tc, fill, sh, rest, kmax);
+        stream_slice<THREADS, BF16, false>(P, row, e0, e1, th.tc, fill, f0, sh, rest, kmax);
     __syncthreads();
-    // publish: the staged candidates go to the row list in one reservation
+    // publish: the staged candidates go to the row list in one reservation,
+    // whose round trip overlaps the maximum over the stage
     const uint32_t nst = min(sh.ncand, (uint32_t)P.stage_cap);
-    if (threadIdx.x == 0) sh.u32[0] = nst ? atomicAdd(&hdr[H_LIST], nst) : 0u;
-    __syncthreads();
-    const uint32_t gb = sh.u32[0];
-    uint64_t* a = lds_cands();
-    uint64_t* lst = P.glist + row * (int64_t)P.list_stride;
-    bool over = false;
-    for (uint32_t i = threadIdx.x; i < nst; i += THREADS) {
-        const uint64_t r = a[i];
-        const uint32_t key = f32_key((uint32_t)(r >> 32));
-        kmax = key > kmax ? key : kmax;
-        if (gb + i < (uint32_t)P.list_cap)
-            lst[gb + i] = make_cand(key, (uint32_t)r);
-        else
-            over = true;
+    uint32_t gb = 0;
+    if (threadIdx.x == 0 && nst) gb = atomicAdd(&hdr[H_LIST], nst);
+    constexpr int PER = kSampleN / THREADS;  // stage entries per thread (stage_cap <= 2048)
+    const uint64_t* a = lds_cands();
+    uint32_t keys[PER], lows[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+        const uint32_t i = (uint32_t)u * THREADS + threadIdx.x;
+        const uint64_t r = i < nst ? a[i] : 0ull;
+        keys[u] = i < nst ? f32_key((uint32_t)(r >> 32)) : 0u;
+        lows[u] = ~(uint32_t)r;
+        kmax = keys[u] > kmax ? keys[u] : kmax;
     }
-    if (over) atomicOr(&sh.flags, 1u);
+    if (threadIdx.x == 0) sh.u32[0] = gb;
     uint32_t d0 = 0, d1 = 0;
     block_sum_min_max<THREADS>(d0, d1, kmax, rest, sh, rb);
+    gb = sh.u32[0];
+    uint64_t* lst = P.glist + row * (int64_t)P.list_stride;
+    bool over = false;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+        const uint32_t i = (uint32_t)u * THREADS + threadIdx.x;
+        if (i < nst) {
+            if (gb + i < (uint32_t)P.list_cap)
+                lst[gb + i] = ((uint64_t)keys[u] << 32) | lows[u];
+            else
+                over = true;
+        }
+    }
+    if (over) atomicOr(&hdr[H_FLAGS], 1u);
     if (threadIdx.x == 0) {
         if (kmax) atomicMax(&hdr[H_KMAX], kmax);
         if (rest) atomicAdd((unsigned long long*)(hdr + H_REST), (unsigned long long)rest);
