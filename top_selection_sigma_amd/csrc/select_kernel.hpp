@@ -89,7 +89,7 @@ constexpr int kHistBins = 256;  // pass 1: sample histogram for the miss predict
 
 struct Shared {
     alignas(16) uint32_t slot[2][kMaxWaves][16];  // per-wave partial records, double-buffered
-    uint32_t ties[kTieDirect];
+    alignas(16) uint32_t ties[kTieDirect + 4];
     uint32_t hist[kHistBins];
     float fred[2 * kMaxWaves];
     uint32_t ncand;
@@ -348,9 +348,10 @@ QRITA_DEV uint32_t comb_sum32(uint32_t v, Shared& sh, int& rb) {
 // ---------------------------------------------------------------------------
 // Candidate sources of the tail. A source hands every candidate to a visitor
 // as (key, low, r): key 0 marks an empty slot or a candidate outside the
-// current set (every real key is nonzero); low() returns the complemented
-// vocabulary index (read on demand: only duplicate resolution, the mask and
-// the index output need it); r is a register slot (RegSet only).
+// current set (every real key is nonzero); low is the complemented
+// vocabulary index (passed only to visits that ask for it: duplicate
+// resolution, the mask and the index output); r is a register slot (RegSet
+// only).
 // restrict_to(B) shrinks the set to the candidates c >= B; prepare_mass(m)
 // makes mass_at() return a candidate's softmax mass exp(z - m) relative to
 // the maximum m (0 outside the set).
@@ -361,6 +362,31 @@ QRITA_DEV uint32_t comb_sum32(uint32_t v, Shared& sh, int& rb) {
 // masses wait in LDS under the same slot numbering. Slot rows past the last
 // candidate are skipped per wave.
 // ---------------------------------------------------------------------------
+// Exclusive prefix over the waves of a workgroup of per-wave counts c (wave
+// uniform): returns the sum over the lower waves and sets total to the sum
+// over all of them.
+template <int NT>
+QRITA_DEV uint32_t wave_prefix(uint32_t c, uint32_t& total, Shared& sh, int& rb) {
+    constexpr int NW = NT / kWave;
+    if (NW == 1) {
+        total = c;
+        return 0u;
+    }
+    const uint32_t lane = tid_here() & (kWave - 1), wave = wave_base_here() / kWave;
+    if (lane == 0) sh.slot[rb][wave][0] = c;
+    __syncthreads();
+    uint32_t before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        const uint32_t q = sh.slot[rb][w][0];
+        before += (uint32_t)w < wave ? q : 0u;
+        all += q;
+    }
+    rb ^= 1;
+    total = all;
+    return before;
+}
+
 // Calls f(std::integral_constant<int, C>) for C = B .. E-1 (compile-time
 // register indices).
 template <int B, int E, class F>
@@ -404,13 +430,27 @@ struct RegSet {
         chunks_from<0>(f, rows_here());
     }
 
-    template <class F>
+    // f(key, low, r) for every visited slot; with LOWS the complemented
+    // indices are first read from LDS in one batch (else low is 0).
+    template <bool LOWS, class F>
     QRITA_DEV void visit(F&& f) const {
-        const uint32_t* lp = lows + tid_here();
-        for_rows([&](auto rc) {
-            constexpr int r = decltype(rc)::value;
-            f(key[r], [lp]() { return lp[r * NT]; }, r);
-        });
+        if constexpr (LOWS) {
+            const uint32_t* lp = lows + tid_here();
+            uint32_t lw[R];
+            for_rows([&](auto rc) {
+                constexpr int r = decltype(rc)::value;
+                lw[r] = lp[r * NT];
+            });
+            for_rows([&](auto rc) {
+                constexpr int r = decltype(rc)::value;
+                f(key[r], lw[r], r);
+            });
+        } else {
+            for_rows([&](auto rc) {
+                constexpr int r = decltype(rc)::value;
+                f(key[r], 0u, r);
+            });
+        }
     }
     QRITA_DEV float mass_at(int r, uint32_t) const { return em[tid_here() + r * NT]; }
 
@@ -434,17 +474,103 @@ struct RegSet {
         });
         block_sync<NT>();
     }
+    // Keys through LDS (slot i at kb[i]), to hand a set to a different number
+    // of threads; the indices stay in `lows`, which every layout indexes by
+    // slot.
+    QRITA_DEV void store_keys(uint32_t* kb) const {
+        const uint32_t t = tid_here();
+        const uint32_t ns = nslots;
+        for_rows([&](auto rc) {
+            constexpr int r = decltype(rc)::value;
+            const uint32_t i = (uint32_t)r * NT + t;
+            if (i < ns) kb[i] = key[r];
+        });
+    }
+    QRITA_DEV void load_keys(const uint32_t* kb, uint32_t n) {
+        nslots = n;
+        const uint32_t t = tid_here();
+        for_rows([&](auto rc) {
+            constexpr int r = decltype(rc)::value;
+            const uint32_t i = (uint32_t)r * NT + t;
+            key[r] = i < n ? kb[i] : 0u;
+        });
+    }
+
+    // The same from candidates already loaded into pre[r] (slot r * NT + t).
+    QRITA_DEV void load_from(const uint64_t (&pre)[R], uint32_t n) {
+        nslots = n;
+        const uint32_t t = tid_here();
+        uint32_t* lp = lows + t;
+        for_rows([&](auto rc) {
+            constexpr int r = decltype(rc)::value;
+            const uint32_t i = (uint32_t)r * NT + t;
+            key[r] = i < n ? cand_key(pre[r]) : 0u;
+            lp[r * NT] = cand_low(pre[r]);
+        });
+        block_sync<NT>();
+    }
     QRITA_DEV void restrict_to(uint64_t B) {
         const uint32_t bk = cand_key(B), bl = cand_low(B);
         const uint32_t* lp = lows + tid_here();
+        uint32_t lw[R];
         for_rows([&](auto rc) {
             constexpr int r = decltype(rc)::value;
-            const uint32_t lw = lp[r * NT];
+            lw[r] = lp[r * NT];
+        });
+        for_rows([&](auto rc) {
+            constexpr int r = decltype(rc)::value;
             const uint32_t k = key[r];
-            const bool keep = k > bk || (k == bk && lw >= bl);
+            const bool keep = k > bk || (k == bk && lw[r] >= bl);
             key[r] = keep ? k : 0u;
         });
     }
+    // Move the candidates still in the set (key != 0) to the first slots,
+    // keeping their slot order, through buf (room for cap pairs); nothing
+    // moves when more than cap remain. Later visits then skip the emptied
+    // slot rows.
+    QRITA_DEV void compact(uint32_t* buf, uint32_t cap, Shared& sh, int& rb) {
+        uint32_t c = 0;
+        for_rows([&](auto rc) {
+            constexpr int r = decltype(rc)::value;
+            c += (uint32_t)__popcll(__ballot(key[r] != 0u));
+        });
+        uint32_t total = 0;
+        uint32_t run = wave_prefix<NT>(c, total, sh, rb);
+        if (total > cap) return;
+        const uint32_t t = tid_here();
+        const uint32_t* lp = lows + t;
+        uint32_t lw[R];
+        for_rows([&](auto rc) {
+            constexpr int r = decltype(rc)::value;
+            lw[r] = lp[r * NT];
+        });
+        for_rows([&](auto rc) {
+            constexpr int r = decltype(rc)::value;
+            const uint32_t k = key[r];
+            const uint64_t b = __ballot(k != 0u);
+            if (k != 0u) {
+                const uint32_t pos = run + lanes_below(b);
+                buf[pos] = k;
+                buf[cap + pos] = lw[r];
+            }
+            run += (uint32_t)__popcll(b);
+        });
+        block_sync<NT>();
+        nslots = total;
+        uint32_t* lq = lows + t;
+        for_rows([&](auto rc) {
+            constexpr int r = decltype(rc)::value;
+            const uint32_t i = (uint32_t)r * NT + t;
+            key[r] = i < total ? buf[i] : 0u;
+            lw[r] = i < total ? buf[cap + i] : 0u;
+        });
+        for_rows([&](auto rc) {
+            constexpr int r = decltype(rc)::value;
+            lq[r * NT] = lw[r];
+        });
+        block_sync<NT>();
+    }
+
     QRITA_DEV void prepare_mass(float m) {
         float* ep = em + tid_here();
         for_rows([&](auto rc) {
@@ -470,7 +596,7 @@ struct MemSrc {
         if (ROW) return make_cand(f32_key(__float_as_uint(load_value<BF16>(row, i))), i);
         return p[i];
     }
-    template <class F>
+    template <bool LOWS, class F>
     QRITA_DEV void visit(F&& f) const {
         constexpr int U = 4;
         const uint32_t t = tid_here();
@@ -485,8 +611,7 @@ struct MemSrc {
             for (int u = 0; u < U; ++u) {
                 const uint32_t i = base + (uint32_t)u * NT + t;
                 const bool ok = i < n && c[u] >= filter;
-                const uint32_t lw = cand_low(c[u]);
-                f(ok ? cand_key(c[u]) : 0u, [lw]() { return lw; }, 0);
+                f(ok ? cand_key(c[u]) : 0u, cand_low(c[u]), 0);
             }
         }
     }
@@ -552,11 +677,10 @@ QRITA_DEV uint64_t sel3(int j, const uint64_t x[3]) { return j == 2 ? x[2] : (j 
 
 // Field 0 searches keys; field 1 searches the complemented indices of the
 // candidates whose key is v_eq (duplicate resolution).
-template <int FIELD, class LowFn>
-QRITA_DEV uint32_t field_of(uint32_t key, const LowFn& low, uint32_t v_eq) {
+template <int FIELD>
+QRITA_DEV uint32_t field_of(uint32_t key, uint32_t low, uint32_t v_eq) {
     if (FIELD == 0) return key;
-    const uint32_t lw = low();
-    return key == v_eq ? lw : 0u;
+    return key == v_eq ? low : 0u;
 }
 
 template <int NT, int FIELD, bool MASS, class S>
@@ -570,7 +694,7 @@ QRITA_DEV Eval eval_pivots(const S& src, uint32_t v_eq, const uint32_t piv[3], u
     uint32_t mh[3] = {0u, 0u, 0u}, ml[3] = {0u, 0u, 0u};
     uint64_t mm[3] = {0ull, 0ull, 0ull};
     const uint32_t p0 = piv[0], p1 = piv[1], p2 = piv[2];
-    src.visit([&](uint32_t key, const auto& low, int r) {
+    src.template visit<FIELD == 1>([&](uint32_t key, uint32_t low, int r) {
         const uint32_t f = field_of<FIELD>(key, low, v_eq);
         const uint32_t b0 = gt01(f, p0), b1 = gt01(f, p1), b2 = gt01(f, p2);
         g[0] += b0;
@@ -617,7 +741,7 @@ QRITA_DEV Eval eval_pivots(const S& src, uint32_t v_eq, const uint32_t piv[3], u
     const uint32_t pj1 = (E.js >= 0 ? sel3(E.js, piv) : 0xFFFFFFFEu) + 1u;
     const uint32_t pu = E.js < 2 ? sel3(E.js + 1, piv) : 0xFFFFFFFFu;
     uint32_t du = 0xFFFFFFFFu, dv = 0xFFFFFFFFu;
-    src.visit([&](uint32_t key, const auto& low, int) {
+    src.template visit<FIELD == 1>([&](uint32_t key, uint32_t low, int) {
         const uint32_t f = field_of<FIELD>(key, low, v_eq);
         const uint32_t u = f - pj1, v = pu - f;
         du = u < du ? u : du;
@@ -631,7 +755,7 @@ QRITA_DEV Eval eval_pivots(const S& src, uint32_t v_eq, const uint32_t piv[3], u
     if (E.js >= 0) {
         const uint32_t mn = E.mn;
         uint32_t ne = 0, cnt = 0;
-        src.visit([&](uint32_t key, const auto& low, int) {
+        src.template visit<FIELD == 1>([&](uint32_t key, uint32_t low, int) {
             const uint32_t f = field_of<FIELD>(key, low, v_eq);
             ne += ne01(f, mn);
             ++cnt;
@@ -733,24 +857,46 @@ QRITA_DEV uint64_t tie_boundary(const S& src, uint32_t v, uint32_t need, uint32_
             const uint32_t lane = tid_here() & (kWave - 1);
             block_sync<NT>();
             if (threadIdx.x == 0) sh.gather_n = 0;
-            block_sync<NT>();
-            src.visit([&](uint32_t key, const auto& low, int) {
-                const bool tie = key == v;
-                const uint64_t bb = __ballot(tie);
-                if (bb) {
-                    uint32_t base = 0;
-                    if (lane == 0) base = atomicAdd(&sh.gather_n, (uint32_t)__popcll(bb));
-                    base = readlane(base, 0);
-                    const uint32_t pos = base + lanes_below(bb);
-                    if (tie && pos < (uint32_t)kTieDirect) sh.ties[pos] = low();
-                }
-            });
+            // zeros after the ties (below every complemented index) round the
+            // list up to whole uint4 reads
+            if (threadIdx.x < 4u && N + threadIdx.x < (uint32_t)kTieDirect) sh.ties[N + threadIdx.x] = 0u;
+            if constexpr (S::kRegs) {
+                // slots from per-wave counts, no atomics
+                uint32_t c = 0;
+                src.template visit<false>([&](uint32_t key, uint32_t, int) { c += (uint32_t)__popcll(__ballot(key == v)); });
+                uint32_t total = 0;
+                uint32_t run = wave_prefix<NT>(c, total, sh, rb);
+                src.template visit<true>([&](uint32_t key, uint32_t low, int) {
+                    const bool tie = key == v;
+                    const uint64_t bb = __ballot(tie);
+                    const uint32_t pos = run + lanes_below(bb);
+                    if (tie && pos < (uint32_t)kTieDirect) sh.ties[pos] = low;
+                    run += (uint32_t)__popcll(bb);
+                });
+            } else {
+                block_sync<NT>();
+                src.template visit<true>([&](uint32_t key, uint32_t low, int) {
+                    const bool tie = key == v;
+                    const uint64_t bb = __ballot(tie);
+                    if (bb) {
+                        uint32_t base = 0;
+                        if (lane == 0) base = atomicAdd(&sh.gather_n, (uint32_t)__popcll(bb));
+                        base = readlane(base, 0);
+                        const uint32_t pos = base + lanes_below(bb);
+                        if (tie && pos < (uint32_t)kTieDirect) sh.ties[pos] = low;
+                    }
+                });
+            }
             block_sync<NT>();
             // the tie whose complemented index has exactly need - 1 larger ones
+            const uint32_t n4 = (N + 3u) / 4u;
             for (uint32_t i = threadIdx.x; i < N; i += NT) {
                 const uint32_t x = sh.ties[i];
                 uint32_t above = 0;
-                for (uint32_t j = 0; j < N; ++j) above += sh.ties[j] > x ? 1u : 0u;
+                for (uint32_t j = 0; j < n4; ++j) {
+                    const uint4 q = *(const uint4*)&sh.ties[4 * j];
+                    above += (q.x > x ? 1u : 0u) + (q.y > x ? 1u : 0u) + (q.z > x ? 1u : 0u) + (q.w > x ? 1u : 0u);
+                }
                 if (above == need - 1) sh.u32[6] = x;
             }
             block_sync<NT>();
@@ -899,7 +1045,7 @@ __device__ __attribute__((noinline)) void sort_emit(uint32_t cnt, int32_t* out) 
 // rank order to out_idx[row][off ...].
 template <int NT, class S>
 QRITA_DEV void emit_indices(const Params& P, int64_t row, const S& src, uint64_t lo_b, uint64_t hi_b,
-                            uint32_t cnt, uint32_t off, Shared& sh, bool defer = false) {
+                            uint32_t cnt, uint32_t off, Shared& sh, int& rb, bool defer = false) {
     uint64_t* a = lds_cands();
     const uint32_t lane = tid_here() & (kWave - 1);
     const uint32_t cap = (uint32_t)P.tail_alloc;
@@ -907,18 +1053,35 @@ QRITA_DEV void emit_indices(const Params& P, int64_t row, const S& src, uint64_t
     if (threadIdx.x == 0) sh.gather_n = 0;
     block_sync<NT>();
     const uint32_t lk = cand_key(lo_b), ll = cand_low(lo_b), hk = cand_key(hi_b), hl = cand_low(hi_b);
-    src.visit([&](uint32_t key, const auto& low, int) {
-        const uint32_t lw = low();
-        const bool take = key != 0 && (key > lk || (key == lk && lw >= ll)) && (key < hk || (key == hk && lw < hl));
-        const uint64_t b = __ballot(take);
-        if (b) {
-            uint32_t base = 0;
-            if (lane == 0) base = atomicAdd(&sh.gather_n, (uint32_t)__popcll(b));
-            base = readlane(base, 0);
-            const uint32_t pos = base + lanes_below(b);
+    auto takes = [&](uint32_t key, uint32_t lw) {
+        return key != 0 && (key > lk || (key == lk && lw >= ll)) && (key < hk || (key == hk && lw < hl));
+    };
+    if constexpr (S::kRegs) {
+        // positions from per-wave counts, no atomics
+        uint32_t c = 0;
+        src.template visit<true>([&](uint32_t key, uint32_t low, int) { c += (uint32_t)__popcll(__ballot(takes(key, low))); });
+        uint32_t total = 0;
+        uint32_t run = wave_prefix<NT>(c, total, sh, rb);
+        src.template visit<true>([&](uint32_t key, uint32_t lw, int) {
+            const bool take = takes(key, lw);
+            const uint64_t b = __ballot(take);
+            const uint32_t pos = run + lanes_below(b);
             if (take && pos < cap) a[pos] = ((uint64_t)key << 32) | lw;
-        }
-    });
+            run += (uint32_t)__popcll(b);
+        });
+    } else {
+        src.template visit<true>([&](uint32_t key, uint32_t lw, int) {
+            const bool take = takes(key, lw);
+            const uint64_t b = __ballot(take);
+            if (b) {
+                uint32_t base = 0;
+                if (lane == 0) base = atomicAdd(&sh.gather_n, (uint32_t)__popcll(b));
+                base = readlane(base, 0);
+                const uint32_t pos = base + lanes_below(b);
+                if (take && pos < cap) a[pos] = ((uint64_t)key << 32) | lw;
+            }
+        });
+    }
     block_sync<NT>();
     if (defer) {
         // a step run by one wave leaves the sort to the whole workgroup
@@ -936,6 +1099,17 @@ struct TailDiag {
     int32_t iters;
 };
 
+// What finish_head leaves for finish_rest: the kept set {c >= B} of L
+// tokens, setn of them among the candidates, and the row's facts.
+struct RowState {
+    uint64_t B;
+    uint32_t L, setn, n, kmax;
+    int64_t key_lo;
+    uint64_t rest_fx;
+    float rest_ref, m;
+    bool topk, topp;
+};
+
 // Rank windows of sort_cap entries of the kept set {c >= B} (Lout of its
 // `setn` candidates, keys in (lo_b, kmax]), each window found by its own
 // boundary.
@@ -948,7 +1122,7 @@ QRITA_DEV void emit_windows_src(const Params& P, int64_t row, const S& src, uint
         const uint32_t cnt = min(cap, Lout - done);
         const uint64_t Bn = select_boundary<NT>(src, done + cnt, setn, lo_b, kmax, (uint32_t)P.vocab,
                                                 P.pivot_mode, B, sh, rb, dg.iters);
-        emit_indices<NT>(P, row, src, Bn, prev, cnt, done, sh);
+        emit_indices<NT>(P, row, src, Bn, prev, cnt, done, sh, rb);
         prev = Bn;
         done += cnt;
     }
@@ -974,14 +1148,14 @@ __device__ __attribute__((noinline)) TailDiag emit_windows(const Params& P, int6
 // false when the source does not contain the answer (a truncation miss); then
 // nothing has been written.
 template <int NT, class S>
-QRITA_DEV bool finish_row(const Params& P, int64_t row, const RowMode& md, S& src, uint32_t n, int64_t key_lo,
-                          uint32_t kmax, uint64_t rest_fx, float rest_ref, float t_gauss, Shared& sh, int& rb,
-                          TailDiag& dg) {
+QRITA_DEV bool finish_head(const Params& P, int64_t row, const RowMode& md, S& src, uint32_t n,
+                           int64_t key_lo, uint32_t kmax, uint64_t rest_fx, float rest_ref, float t_gauss,
+                           Shared& sh, int& rb, TailDiag& dg, RowState& st) {
     const uint32_t V = (uint32_t)P.vocab;
     if (P.diag) {  // #{z >= Gaussian t} among the candidates, for diagnostics
         const uint32_t key_t = f32_key(__float_as_uint(t_gauss));
         uint32_t c = 0;
-        src.visit([&](uint32_t key, const auto&, int) { c += key >= key_t ? 1u : 0u; });
+        src.template visit<false>([&](uint32_t key, uint32_t, int) { c += key >= key_t ? 1u : 0u; });
         dg.n_t = (int32_t)comb_sum32<NT>(c, sh, rb);
     }
     bool topk = md.topk, topp = md.topp;
@@ -1003,11 +1177,30 @@ QRITA_DEV bool finish_row(const Params& P, int64_t row, const RowMode& md, S& sr
         L = K;
         setn = K;
         src.restrict_to(B);
+        if constexpr (S::kRegs) src.compact((uint32_t*)lds_cands(), (uint32_t)P.tail_alloc, sh, rb);
     }
+    st = RowState{B, L, setn, n, kmax, key_lo, rest_fx, rest_ref, m, topk, topp};
+    return true;
+}
+
+// Steps a6-a7 after finish_head (possibly on a register set handed to
+// fewer threads). Returns false only for a top-p-only row whose candidates
+// do not hold mass p (a truncation miss; nothing has been written).
+template <int NT, class S>
+QRITA_DEV bool finish_rest(const Params& P, int64_t row, const RowMode& md, S& src, const RowState& st,
+                           Shared& sh, int& rb, TailDiag& dg) {
+    const uint32_t V = (uint32_t)P.vocab;
+    const bool topk = st.topk, topp = st.topp;
+    const uint32_t n = st.n, kmax = st.kmax;
+    const int64_t key_lo = st.key_lo;
+    const uint64_t rest_fx = st.rest_fx;
+    const float rest_ref = st.rest_ref, m = st.m;
+    uint64_t B = st.B;
+    uint32_t L = st.L, setn = st.setn;
     if (topp) {
         src.prepare_mass(m);
         uint64_t ms = 0;
-        src.visit([&](uint32_t key, const auto&, int r) { ms += fx_from_unit_f32(src.mass_at(r, key)); });
+        src.template visit<false>([&](uint32_t key, uint32_t, int r) { ms += fx_from_unit_f32(src.mass_at(r, key)); });
         ms = comb_sum64<NT>(ms, sh, rb);
         double mass_all = (double)ms;
         // the dropped logits' mass was taken relative to rest_ref <= m
@@ -1033,13 +1226,13 @@ QRITA_DEV bool finish_row(const Params& P, int64_t row, const RowMode& md, S& sr
         L = mo.n_gt + need;
         setn = L;
         src.restrict_to(B);
+        if constexpr (S::kRegs) src.compact((uint32_t*)lds_cands(), (uint32_t)P.tail_alloc, sh, rb);
     }
     // a7: mask (pass 1 zero-filled the row; keep-all rows were filled there)
     if (P.mask && !md.keep_all) {
         uint8_t* mrow = P.mask + row * (int64_t)V;
         const uint32_t bk = cand_key(B), bl = cand_low(B);
-        src.visit([&](uint32_t key, const auto& low, int) {
-            const uint32_t lw = low();
+        src.template visit<true>([&](uint32_t key, uint32_t lw, int) {
             if (key != 0 && (key > bk || (key == bk && lw >= bl))) mrow[~lw] = 1;
         });
     }
@@ -1054,7 +1247,7 @@ QRITA_DEV bool finish_row(const Params& P, int64_t row, const RowMode& md, S& sr
                 Bo = select_boundary<NT>(src, Lout, setn, lo_b, kmax, V, P.pivot_mode, B, sh, rb, dg.iters);
                 src.restrict_to(Bo);
             }
-            emit_indices<NT>(P, row, src, Bo, ~0ull, Lout, 0u, sh, NT == kWave && Lout > 128);
+            emit_indices<NT>(P, row, src, Bo, ~0ull, Lout, 0u, sh, rb, NT == kWave && Lout > 128);
         } else if constexpr (S::kRegs) {
             // a kept set larger than one sort: windows over the row list
             const TailDiag w = emit_windows<NT>(P, row, n, B, Lout, setn, lo_b, kmax, sh, rb);
@@ -1066,6 +1259,16 @@ QRITA_DEV bool finish_row(const Params& P, int64_t row, const RowMode& md, S& sr
     }
     if (P.out_count && threadIdx.x == 0) P.out_count[row] = (int32_t)L;
     return true;
+}
+
+template <int NT, class S>
+QRITA_DEV bool finish_row(const Params& P, int64_t row, const RowMode& md, S& src, uint32_t n, int64_t key_lo,
+                          uint32_t kmax, uint64_t rest_fx, float rest_ref, float t_gauss, Shared& sh, int& rb,
+                          TailDiag& dg) {
+    RowState st;
+    if (!finish_head<NT>(P, row, md, src, n, key_lo, kmax, rest_fx, rest_ref, t_gauss, sh, rb, dg, st))
+        return false;
+    return finish_rest<NT>(P, row, md, src, st, sh, rb, dg);
 }
 
 
@@ -1707,6 +1910,17 @@ __global__ __launch_bounds__(NT) void tail_kernel(Params P) {
     const int32_t V = P.vocab;
     uint32_t* hdr = P.hdr + row * H_WORDS;
     const uint64_t* lst = P.glist + row * (int64_t)P.list_stride;
+    // wave 0 reads the head of the row list before the header tells how much
+    // of it is filled (entries past the fill are ignored)
+    uint64_t pre[kWaveR];
+    if (threadIdx.x < (uint32_t)kWave) {
+        const uint32_t lim = min((uint32_t)P.list_stride, (uint32_t)(kWave * kWaveR));
+#pragma unroll
+        for (int r = 0; r < kWaveR; ++r) {
+            const uint32_t i = (uint32_t)r * kWave + threadIdx.x;
+            pre[r] = i < lim ? lst[i] : 0ull;
+        }
+    }
     const RowMode md = row_mode(P, row);
     const float t = __uint_as_float(hdr[H_T]);
     const float tc = __uint_as_float(hdr[H_TC]);
@@ -1734,7 +1948,7 @@ __global__ __launch_bounds__(NT) void tail_kernel(Params P) {
                     RegSet<kWave, kWaveR> src;
                     src.lows = (uint32_t*)(lds_cands() + P.tail_alloc);
                     src.em = (float*)lds_cands();
-                    src.load(lst, nlist);
+                    src.load_from(pre, nlist);
                     const bool ok =
                         finish_row<kWave>(P, row, md, src, nlist, key_lo, kmax, rest, tc, t, sh, rb, dg);
                     if (threadIdx.x == 0) sh.u32[7] = ok ? 1u : 0u;
@@ -1748,7 +1962,28 @@ __global__ __launch_bounds__(NT) void tail_kernel(Params P) {
                 src.lows = (uint32_t*)(lds_cands() + P.tail_alloc);
                 src.em = (float*)lds_cands();  // the sort buffer is free until the indices are emitted
                 src.load(lst, nlist);
-                done = finish_row<NT>(P, row, md, src, nlist, key_lo, kmax, rest, tc, t, sh, rb, dg);
+                RowState st;
+                const bool hit = finish_head<NT>(P, row, md, src, nlist, key_lo, kmax, rest, tc, t, sh, rb, dg, st);
+                if (hit && src.nslots <= (uint32_t)(kWave * kWaveR)) {
+                    // the top-k set is small: one wave carries on without barriers
+                    uint32_t* kb = (uint32_t*)lds_cands();
+                    src.store_keys(kb);
+                    __syncthreads();
+                    if (threadIdx.x < (uint32_t)kWave) {
+                        if (threadIdx.x == 0) sh.u32[5] = 0u;
+                        RegSet<kWave, kWaveR> s1;
+                        s1.lows = src.lows;
+                        s1.em = src.em;
+                        s1.load_keys(kb, src.nslots);
+                        const bool ok = finish_rest<kWave>(P, row, md, s1, st, sh, rb, dg);
+                        if (threadIdx.x == 0) sh.u32[7] = ok ? 1u : 0u;
+                    }
+                    __syncthreads();
+                    done = sh.u32[7] != 0;
+                    if (done && sh.u32[5]) sort_emit<NT>(sh.u32[4], P.out_idx + row * (int64_t)P.idx_cap);
+                } else if (hit) {
+                    done = finish_rest<NT>(P, row, md, src, st, sh, rb, dg);
+                }
             }
         }
         if (!done) {
