@@ -960,29 +960,36 @@ QRITA_DEV void bitonic_sort(uint64_t* a, int32_t* out, uint32_t cnt) {
         for (uint32_t j = min(k >> 1, 32u * E); j >= (uint32_t)E; j >>= 1) {
             const uint32_t g0 = t * E;
             const bool keep_max = ((g0 & j) == 0) == ((g0 & k) == 0);
-            // every exchange of the stage is issued before the first compare
-            const int src_lane = (int)(((t ^ (j / E)) & (kWave - 1)) << 2);
-            uint32_t ylo[E], yhi[E];
+            const uint32_t d = j / E;
+            {
+                // every exchange of the stage is issued before the first compare
+                const int src_lane = (int)(((t ^ d) & (kWave - 1)) << 2);
+                uint32_t ylo[E], yhi[E];
 #pragma unroll
-            for (int e = 0; e < E; ++e) {
-                ylo[e] = (uint32_t)__builtin_amdgcn_ds_bpermute(src_lane, (int)(uint32_t)x[e]);
-                yhi[e] = (uint32_t)__builtin_amdgcn_ds_bpermute(src_lane, (int)(uint32_t)(x[e] >> 32));
-            }
+                for (int e = 0; e < E; ++e) {
+                    ylo[e] = (uint32_t)__builtin_amdgcn_ds_bpermute(src_lane, (int)(uint32_t)x[e]);
+                    yhi[e] = (uint32_t)__builtin_amdgcn_ds_bpermute(src_lane, (int)(uint32_t)(x[e] >> 32));
+                }
 #pragma unroll
-            for (int e = 0; e < E; ++e) {
-                const uint64_t y = ((uint64_t)yhi[e] << 32) | ylo[e];
-                x[e] = ((x[e] > y) == keep_max) ? x[e] : y;
+                for (int e = 0; e < E; ++e) {
+                    const uint64_t y = ((uint64_t)yhi[e] << 32) | ylo[e];
+                    x[e] = ((x[e] > y) == keep_max) ? x[e] : y;
+                }
             }
         }
+        // direction of element e: descending iff bit k of t * E + e is clear;
+        // for k >= E that is one lane mask for all e, below it depends on e only
+        const bool desc_t = ((t * E) & k) == 0;
 #pragma unroll
         for (int j = E / 2; j >= 1; j >>= 1) {
             if ((uint32_t)j < k) {
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
                     if ((e & j) == 0) {
-                        const bool desc = ((t * E + e) & k) == 0;
+                        const bool desc = k >= (uint32_t)E ? desc_t : (((uint32_t)e & k) == 0);
                         const uint64_t p = x[e], q = x[e | j];
-                        const bool sw = desc ? (p < q) : (p > q);
+                        // equal entries (only padding) may swap either way
+                        const bool sw = (p < q) == desc;
                         x[e] = sw ? q : p;
                         x[e | j] = sw ? p : q;
                     }
@@ -1005,7 +1012,7 @@ QRITA_DEV void bitonic_sort(uint64_t* a, int32_t* out, uint32_t cnt) {
 // instead of on top of everything live at each of its call sites.
 template <int NT>
 QRITA_DEV uint32_t sort_cap(const Params& P) {
-    return NT == kWave ? 32u * kWave : min((uint32_t)P.tail_alloc, 16u * NT);
+    return NT == kWave ? (uint32_t)(kWave * kWaveR) : min((uint32_t)P.tail_alloc, 16u * NT);
 }
 template <int NT>
 __device__ __attribute__((noinline)) void sort_emit(uint32_t cnt, int32_t* out) {
@@ -1023,21 +1030,21 @@ __device__ __attribute__((noinline)) void sort_emit(uint32_t cnt, int32_t* out) 
         block_sync<NT>();
         return;
     }
-    uint32_t np = next_pow2(cnt);
-    if (np < (uint32_t)NT) np = NT;
-    for (uint32_t i = cnt + threadIdx.x; i < np; i += NT) a[i] = 0ull;
-    block_sync<NT>();
-    switch (np / NT) {
-        case 1: bitonic_sort<NT, 1>(a, out, cnt); break;
-        case 2: bitonic_sort<NT, 2>(a, out, cnt); break;
-        case 4: bitonic_sort<NT, 4>(a, out, cnt); break;
-        case 8: bitonic_sort<NT, 8>(a, out, cnt); break;
-        case 16: bitonic_sort<NT, 16>(a, out, cnt); break;
-        default:
-            if constexpr (NT == kWave) bitonic_sort<NT, 32>(a, out, cnt);
-            break;
+    // a one-wave step hands sets above 128 to the whole workgroup's sort
+    if constexpr (NT > kWave) {
+        uint32_t np = next_pow2(cnt);
+        if (np < (uint32_t)NT) np = NT;
+        for (uint32_t i = cnt + threadIdx.x; i < np; i += NT) a[i] = 0ull;
+        block_sync<NT>();
+        switch (np / NT) {
+            case 1: bitonic_sort<NT, 1>(a, out, cnt); break;
+            case 2: bitonic_sort<NT, 2>(a, out, cnt); break;
+            case 4: bitonic_sort<NT, 4>(a, out, cnt); break;
+            case 8: bitonic_sort<NT, 8>(a, out, cnt); break;
+            default: bitonic_sort<NT, 16>(a, out, cnt); break;
+        }
+        block_sync<NT>();
     }
-    block_sync<NT>();
 }
 
 // Gather the candidates c with lo_b <= c < hi_b (exactly cnt <= tail_alloc of
