@@ -14,6 +14,7 @@ last timed call are checked against the CPU oracle, which is then timed on a
 bounded sample of the same workload as the CPU baseline.
 """
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -26,6 +27,34 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCES = ("top_selection_sigma_amd/csrc/select_kernel.hpp", "top_selection_sigma_amd/csrc/device_common.hpp",
+                  "top_selection_sigma_amd/csrc/qrita.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pass1_traffic.json")
+
+
+def kernel_source_digest():
+    """sha256 over the kernel sources: counter readings taken on other
+    sources do not describe this build."""
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload):
+    """HBM bytes per pass-1 launch from the rocprofv3 FETCH_SIZE/WRITE_SIZE
+    readings recorded in profiles/pass1_traffic.json (already scaled by the
+    copy-kernel factor), or None when absent or taken on other sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = rec.get("workloads", {}).get(workload)
+    if not ent or rec.get("kernel_sha256") != kernel_source_digest():
+        return None
+    return ent.get("hbm_bytes_per_launch")
 METRIC = "rows/sec and effective HBM GB/s (% of peak) for exact top-k/top-p masks"
 
 
@@ -98,10 +127,24 @@ def bench_config(index, steps, warmup, rotate_bytes):
     torch.cuda.synchronize()
     pass1_ms = float(np.mean([s.elapsed_time(m) for s, m in zip(starts, mids)]))
     tail_ms = float(np.mean([m.elapsed_time(e) for m, e in zip(mids, ends)]))
+    per_step = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+
+    # truncation outcome per row (one extra call with diagnostics)
+    diag = torch.zeros(B * q.DIAG_FIELDS, dtype=torch.int32, device=dev)
+    step(0, q.Options(diag=diag))
+    torch.cuda.synchronize()
+    dg = diag.cpu().numpy().reshape(B, q.DIAG_FIELDS)
+    path = dg[:, 4]
 
     res = dict(index=index, name=x.name, batch=B, vocab=V, dtype=x.dtype, steps=steps,
                warmup=warmup, rotation_sets=nsets, ms_per_step=total_ms / steps,
-               pass1_ms=pass1_ms, tail_ms=tail_ms)
+               pass1_ms=pass1_ms, tail_ms=tail_ms,
+               step_ms_p10_p50_p90=[float(np.percentile(per_step, q_)) for q_ in (10, 50, 90)],
+               rows_single_pass=int(np.sum(path <= 1)), rows_miss_predicted=int(np.sum(dg[:, 7] == 1)),
+               rows_recollected=int(np.sum(path == 2)), rows_full_row=int(np.sum(path == 3)),
+               gaussian_t_hit_rows=int(np.sum(dg[:, 5] == 1)),
+               workspace_bytes=int(q.qrita_workspace_bytes(B, V, q.dtype_code(logits0), idx_cap)),
+               sort_based_bytes=int(B * V * (es + 4) * 2))
     lg, m, ix, c = sets[last]
     count = c.cpu().numpy()
     kept_idx = np.minimum(count, idx_cap).astype(np.int64).sum()
@@ -229,13 +272,18 @@ def main():
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(head["pass1_gbps"] / PEAK_HBM_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(head["name"]),
             "pass1_us": round(head["pass1_ms"] * 1e3, 3),
             "tail_us": round(head["tail_ms"] * 1e3, 3),
             "alg_bytes_per_launch": head["pass1_alg_bytes"],
         },
         "cpu_baseline": cpu,
         "parity": head.get("parity"),
+        "step_ms_p10_p50_p90": [round(v, 5) for v in head["step_ms_p10_p50_p90"]],
+        "truncation": {"rows": head["batch"], "single_pass": head["rows_single_pass"],
+                       "miss_predicted": head["rows_miss_predicted"], "recollected": head["rows_recollected"],
+                       "full_row": head["rows_full_row"], "gaussian_t_hit": head["gaussian_t_hit_rows"]},
+        "memory": {"workspace_bytes": head["workspace_bytes"], "sort_based_bytes": head["sort_based_bytes"]},
         "per_config": per,
         "device": dev_name,
     }
