@@ -33,8 +33,9 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pass1_traffic.json")
 
 
 def kernel_source_digest():
-    """sha256 over the kernel sources: counter readings taken on other
-    sources do not describe this build."""
+    """sha256 over the pass-1 kernel's sources (the tail lives in its own
+    file): counter readings taken on other sources do not describe this
+    build."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
         with open(os.path.join(ROOT, rel), "rb") as f:

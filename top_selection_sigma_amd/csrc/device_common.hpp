@@ -45,16 +45,16 @@ QRITA_DEV uint32_t cand_idx(uint64_t c) { return ~(uint32_t)c; }
 
 // ---------------------------------------------------------------------------
 // Softmax mass in fixed point: e = exp(z - ref) in [0, 1] is stored as
-// floor(e * 2^44) in 64 bits. Integer sums are exact and associative, so a
+// floor(e * 2^43) in 64 bits. Integer sums are exact and associative, so a
 // mass does not depend on how candidates are split over lanes, waves or
-// workgroups. 2^18 terms of at most 2^44 fit in 63 bits; the truncation error
-// is below 2^-44 per term.
+// workgroups. 2^18 terms of at most 2^43 fit in 62 bits; the truncation error
+// is below 2^-43 per term.
 // ---------------------------------------------------------------------------
-constexpr int kFxShift = 44;
+constexpr int kFxShift = 43;
 
 QRITA_DEV uint64_t fx_from_unit_f32(float e) {
-    // e * 2^44 is exact in float; split it into two exact 32-bit halves.
-    float x = e * 0x1p44f;
+    // e * 2^43 is exact in float; split it into two exact 32-bit halves.
+    float x = e * 0x1p43f;
     uint32_t hi = (uint32_t)(x * 0x1p-32f);
     float rem = fmaf((float)hi, -0x1p32f, x);
     uint32_t lo = (uint32_t)rem;
@@ -75,7 +75,7 @@ QRITA_DEV float mass_f32(uint32_t key, float m) {
     return ldexpf(__builtin_amdgcn_exp2f((float)(y - fl)), (int)fl);
 }
 
-// Fixed-point softmax mass of a candidate key, floor(exp(z - m) * 2^44).
+// Fixed-point softmax mass of a candidate key, floor(exp(z - m) * 2^43).
 QRITA_DEV uint64_t mass_fx(uint32_t key, float m) { return fx_from_unit_f32(mass_f32(key, m)); }
 
 // ---------------------------------------------------------------------------
@@ -154,7 +154,7 @@ QRITA_DEV uint64_t wave_sum_u64(uint64_t x) {
     return ((uint64_t)readlane(hi, 63) << 32) | readlane(lo, 63);
 }
 // Wave total of the fixed-point masses hi * 2^22 + lo held per lane as
-// 32-bit half sums (each below 2^27): 16-lane row sums stay within 32 bits,
+// 32-bit half sums (each below 2^28): 16-lane row sums stay within 32 bits,
 // the cross-row steps run in 64 bits.
 QRITA_DEV uint64_t wave_sum_split(uint32_t hi, uint32_t lo) {
     {
@@ -229,12 +229,13 @@ QRITA_DEV uint32_t ne01(uint32_t a, uint32_t b) {
     return d;
 }
 
-// A softmax mass e in [0, 1] as floor(e * 2^44) = hi * 2^22 + lo with
-// hi, lo < 2^22 + 1 (both exact; the same value as fx_from_unit_f32). Sums of
-// up to 512 such halves fit 32 bits.
+// A softmax mass e in [0, 1] as floor(e * 2^43) = hi * 2^22 + lo with
+// hi <= 2^21 and lo < 2^22 (both exact; the same value as fx_from_unit_f32).
+// Per-lane sums of up to 64 such halves, summed over a 16-lane row, stay
+// below 2^32.
 QRITA_DEV void fx_split(float e, uint32_t& hi, uint32_t& lo) {
-    hi = (uint32_t)(e * 0x1p22f);
-    lo = (uint32_t)fmaf((float)hi, -0x1p22f, e * 0x1p44f);
+    hi = (uint32_t)(e * 0x1p21f);
+    lo = (uint32_t)fmaf((float)hi, -0x1p22f, e * 0x1p43f);
 }
 
 // threadIdx.x behind an optimisation barrier: address and mask arithmetic

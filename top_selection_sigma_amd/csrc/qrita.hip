@@ -14,10 +14,11 @@ using qrita::Params;
 
 constexpr int64_t kHeaderBytes = qrita::H_WORDS * 4;
 constexpr int64_t kListMax = 32768;
-// tail workgroup: two waves per SIMD; up to 32 candidate keys per thread in
+// tail workgroup: one wave per SIMD; up to 64 candidate keys per thread in
 // registers (16384 per row) with their indices in LDS, and an LDS buffer of
-// 8192 candidates for sorting (larger kept sets are sorted in windows)
-constexpr int kTailThreads = 512;
+// 8192 candidates for gathering the kept set (sets above 4096 are sorted in
+// windows) that holds the candidates' softmax masses before that
+constexpr int kTailThreads = 256;
 constexpr int kTailRegCap = kTailThreads * qrita::kTailR;
 constexpr int kTailLdsEntries = 8192;
 
@@ -45,7 +46,7 @@ int64_t next_pow2(int64_t x) {
 // for full rows, small ones for truncated sets). Here it is a static function
 // of the shape: pass 1 gets enough workgroups to cover 256 CUs several times
 // with slices of at least 8192 logits, so the per-workgroup sample stays small
-// next to the streamed bytes; the tail gets one 512-thread workgroup per row
+// next to the streamed bytes; the tail gets one 256-thread workgroup per row
 // over the much smaller candidate set.
 Tier choose_tier(int64_t B, int64_t V, const qrita_options* o) {
     Tier t;
