@@ -249,17 +249,27 @@ QRITA_DEV uint32_t tid_here() {
 // first thread of this thread's wave, as a wave-uniform (scalar) value
 QRITA_DEV uint32_t wave_base_here() { return __builtin_amdgcn_readfirstlane(tid_here() & ~(uint32_t)(kWave - 1)); }
 
-// Barrier over the NT threads that run a step: the workgroup barrier, or for
-// a step run by one wave alone a fence that completes its LDS accesses (the
-// lanes of a wave run in lockstep, and other waves are not waiting).
+// Workgroup barrier that orders LDS accesses only: global stores issued
+// before it are not waited for. For code in which no thread reads global
+// memory that another thread of the workgroup wrote during the kernel.
+QRITA_DEV void lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Barrier over the NT threads that run a step (LDS ordering only): the
+// workgroup barrier, or for a step run by one wave alone a fence that
+// completes its LDS accesses (the lanes of a wave run in lockstep, and other
+// waves are not waiting).
 template <int NT>
 QRITA_DEV void block_sync() {
     if (NT > kWave) {
-        __syncthreads();
+        lds_sync();
     } else {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
         __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
     }
 }
 

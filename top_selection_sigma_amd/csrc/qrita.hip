@@ -21,6 +21,9 @@ constexpr int64_t kListMax = 32768;
 constexpr int kTailThreads = 256;
 constexpr int kTailRegCap = kTailThreads * qrita::kTailR;
 constexpr int kTailLdsEntries = 8192;
+// tail LDS: gather/sort buffer and masses, the candidates' indices (then the
+// sort's second buffer), and the sort's bin counts
+constexpr size_t kTailLds = (size_t)kTailLdsEntries * 8 + (size_t)kTailRegCap * 4 + (qrita::kSortBins + 4) * 4;
 
 int64_t list_stride_for(int64_t vocab) { return std::min<int64_t>(vocab, kListMax); }
 
@@ -81,8 +84,8 @@ Tier choose_tier(int64_t B, int64_t V, const qrita_options* o) {
 }
 
 // Dynamic LDS above 64 KiB must be enabled per kernel; the largest request is
-// the tail's sort buffer and index store (128 KiB) next to its static LDS.
-constexpr int kMaxDynLds = 128 * 1024;
+// the tail's (kTailLds, about 144 KiB) next to its static LDS.
+constexpr int kMaxDynLds = 150 * 1024;
 
 template <class Kern>
 hipError_t allow_lds(Kern kern, std::once_flag& once, hipError_t& err) {
@@ -111,8 +114,7 @@ hipError_t launch_tail(const Params& P, const Tier& t, hipStream_t stream) {
     static std::once_flag once;
     static hipError_t attr = hipSuccess;
     if (allow_lds(kern, once, attr) != hipSuccess) return attr;
-    const size_t lds = (size_t)t.tail_alloc * sizeof(uint64_t) + (size_t)kTailRegCap * sizeof(uint32_t);
-    hipLaunchKernelGGL(kern, dim3((unsigned)P.batch), dim3(THREADS), lds, stream, P);
+    hipLaunchKernelGGL(kern, dim3((unsigned)P.batch), dim3(THREADS), kTailLds, stream, P);
     return hipGetLastError();
 }
 

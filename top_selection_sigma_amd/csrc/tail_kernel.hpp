@@ -1,6 +1,10 @@
 // The tail of the path (steps a4-a7): one workgroup of four waves per row,
 // launched after pass 1 has completed for every row.
 //
+// No thread of a tail workgroup reads global memory that another one wrote
+// (outside the re-collection of the fallback, which synchronises fully), so
+// its barriers order LDS only and never wait for the mask and index stores.
+//
 // The row's candidate list is held in registers (RegSet: up to 64 keys per
 // thread, 16384 per row) and every pivot evaluation of the quaternary search
 // is one pass over those registers followed by one combination across the
@@ -36,7 +40,7 @@ QRITA_DEV uint32_t wave_prefix(uint32_t c, uint32_t& total, Shared& sh, int& rb)
     }
     const uint32_t lane = tid_here() & (kWave - 1), wave = wave_base_here() / kWave;
     if (lane == 0) sh.slot[rb][wave][0] = c;
-    __syncthreads();
+    lds_sync();
     uint32_t before = 0, all = 0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
@@ -54,6 +58,13 @@ QRITA_DEV uint32_t comb_sum32(uint32_t v, Shared& sh, int& rb) {
     uint32_t total = 0;
     wave_prefix<NT>(wave_sum_u32(v), total, sh, rb);
     return total;
+}
+
+template <int NT>
+QRITA_DEV uint32_t comb_max32(uint32_t v, Shared& sh, int& rb) {
+    uint32_t mn[1] = {~wave_max_u32(v)};
+    comb_record<NT, 0, 0, 1>(nullptr, nullptr, mn, sh, rb);
+    return ~mn[0];
 }
 
 // Records of N32 u32 sums, N64 u64 sums and NMIN u32 minima (wave totals on
@@ -85,7 +96,7 @@ QRITA_DEV void comb_record(uint32_t* s32, uint64_t* s64, uint32_t* mn, Shared& s
             for (int q = 0; q < NQ; ++q)
                 *(uint4*)(base + wave * 32 + 4 * q) = make_uint4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
         }
-        __syncthreads();
+        lds_sync();
 #pragma unroll
         for (int i = 0; i < N32; ++i) s32[i] = 0u;
 #pragma unroll
@@ -728,12 +739,13 @@ QRITA_DEV void rank_sort(uint64_t* a, uint32_t cnt, int32_t* out, Shared& sh) {
     const uint32_t span = (((cnt + P - 1) / P) + 7u) & ~7u;
     if (t < 8u) a[cnt + t] = 0ull;
     if (q == 0 && e < cnt) sh.ties[e] = 0u;
-    __syncthreads();
+    lds_sync();
     uint64_t x = 0;
     if (e < cnt) {
         x = a[e];
         const uint32_t j0 = q * span, j1 = min(j0 + span, (cnt + 7u) & ~7u);
         uint32_t above = 0;
+#pragma unroll 4
         for (uint32_t j = j0; j < j1; j += 8) {
             const uint4* v = (const uint4*)(a + j);
             const uint4 v0 = v[0], v1 = v[1], v2 = v[2], v3 = v[3];
@@ -746,7 +758,7 @@ QRITA_DEV void rank_sort(uint64_t* a, uint32_t cnt, int32_t* out, Shared& sh) {
         }
         if (above) atomicAdd(&sh.ties[e], above);
     }
-    __syncthreads();
+    lds_sync();
     if (q == 0 && e < cnt) out[sh.ties[e]] = (int32_t)cand_idx(x);
 }
 
@@ -826,34 +838,206 @@ QRITA_DEV void bitonic_sort(uint64_t* a, int32_t* out, uint32_t cnt) {
     }
 }
 
+// Bucket sort, descending, of the cnt <= E * NT distinct words a[0 .. cnt)
+// into out[rank] = index. Thread t holds words e * NT + t in registers. A
+// word's bin orders it by key first: keys are coded exactly as
+// (kmax - key) >> z, z the number of low bits all keys share (16 for bf16
+// logits), and when the codes need fewer bits than there are bins, the
+// remaining bits split each key by index (lmax - low), so tie groups spread
+// over several bins. Bins ascend as words descend. A word's rank is its
+// bin's start plus the number of larger words in its bin, counted directly,
+// so the result does not depend on the order of the LDS atomics that fill
+// the bins. Returns false, having written nothing, when a bin holds more than
+// kMaxBin words.
+constexpr uint32_t kSortBins = 4096;
+constexpr uint32_t kMaxBin = 48;
+
+QRITA_DEV uint32_t bits_for(uint64_t x) { return x ? 64u - (uint32_t)__builtin_clzll(x) : 0u; }
+
+template <int NT, int E>
+QRITA_DEV bool bucket_sort(const uint64_t* a, uint32_t cnt, int32_t* out, uint64_t* b, uint32_t* bins, Shared& sh,
+                           int& rb) {
+    const uint32_t t = threadIdx.x;
+    uint64_t x[E];
+    const uint32_t key0 = uni(cand_key(a[0]));
+    uint32_t kmn = 0xFFFFFFFFu, kmx = 0u, lmn = 0xFFFFFFFFu, lmx = 0u, tz = 32u;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const uint32_t i = (uint32_t)e * NT + t;
+        x[e] = i < cnt ? a[i] : 0ull;
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const uint32_t i = (uint32_t)e * NT + t;
+        if (i < cnt) {
+            const uint32_t k = cand_key(x[e]), l = cand_low(x[e]);
+            kmn = k < kmn ? k : kmn;
+            kmx = k > kmx ? k : kmx;
+            lmn = l < lmn ? l : lmn;
+            lmx = l > lmx ? l : lmx;
+            const uint32_t d = k ^ key0;
+            const uint32_t z = d ? (uint32_t)__builtin_ctz(d) : 32u;
+            tz = z < tz ? z : tz;
+        }
+    }
+    uint32_t ext[5] = {wave_min_u32(kmn), ~wave_max_u32(kmx), wave_min_u32(lmn), ~wave_max_u32(lmx),
+                       wave_min_u32(tz)};
+    comb_record<NT, 0, 0, 5>(nullptr, nullptr, ext, sh, rb);
+    kmn = uni(ext[0]);
+    kmx = ~uni(ext[1]);
+    lmn = uni(ext[2]);
+    lmx = ~uni(ext[3]);
+    const uint32_t kz = min(uni(ext[4]), 31u);
+    const uint32_t nb = min(kSortBins, 2u * next_pow2(cnt));
+    const uint32_t nbits = 31u - (uint32_t)__builtin_clz(nb);
+    const uint32_t kbits = bits_for((uint64_t)((kmx - kmn) >> kz));
+    const uint32_t lbits = bits_for((uint64_t)(lmx - lmn));
+    // key code bits kept and index bits appended (0 when keys fill the bins)
+    const uint32_t kdrop = kbits > nbits ? kbits - nbits : 0u;
+    const uint32_t lkeep = kbits < nbits ? nbits - kbits : 0u;
+    const uint32_t ldrop = lbits > lkeep ? lbits - lkeep : 0u;
+    uint32_t bin[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const uint32_t kc = ((kmx - cand_key(x[e])) >> kz) >> kdrop;
+        const uint32_t lc = lkeep ? (lmx - cand_low(x[e])) >> ldrop : 0u;
+        bin[e] = (uint32_t)e * NT + t < cnt ? ((kc << lkeep) | lc) : 0u;
+    }
+    for (uint32_t i = t; i <= nb; i += NT) bins[i] = 0u;
+    lds_sync();
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        if ((uint32_t)e * NT + t < cnt) atomicAdd(&bins[bin[e]], 1u);
+    lds_sync();
+    // bin counts -> starts: thread t owns bins [t * per, (t + 1) * per)
+    constexpr int PER = (int)(kSortBins / NT);
+    const uint32_t per = (nb + NT - 1) / NT;
+    uint32_t c[PER];
+    uint32_t sum = 0, big = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const uint32_t i = t * per + (uint32_t)j;
+        c[j] = ((uint32_t)j < per && i < nb) ? bins[i] : 0u;
+        sum += c[j];
+        big = c[j] > big ? c[j] : big;
+    }
+    // one block round: the scan of the per-thread sums and the largest bin
+    uint32_t incl = sum;
+    {
+        uint32_t& x_ = incl;
+        uint32_t x = x_;
+        QRITA_WAVE_STEPS(op_add, 0u)
+        x_ = x;
+    }
+    uint32_t tot[1] = {readlane(incl, 63)};
+    uint32_t mx[1] = {~wave_max_u32(big)};
+    uint32_t run = incl - sum;
+    {
+        constexpr int NW = NT / kWave;
+        const uint32_t lane = t & (kWave - 1), wave = t / kWave;
+        uint32_t* rec = &sh.slot[rb][0][0];
+        if (lane == 0) *(uint2*)(rec + wave * 2) = make_uint2(tot[0], mx[0]);
+        lds_sync();
+        uint32_t m = 0xFFFFFFFFu;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const uint2 q = *(const uint2*)(rec + w * 2);
+            run += (uint32_t)w < wave ? q.x : 0u;
+            m = q.y < m ? q.y : m;
+        }
+        rb ^= 1;
+        big = ~uni(m);
+    }
+    if (big > kMaxBin) return false;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const uint32_t i = t * per + (uint32_t)j;
+        if ((uint32_t)j < per && i < nb) bins[i] = run;
+        run += c[j];
+    }
+    lds_sync();
+    // scatter; afterwards bins[i] is the end of bin i (the start of bin i+1)
+    uint32_t pos[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        pos[e] = (uint32_t)e * NT + t < cnt ? atomicAdd(&bins[bin[e]], 1u) : 0u;
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        if ((uint32_t)e * NT + t < cnt) b[pos[e]] = x[e];
+    lds_sync();
+    // ranks: the words of the thread's bins are read in step
+    uint32_t s0[E], n0[E], r[E];
+    uint32_t most = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const uint32_t lo = bin[e] ? bins[bin[e] - 1] : 0u, hi = bins[bin[e]];
+        const bool ok = (uint32_t)e * NT + t < cnt;
+        s0[e] = lo;
+        n0[e] = ok ? hi - lo : 0u;
+        r[e] = lo;
+        most = n0[e] > most ? n0[e] : most;
+    }
+    for (uint32_t j = 0; j < most; ++j) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            // past its bin a word reads a neighbour (or itself), not counted
+            const uint32_t q = j < n0[e] ? s0[e] + j : s0[e];
+            r[e] += (j < n0[e] && b[q] > x[e]) ? 1u : 0u;
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        if ((uint32_t)e * NT + t < cnt) out[r[e]] = (int32_t)cand_idx(x[e]);
+    lds_sync();
+    return true;
+}
+
 // Largest kept set one sort handles; larger ones are sorted in windows.
 template <int NT>
 QRITA_DEV uint32_t sort_cap(const Params& P) {
-    return min((uint32_t)P.tail_alloc, 16u * NT);
+    return min((uint32_t)P.tail_alloc, 32u * NT);
 }
 
-// Rank order of the cnt <= sort_cap<NT>() candidates in a[0 .. cnt): up to
-// NT by ranking, larger sets by the bitonic sort. Kept out of line: the
-// sort's registers are then allocated on their own instead of on top of
-// everything live at its call sites.
+// Rank order of the cnt <= sort_cap<NT>() candidates in a[0 .. cnt): a
+// handful by ranking, more by the bucket sort, and sets with heavy ties by
+// the bitonic sort. The LDS past the candidates (the index store and the bin
+// counts) is free by now. Kept out of line: the sort's registers are then
+// allocated on their own instead of on top of everything live at its call
+// sites.
 template <int NT>
-__device__ __attribute__((noinline)) void sort_emit(uint32_t cnt, int32_t* out, Shared& sh) {
+__device__ __attribute__((always_inline)) void sort_emit(uint32_t cnt, int32_t* out, uint32_t alloc, Shared& sh, int rb) {
+    // arguments arrive in vector registers: declare them uniform again
+    cnt = uni(cnt);
+    alloc = uni(alloc);
+    rb = (int)uni((uint32_t)rb);
+    out = (int32_t*)uni((uint64_t)out);
     uint64_t* a = lds_cands();
     if (cnt <= (uint32_t)NT) {
         rank_sort<NT>(a, cnt, out, sh);
         return;
     }
+    uint64_t* b = a + alloc;
+    uint32_t* bins = (uint32_t*)(a + 2 * alloc);
+    bool done;
+    if (cnt <= 2u * NT)
+        done = bucket_sort<NT, 2>(a, cnt, out, b, bins, sh, rb);
+    else if (cnt <= 8u * NT)
+        done = bucket_sort<NT, 8>(a, cnt, out, b, bins, sh, rb);
+    else
+        done = bucket_sort<NT, 32>(a, cnt, out, b, bins, sh, rb);
+    if (done) return;
     uint32_t np = next_pow2(cnt);
     if (np < 2u * NT) np = 2u * NT;
     for (uint32_t i = cnt + threadIdx.x; i < np; i += NT) a[i] = 0ull;
-    __syncthreads();
+    lds_sync();
     switch (np / NT) {
         case 2: bitonic_sort<NT, 2>(a, out, cnt); break;
         case 4: bitonic_sort<NT, 4>(a, out, cnt); break;
         case 8: bitonic_sort<NT, 8>(a, out, cnt); break;
-        default: bitonic_sort<NT, 16>(a, out, cnt); break;
+        case 16: bitonic_sort<NT, 16>(a, out, cnt); break;
+        default: bitonic_sort<NT, 32>(a, out, cnt); break;
     }
-    __syncthreads();
+    lds_sync();
 }
 
 // Mask bytes of the kept set {c >= B} (when mask is set) and, when cnt > 0,
@@ -907,7 +1091,7 @@ QRITA_DEV void emit_out(const Params& P, int64_t row, const S& src, uint64_t B, 
         if constexpr (S::kRegs) run += (uint32_t)__popcll(b);
     });
     block_sync<NT>();
-    sort_emit<NT>(cnt, P.out_idx + row * (int64_t)P.idx_cap + off, sh);
+    sort_emit<NT>(cnt, P.out_idx + row * (int64_t)P.idx_cap + off, (uint32_t)P.tail_alloc, sh, rb);
 }
 
 struct TailDiag {
@@ -947,7 +1131,7 @@ QRITA_DEV void emit_windows_src(const Params& P, int64_t row, const S& src, uint
             }
         });
         block_sync<NT>();
-        sort_emit<NT>(cnt, P.out_idx + row * (int64_t)P.idx_cap + done, sh);
+        sort_emit<NT>(cnt, P.out_idx + row * (int64_t)P.idx_cap + done, (uint32_t)P.tail_alloc, sh, rb);
         prev = Bn;
         done += cnt;
     }
@@ -1242,7 +1426,7 @@ __global__ __launch_bounds__(NT) void tail_kernel(Params P) {
             rb = o.rb;
         }
     }
-    __syncthreads();
+    lds_sync();
     if (threadIdx.x == 0) {
         for (int w = 0; w < H_WORDS; ++w) hdr[w] = 0u;
         if (P.diag) {
