@@ -249,8 +249,8 @@ QRITA_DEV void load_sample(const void* rowp, int32_t V, float x[8], bool in[8]) 
 
 
 template <int THREADS, bool BF16>
-QRITA_DEV Thresh compute_threshold(const Params& P, const RowMode& md, const void* rowp, Shared& sh,
-                                   int& rb) {
+QRITA_DEV Thresh compute_threshold(const Params& P, const RowMode& md, const void* rowp, const float (&x)[8],
+                                   const bool (&in)[8], float c0, Shared& sh, int& rb) {
     constexpr int NW = THREADS / kWave;
     const float kInf = __builtin_inff();
     Thresh th{kInf, kInf, false, 0u, 0.0f};
@@ -258,12 +258,21 @@ QRITA_DEV Thresh compute_threshold(const Params& P, const RowMode& md, const voi
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int32_t V = P.vocab;
     for (int i = threadIdx.x; i < kHistBins; i += THREADS) sh.hist[i] = 0u;
-    float x[8];
-    bool in[8];
-    load_sample<BF16>(rowp, V, x, in);
+    // the table entries depend on K, p and V only: read them while the sample
+    // is in flight
+    const float cap = qrita_lut_k[lut_k_index(1.0f / (float)V)];
+    float tab;
+    if (md.K_t > 0) {
+        tab = qrita_lut_k[lut_k_index((float)md.K_t / (float)V)];
+    } else {
+        const float s = 1.0f - md.p;
+        const float f = floorf((log2f(s) - QRITA_LUT_P_MIN) * QRITA_LUT_P_STEPS);
+        const int i = (int)fminf(fmaxf(f, 0.0f), (float)(QRITA_LUT_P_N - 1));
+        tab = qrita_lut_p[i];
+    }
+    asm volatile("" ::"s"(cap), "s"(tab));
     // mean, variance and range of the finite sample values in one reduction
-    // (moments about the row's first logit, fixed reduction order)
-    float c0 = load_value<BF16>(rowp, 0);
+    // (moments about the row's first logit c0, fixed reduction order)
     c0 = __builtin_isfinite(c0) ? c0 : 0.0f;
     float s1 = 0.0f, s2 = 0.0f;
     uint32_t nf = 0, kmn = 0xFFFFFFFFu, kmx = 0u;
@@ -311,16 +320,12 @@ QRITA_DEV Thresh compute_threshold(const Params& P, const RowMode& md, const voi
         t = -kInf;
     } else {
         float delta;
-        const float cap = qrita_lut_k[lut_k_index(1.0f / (float)V)];
         if (md.K_t > 0) {
-            delta = qrita_lut_k[lut_k_index((float)md.K_t / (float)V)];
+            delta = tab;
         } else {
             // top-p: softmax mass of N(mu, sigma^2) above t is
             // 1 - Phi((t - mu)/sigma - sigma); keep at least p of it, less a margin.
-            const float s = 1.0f - md.p;
-            const float f = floorf((log2f(s) - QRITA_LUT_P_MIN) * QRITA_LUT_P_STEPS);
-            const int i = (int)fminf(fmaxf(f, 0.0f), (float)(QRITA_LUT_P_N - 1));
-            delta = fminf(sigma + qrita_lut_p[i] - 0.5f, cap);
+            delta = fminf(sigma + tab - 0.5f, cap);
         }
         t = mu + P.delta_scale * delta * sigma;
     }
@@ -604,14 +609,22 @@ __global__ __launch_bounds__(THREADS) void pass1_kernel(Params P) {
     int64_t e1 = A + (int64_t)(slice + 1) * P.slice_len;
     if (slice + 1 == (uint32_t)P.slices || e1 > V) e1 = V;
     if (e0 > V) e0 = V;
-    // the first full tile is loaded before the threshold is known
+    // a2: every slice computes the same threshold from the same sample, whose
+    // loads are issued first; the first full tile is loaded before the
+    // threshold is known
+    float xs[8];
+    bool ins[8];
+    float c0 = 0.0f;
+    if (md.need_cand) {
+        load_sample<BF16>(rowp, V, xs, ins);
+        c0 = load_value<BF16>(rowp, 0);
+    }
     float f0[16];
     {
         const int64_t a = aligned_start(roff, e0, e1);
         if (e1 - a >= (int64_t)THREADS * 16) load_tile<THREADS, BF16>(rowp, a, f0);
     }
-    // a2: every slice computes the same threshold from the same sample
-    const Thresh th = compute_threshold<THREADS, BF16>(P, md, rowp, sh, rb);
+    const Thresh th = compute_threshold<THREADS, BF16>(P, md, rowp, xs, ins, c0, sh, rb);
     if (slice == 0 && threadIdx.x == 0) {
         hdr[H_T] = __float_as_uint(th.t);
         hdr[H_TC] = __float_as_uint(th.tc);

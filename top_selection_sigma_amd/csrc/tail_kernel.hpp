@@ -838,24 +838,83 @@ QRITA_DEV void bitonic_sort(uint64_t* a, int32_t* out, uint32_t cnt) {
     }
 }
 
-// Bucket sort, descending, of the cnt <= E * NT distinct words a[0 .. cnt)
-// into out[rank] = index. Thread t holds words e * NT + t in registers. A
-// word's bin orders it by key first: keys are coded exactly as
-// (kmax - key) >> z, z the number of low bits all keys share (16 for bf16
-// logits), and when the codes need fewer bits than there are bins, the
-// remaining bits split each key by index (lmax - low), so tie groups spread
-// over several bins. Bins ascend as words descend. A word's rank is its
-// bin's start plus the number of larger words in its bin, counted directly,
-// so the result does not depend on the order of the LDS atomics that fill
-// the bins. Returns false, having written nothing, when a bin holds more than
-// kMaxBin words.
+// Exclusive prefix sum, in place, of the n <= kSortBins counts v[0 .. n)
+// (thread t owns entries [t * per, (t + 1) * per)); v[n] becomes the total.
+// Returns the largest count (uniform). One block round.
 constexpr uint32_t kSortBins = 4096;
-constexpr uint32_t kMaxBin = 48;
+
+template <int NT>
+QRITA_DEV uint32_t scan_counts(uint32_t* v, uint32_t n, Shared& sh, int& rb) {
+    constexpr int PER = (int)(kSortBins / NT);
+    const uint32_t t = threadIdx.x;
+    const uint32_t per = (n + NT - 1) / NT;
+    uint32_t c[PER];
+    uint32_t sum = 0, big = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const uint32_t i = t * per + (uint32_t)j;
+        c[j] = ((uint32_t)j < per && i < n) ? v[i] : 0u;
+        sum += c[j];
+        big = c[j] > big ? c[j] : big;
+    }
+    uint32_t incl = sum;
+    {
+        uint32_t x = incl;
+        QRITA_WAVE_STEPS(op_add, 0u)  // inclusive prefix over the wave
+        incl = x;
+    }
+    const uint32_t wtot = readlane(incl, 63), wbig = wave_max_u32(big);
+    uint32_t run = incl - sum;
+    uint32_t total = 0;
+    {
+        constexpr int NW = NT / kWave;
+        const uint32_t lane = t & (kWave - 1), wave = t / kWave;
+        uint32_t* rec = &sh.slot[rb][0][0];
+        if (lane == 0) *(uint2*)(rec + wave * 2) = make_uint2(wtot, wbig);
+        lds_sync();
+        uint32_t m = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const uint2 q = *(const uint2*)(rec + w * 2);
+            run += (uint32_t)w < wave ? q.x : 0u;
+            total += q.x;
+            m = q.y > m ? q.y : m;
+        }
+        rb ^= 1;
+        big = uni(m);
+    }
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const uint32_t i = t * per + (uint32_t)j;
+        if ((uint32_t)j < per && i < n) v[i] = run;
+        run += c[j];
+    }
+    if (t == 0) v[n] = uni(total);
+    lds_sync();
+    return big;
+}
+
+// Bucket sort, descending, of the cnt <= E * NT distinct words a[0 .. cnt)
+// into out[rank] = index. Thread t holds words e * NT + t in registers.
+//
+// Bins ascend as words descend. Keys are coded exactly as (kmax - key) >> z,
+// z the number of low bits all keys share (16 for bf16 logits), coarsened by
+// dropping low code bits if the codes outnumber the bins. Within a code,
+// words spread by a sub-coordinate: the dropped code bits, then the index
+// (lmax - low), so tie groups spread too. First every code gets the same
+// number of bins; if a bin then holds more than kMaxBin words, each code
+// instead gets a run of bins in proportion to how many words it holds (from
+// a histogram over the codes). A word's rank is its bin's start plus the
+// number of larger words in its bin, counted directly, so the result does
+// not depend on the order of the LDS atomics that fill the bins. Returns
+// false, having written nothing, when a bin still holds more than kMaxBin
+// words.
+constexpr uint32_t kMaxBin = 96;
 
 QRITA_DEV uint32_t bits_for(uint64_t x) { return x ? 64u - (uint32_t)__builtin_clzll(x) : 0u; }
 
 template <int NT, int E>
-QRITA_DEV bool bucket_sort(const uint64_t* a, uint32_t cnt, int32_t* out, uint64_t* b, uint32_t* bins, Shared& sh,
+QRITA_DEV bool bucket_sort(uint64_t* a, uint32_t cnt, int32_t* out, uint64_t* b, uint32_t* bins, Shared& sh,
                            int& rb) {
     const uint32_t t = threadIdx.x;
     uint64_t x[E];
@@ -890,18 +949,31 @@ QRITA_DEV bool bucket_sort(const uint64_t* a, uint32_t cnt, int32_t* out, uint64
     const uint32_t kz = min(uni(ext[4]), 31u);
     const uint32_t nb = min(kSortBins, 2u * next_pow2(cnt));
     const uint32_t nbits = 31u - (uint32_t)__builtin_clz(nb);
-    const uint32_t kbits = bits_for((uint64_t)((kmx - kmn) >> kz));
+    const uint32_t fine_max = (kmx - kmn) >> kz;
+    const uint32_t cbits = bits_for((uint64_t)fine_max);
+    const uint32_t kdrop = cbits > nbits ? cbits - nbits : 0u;
+    const uint32_t ncodes = (fine_max >> kdrop) + 1u;
     const uint32_t lbits = bits_for((uint64_t)(lmx - lmn));
-    // key code bits kept and index bits appended (0 when keys fill the bins)
-    const uint32_t kdrop = kbits > nbits ? kbits - nbits : 0u;
-    const uint32_t lkeep = kbits < nbits ? nbits - kbits : 0u;
-    const uint32_t ldrop = lbits > lkeep ? lbits - lkeep : 0u;
+    // sub-coordinate: dropped code bits, then the index, within 48 bits
+    const uint32_t sfull = kdrop + lbits;
+    const uint32_t scut = sfull > 48u ? sfull - 48u : 0u;
+    const uint32_t sbits = sfull - scut;
+    uint32_t code[E];
+    uint64_t sub[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const uint32_t fine = (kmx - cand_key(x[e])) >> kz;
+        code[e] = fine >> kdrop;
+        const uint64_t dropped = kdrop ? (uint64_t)(fine & ((1u << kdrop) - 1u)) : 0ull;
+        sub[e] = ((dropped << lbits) | (uint64_t)(lmx - cand_low(x[e]))) >> scut;
+    }
+    // every code the same run of bins: code bits, then the top sub bits
+    const uint32_t lkeep = nbits - (cbits - kdrop);
     uint32_t bin[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-        const uint32_t kc = ((kmx - cand_key(x[e])) >> kz) >> kdrop;
-        const uint32_t lc = lkeep ? (lmx - cand_low(x[e])) >> ldrop : 0u;
-        bin[e] = (uint32_t)e * NT + t < cnt ? ((kc << lkeep) | lc) : 0u;
+        const uint32_t sc = lkeep ? (uint32_t)(sub[e] >> (sbits > lkeep ? sbits - lkeep : 0u)) : 0u;
+        bin[e] = (uint32_t)e * NT + t < cnt ? ((code[e] << lkeep) | sc) : 0u;
     }
     for (uint32_t i = t; i <= nb; i += NT) bins[i] = 0u;
     lds_sync();
@@ -909,85 +981,77 @@ QRITA_DEV bool bucket_sort(const uint64_t* a, uint32_t cnt, int32_t* out, uint64
     for (int e = 0; e < E; ++e)
         if ((uint32_t)e * NT + t < cnt) atomicAdd(&bins[bin[e]], 1u);
     lds_sync();
-    // bin counts -> starts: thread t owns bins [t * per, (t + 1) * per)
-    constexpr int PER = (int)(kSortBins / NT);
-    const uint32_t per = (nb + NT - 1) / NT;
-    uint32_t c[PER];
-    uint32_t sum = 0, big = 0;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-        const uint32_t i = t * per + (uint32_t)j;
-        c[j] = ((uint32_t)j < per && i < nb) ? bins[i] : 0u;
-        sum += c[j];
-        big = c[j] > big ? c[j] : big;
-    }
-    // one block round: the scan of the per-thread sums and the largest bin
-    uint32_t incl = sum;
-    {
-        uint32_t& x_ = incl;
-        uint32_t x = x_;
-        QRITA_WAVE_STEPS(op_add, 0u)
-        x_ = x;
-    }
-    uint32_t tot[1] = {readlane(incl, 63)};
-    uint32_t mx[1] = {~wave_max_u32(big)};
-    uint32_t run = incl - sum;
-    {
-        constexpr int NW = NT / kWave;
-        const uint32_t lane = t & (kWave - 1), wave = t / kWave;
-        uint32_t* rec = &sh.slot[rb][0][0];
-        if (lane == 0) *(uint2*)(rec + wave * 2) = make_uint2(tot[0], mx[0]);
+    uint32_t big = scan_counts<NT>(bins, nb, sh, rb);
+    if (big > kMaxBin) {
+        // runs of bins in proportion to the codes' sizes; the code histogram
+        // sits in the second buffer (free until the scatter)
+        uint32_t* hc = (uint32_t*)b;
+        for (uint32_t i = t; i <= ncodes; i += NT) hc[i] = 0u;
         lds_sync();
-        uint32_t m = 0xFFFFFFFFu;
 #pragma unroll
-        for (int w = 0; w < NW; ++w) {
-            const uint2 q = *(const uint2*)(rec + w * 2);
-            run += (uint32_t)w < wave ? q.x : 0u;
-            m = q.y < m ? q.y : m;
+        for (int e = 0; e < E; ++e)
+            if ((uint32_t)e * NT + t < cnt) atomicAdd(&hc[code[e]], 1u);
+        lds_sync();
+        scan_counts<NT>(hc, ncodes, sh, rb);
+        const float ratio = (float)nb / (float)cnt;
+        auto first = [&](uint32_t c) {
+            if (c >= ncodes) return nb;
+            const uint32_t f = (uint32_t)((float)hc[c] * ratio);
+            return f < nb - 1u ? f : nb - 1u;
+        };
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const uint32_t f0 = first(code[e]), nsub = first(code[e] + 1u) - f0;
+            const uint32_t off = sbits ? (uint32_t)((sub[e] * nsub) >> sbits) : 0u;
+            bin[e] = (uint32_t)e * NT + t < cnt ? f0 + off : 0u;
         }
-        rb ^= 1;
-        big = ~uni(m);
-    }
-    if (big > kMaxBin) return false;
+        for (uint32_t i = t; i <= nb; i += NT) bins[i] = 0u;
+        lds_sync();  // the code starts are read before the scatter reuses the buffer
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-        const uint32_t i = t * per + (uint32_t)j;
-        if ((uint32_t)j < per && i < nb) bins[i] = run;
-        run += c[j];
+        for (int e = 0; e < E; ++e)
+            if ((uint32_t)e * NT + t < cnt) atomicAdd(&bins[bin[e]], 1u);
+        lds_sync();
+        big = scan_counts<NT>(bins, nb, sh, rb);
+        if (big > kMaxBin) return false;
     }
-    lds_sync();
-    // scatter; afterwards bins[i] is the end of bin i (the start of bin i+1)
+    // scatter, with each word's bin beside it (in the first buffer, whose
+    // words are all in registers now); afterwards bins[i] is the end of bin i
+    uint32_t* binp = (uint32_t*)a;
     uint32_t pos[E];
 #pragma unroll
     for (int e = 0; e < E; ++e)
         pos[e] = (uint32_t)e * NT + t < cnt ? atomicAdd(&bins[bin[e]], 1u) : 0u;
 #pragma unroll
-    for (int e = 0; e < E; ++e)
-        if ((uint32_t)e * NT + t < cnt) b[pos[e]] = x[e];
-    lds_sync();
-    // ranks: the words of the thread's bins are read in step
-    uint32_t s0[E], n0[E], r[E];
-    uint32_t most = 0;
-#pragma unroll
     for (int e = 0; e < E; ++e) {
-        const uint32_t lo = bin[e] ? bins[bin[e] - 1] : 0u, hi = bins[bin[e]];
-        const bool ok = (uint32_t)e * NT + t < cnt;
-        s0[e] = lo;
-        n0[e] = ok ? hi - lo : 0u;
-        r[e] = lo;
-        most = n0[e] > most ? n0[e] : most;
-    }
-    for (uint32_t j = 0; j < most; ++j) {
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-            // past its bin a word reads a neighbour (or itself), not counted
-            const uint32_t q = j < n0[e] ? s0[e] + j : s0[e];
-            r[e] += (j < n0[e] && b[q] > x[e]) ? 1u : 0u;
+        if ((uint32_t)e * NT + t < cnt) {
+            b[pos[e]] = x[e];
+            binp[pos[e]] = bin[e];
         }
     }
+    lds_sync();
+    // ranks, by position in the binned order: the lanes of a wave mostly
+    // share a bin, so their scans take the same number of steps
+    for (uint32_t p = t; p < cnt; p += NT) {
+        const uint64_t w = b[p];
+        const uint32_t bi = binp[p];
+        const uint32_t s0 = bi ? bins[bi - 1] : 0u, e0 = bins[bi];
+        uint32_t r = s0;
+        if (e0 - s0 > 1) {
+            // eight words per step from 16-byte reads; words outside the bin
+            // (up to 7 past its end, still inside the LDS allocation) do not count
+            for (uint32_t q = s0 & ~1u; q < e0; q += 8) {
+                const uint4* v = (const uint4*)(b + q);
+                const uint4 v0 = v[0], v1 = v[1], v2 = v[2], v3 = v[3];
+                const uint64_t y[8] = {((uint64_t)v0.y << 32) | v0.x, ((uint64_t)v0.w << 32) | v0.z,
+                                       ((uint64_t)v1.y << 32) | v1.x, ((uint64_t)v1.w << 32) | v1.z,
+                                       ((uint64_t)v2.y << 32) | v2.x, ((uint64_t)v2.w << 32) | v2.z,
+                                       ((uint64_t)v3.y << 32) | v3.x, ((uint64_t)v3.w << 32) | v3.z};
 #pragma unroll
-    for (int e = 0; e < E; ++e)
-        if ((uint32_t)e * NT + t < cnt) out[r[e]] = (int32_t)cand_idx(x[e]);
+                for (int u = 0; u < 8; ++u) r += (q + u >= s0 && q + u < e0 && y[u] > w) ? 1u : 0u;
+            }
+        }
+        out[r] = (int32_t)cand_idx(w);
+    }
     lds_sync();
     return true;
 }
