@@ -10,21 +10,20 @@
 //         truncated set Z_t) as candidates in the row's list, zero-fills the
 //         mask slice and, for top-p-only rows, accumulates the softmax mass
 //         of the dropped logits (§1, "Resultado": a single pass);
-//   tail (one workgroup per row, see tail_kernel; the row's candidates are
+//   tail (one workgroup per row, tail_kernel.hpp; the row's candidates are
 //   held in registers while the searches run):
 //     a4  truncation hit test: |Z_t| >= K (or, for top-p, Z_t holds mass p);
 //         on a miss the search falls back to the full row (§1);
 //     a5  quaternary pivot search over the candidates: three pivots at
-//         25/50/75 % of the search range per iteration, counts by wavefront
-//         ballot/popcount, and for each pivot the smallest key above it (z_mn)
-//         with its multiplicity (N_zmn); the search stops once
+//         25/50/75 % of the search range per iteration, counts above each,
+//         and for each pivot the smallest key above it (z_mn) with its
+//         multiplicity (N_zmn); the search stops once
 //         #{> z_mn} < K <= #{>= z_mn} (§2);
 //     a6  the same search over softmax mass for top-p;
 //     a7  duplicate resolution: the boundary duplicates kept are the lowest
-//         vocabulary indices, found by a second quaternary search over the
-//         indices of the tied candidates; then the mask is set and the kept
-//         indices are written in rank order ("Pipeline": duplicate-handling
-//         mask generation).
+//         vocabulary indices; then the mask is set and the kept indices are
+//         written in rank order ("Pipeline": duplicate-handling mask
+//         generation).
 #pragma once
 
 #include <type_traits>
