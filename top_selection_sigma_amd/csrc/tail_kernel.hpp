@@ -728,12 +728,25 @@ QRITA_DEV uint32_t next_pow2(uint32_t x) {
     return p;
 }
 
+// Where a sort puts the candidate of rank r: index r of the index output
+// (r < lout) and, for r < lmask, its mask byte.
+struct RankOut {
+    int32_t* out;
+    uint32_t lout;
+    uint8_t* mrow;
+    uint32_t lmask;
+    QRITA_DEV void put(uint32_t r, uint32_t idx) const {
+        if (r < lout) out[r] = (int32_t)idx;
+        if (r < lmask) mrow[idx] = 1;
+    }
+};
+
 // Up to NT entries: each entry's rank is the number of larger entries,
 // counted by NT / next_pow2(cnt) threads per entry over a share of the
 // entries each, the shares added in LDS. The entries are read eight at a time
 // (zero padding after the last one is below every entry).
 template <int NT>
-QRITA_DEV void rank_sort(uint64_t* a, uint32_t cnt, int32_t* out, Shared& sh) {
+QRITA_DEV void rank_sort(uint64_t* a, uint32_t cnt, const RankOut& ro, Shared& sh) {
     const uint32_t P = (uint32_t)NT / next_pow2(cnt);
     const uint32_t t = threadIdx.x, e = t / P, q = t % P;
     const uint32_t span = (((cnt + P - 1) / P) + 7u) & ~7u;
@@ -759,7 +772,7 @@ QRITA_DEV void rank_sort(uint64_t* a, uint32_t cnt, int32_t* out, Shared& sh) {
         if (above) atomicAdd(&sh.ties[e], above);
     }
     lds_sync();
-    if (q == 0 && e < cnt) out[sh.ties[e]] = (int32_t)cand_idx(x);
+    if (q == 0 && e < cnt) ro.put(sh.ties[e], cand_idx(x));
 }
 
 // Bitonic sort, descending, of the NT * E entries a[0 .. NT*E) (any order),
@@ -769,7 +782,7 @@ QRITA_DEV void rank_sort(uint64_t* a, uint32_t cnt, int32_t* out, Shared& sh) {
 // (E <= j < 64 E) or across waves through LDS (j >= 64 E; element (t, e) at
 // a[e * NT + t], so the accesses of a wave are consecutive).
 template <int NT, int E>
-QRITA_DEV void bitonic_sort(uint64_t* a, int32_t* out, uint32_t cnt) {
+QRITA_DEV void bitonic_sort(uint64_t* a, const RankOut& ro, uint32_t cnt) {
     constexpr uint32_t NP = (uint32_t)NT * E;
     const uint32_t t = tid_here() % NT;
     uint64_t x[E];
@@ -834,7 +847,7 @@ QRITA_DEV void bitonic_sort(uint64_t* a, int32_t* out, uint32_t cnt) {
 #pragma unroll
     for (int e = 0; e < E; ++e) {
         const uint32_t g = t * E + e;
-        if (g < cnt) out[g] = (int32_t)cand_idx(x[e]);
+        if (g < cnt) ro.put(g, cand_idx(x[e]));
     }
 }
 
@@ -914,7 +927,7 @@ constexpr uint32_t kMaxBin = 96;
 QRITA_DEV uint32_t bits_for(uint64_t x) { return x ? 64u - (uint32_t)__builtin_clzll(x) : 0u; }
 
 template <int NT, int E>
-QRITA_DEV bool bucket_sort(uint64_t* a, uint32_t cnt, int32_t* out, uint64_t* b, uint32_t* bins, Shared& sh,
+QRITA_DEV bool bucket_sort(uint64_t* a, uint32_t cnt, const RankOut& ro, uint64_t* b, uint32_t* bins, Shared& sh,
                            int& rb) {
     const uint32_t t = threadIdx.x;
     uint64_t x[E];
@@ -1050,7 +1063,7 @@ QRITA_DEV bool bucket_sort(uint64_t* a, uint32_t cnt, int32_t* out, uint64_t* b,
                 for (int u = 0; u < 8; ++u) r += (q + u >= s0 && q + u < e0 && y[u] > w) ? 1u : 0u;
             }
         }
-        out[r] = (int32_t)cand_idx(w);
+        ro.put(r, cand_idx(w));
     }
     lds_sync();
     return true;
@@ -1069,37 +1082,34 @@ QRITA_DEV uint32_t sort_cap(const Params& P) {
 // allocated on their own instead of on top of everything live at its call
 // sites.
 template <int NT>
-__device__ __attribute__((always_inline)) void sort_emit(uint32_t cnt, int32_t* out, uint32_t alloc, Shared& sh, int rb) {
-    // arguments arrive in vector registers: declare them uniform again
+__device__ __attribute__((always_inline)) void sort_emit(uint32_t cnt, RankOut ro, uint32_t alloc, Shared& sh, int rb) {
     cnt = uni(cnt);
     alloc = uni(alloc);
-    rb = (int)uni((uint32_t)rb);
-    out = (int32_t*)uni((uint64_t)out);
     uint64_t* a = lds_cands();
     if (cnt <= (uint32_t)NT) {
-        rank_sort<NT>(a, cnt, out, sh);
+        rank_sort<NT>(a, cnt, ro, sh);
         return;
     }
     uint64_t* b = a + alloc;
     uint32_t* bins = (uint32_t*)(a + 2 * alloc);
     bool done;
     if (cnt <= 2u * NT)
-        done = bucket_sort<NT, 2>(a, cnt, out, b, bins, sh, rb);
+        done = bucket_sort<NT, 2>(a, cnt, ro, b, bins, sh, rb);
     else if (cnt <= 8u * NT)
-        done = bucket_sort<NT, 8>(a, cnt, out, b, bins, sh, rb);
+        done = bucket_sort<NT, 8>(a, cnt, ro, b, bins, sh, rb);
     else
-        done = bucket_sort<NT, 32>(a, cnt, out, b, bins, sh, rb);
+        done = bucket_sort<NT, 32>(a, cnt, ro, b, bins, sh, rb);
     if (done) return;
     uint32_t np = next_pow2(cnt);
     if (np < 2u * NT) np = 2u * NT;
     for (uint32_t i = cnt + threadIdx.x; i < np; i += NT) a[i] = 0ull;
     lds_sync();
     switch (np / NT) {
-        case 2: bitonic_sort<NT, 2>(a, out, cnt); break;
-        case 4: bitonic_sort<NT, 4>(a, out, cnt); break;
-        case 8: bitonic_sort<NT, 8>(a, out, cnt); break;
-        case 16: bitonic_sort<NT, 16>(a, out, cnt); break;
-        default: bitonic_sort<NT, 32>(a, out, cnt); break;
+        case 2: bitonic_sort<NT, 2>(a, ro, cnt); break;
+        case 4: bitonic_sort<NT, 4>(a, ro, cnt); break;
+        case 8: bitonic_sort<NT, 8>(a, ro, cnt); break;
+        case 16: bitonic_sort<NT, 16>(a, ro, cnt); break;
+        default: bitonic_sort<NT, 32>(a, ro, cnt); break;
     }
     lds_sync();
 }
@@ -1155,7 +1165,56 @@ QRITA_DEV void emit_out(const Params& P, int64_t row, const S& src, uint64_t B, 
         if constexpr (S::kRegs) run += (uint32_t)__popcll(b);
     });
     block_sync<NT>();
-    sort_emit<NT>(cnt, P.out_idx + row * (int64_t)P.idx_cap + off, (uint32_t)P.tail_alloc, sh, rb);
+    sort_emit<NT>(cnt, RankOut{P.out_idx + row * (int64_t)P.idx_cap + off, cnt, nullptr, 0u}, (uint32_t)P.tail_alloc,
+                  sh, rb);
+}
+
+// The candidates c >= lo_w (every candidate at or above the final boundary
+// value, so the kept set and its boundary duplicates) gathered into LDS and
+// sorted; the sort then writes the mask bytes of ranks < lmask and the
+// indices of ranks < lout directly, so the boundary duplicates are resolved
+// by their rank order (lower index first) without a separate search. The
+// caller guarantees at most sort_cap<NT>() such candidates.
+template <int NT, class S>
+QRITA_DEV void emit_ranked(const Params& P, int64_t row, const S& src, uint64_t lo_w, uint32_t lmask,
+                           uint32_t lout, Shared& sh, int& rb) {
+    const uint32_t lk = cand_key(lo_w), ll = cand_low(lo_w);
+    auto takes = [&](uint32_t key, uint32_t lw) { return key != 0 && (key > lk || (key == lk && lw >= ll)); };
+    uint64_t* a = lds_cands();
+    const uint32_t cap = sort_cap<NT>(P);
+    uint32_t run = 0, cnt = 0;
+    if constexpr (S::kRegs) {
+        uint32_t c = 0;
+        src.template visit<true, false>(
+            [&](uint32_t key, uint32_t lw, float, int) { c += (uint32_t)__popcll(__ballot(takes(key, lw))); });
+        run = wave_prefix<NT>(c, cnt, sh, rb);
+    } else {
+        block_sync<NT>();
+        if (threadIdx.x == 0) sh.gather_n = 0;
+    }
+    block_sync<NT>();  // the masses in the gather buffer are no longer read
+    const uint32_t lane = tid_here() & (kWave - 1);
+    src.template visit<true, false>([&](uint32_t key, uint32_t lw, float, int) {
+        const bool take = takes(key, lw);
+        const uint64_t b = __ballot(take);
+        uint32_t base = run;
+        if constexpr (!S::kRegs) {
+            if (b) {
+                uint32_t r0 = 0;
+                if (lane == 0) r0 = atomicAdd(&sh.gather_n, (uint32_t)__popcll(b));
+                base = readlane(r0, 0);
+            }
+        }
+        const uint32_t pos = base + lanes_below(b);
+        if (take && pos < cap) a[pos] = ((uint64_t)key << 32) | lw;
+        if constexpr (S::kRegs) run += (uint32_t)__popcll(b);
+    });
+    block_sync<NT>();
+    if constexpr (!S::kRegs) cnt = uni(sh.gather_n);
+    cnt = min(cnt, cap);
+    RankOut ro{P.out_idx ? P.out_idx + row * (int64_t)P.idx_cap : nullptr, lout,
+               P.mask ? P.mask + row * (int64_t)P.vocab : nullptr, lmask};
+    sort_emit<NT>(cnt, ro, (uint32_t)P.tail_alloc, sh, rb);
 }
 
 struct TailDiag {
@@ -1195,7 +1254,8 @@ QRITA_DEV void emit_windows_src(const Params& P, int64_t row, const S& src, uint
             }
         });
         block_sync<NT>();
-        sort_emit<NT>(cnt, P.out_idx + row * (int64_t)P.idx_cap + done, (uint32_t)P.tail_alloc, sh, rb);
+        sort_emit<NT>(cnt, RankOut{P.out_idx + row * (int64_t)P.idx_cap + done, cnt, nullptr, 0u},
+                      (uint32_t)P.tail_alloc, sh, rb);
         prev = Bn;
         done += cnt;
     }
@@ -1301,10 +1361,23 @@ QRITA_DEV bool finish_row(const Params& P, int64_t row, const RowMode& md, S& sr
         ngt = mo.n_gt;
         needf = need;
     }
-    // a7: duplicate resolution at the final boundary value
-    const uint64_t B = all ? 0ull : tie_boundary<NT>(src, vf, needf, Nf, V, 0ull, sh, rb, dg.iters);
     const uint32_t L = all ? V : ngt + needf;
     const bool mask = P.mask && !md.keep_all;
+    // a7: when every candidate at or above the final boundary value fits one
+    // sort, the sort's rank order resolves the duplicates and writes the
+    // outputs
+    {
+        const bool want_idx = P.out_idx && P.idx_cap > 0;
+        const uint32_t Lout = want_idx ? (L < (uint32_t)P.idx_cap ? L : (uint32_t)P.idx_cap) : 0u;
+        const uint32_t Gn = all ? n : ngt + Nf;
+        if ((mask || Lout > 0) && Gn <= sort_cap<NT>(P)) {
+            emit_ranked<NT>(P, row, src, all ? 0ull : (uint64_t)vf << 32, mask ? L : 0u, Lout, sh, rb);
+            if (P.out_count && threadIdx.x == 0) P.out_count[row] = (int32_t)L;
+            return true;
+        }
+    }
+    // a7: duplicate resolution at the final boundary value
+    const uint64_t B = all ? 0ull : tie_boundary<NT>(src, vf, needf, Nf, V, 0ull, sh, rb, dg.iters);
     // a7: mask (pass 1 zero-filled the row; keep-all rows were filled there)
     // and the indices in rank order
     if (P.out_idx && P.idx_cap > 0) {
