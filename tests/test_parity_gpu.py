@@ -110,6 +110,18 @@ def test_small_capacities_reach_every_path(lds_cap, list_cap):
     check(x, g, oracle_for(x, 9000), 9000, f"caps {lds_cap}/{list_cap}")
 
 
+@pytest.mark.parametrize("k,list_cap", [(25000, 0), (54000, 0), (25000, 3000)])
+def test_pass1_spill_buffers(k, list_cap):
+    """A 64-entry stage with 40 % or 90 % survivors: the waves' spill buffers
+    fill and move to the row list many times per slice, tiles with more than
+    a buffer's worth spill directly, and a short list overflows inside both."""
+    import top_selection_sigma_amd as q
+
+    x = w.make_rows(4, 60000, "f32", "gauss_outliers", seed=17, k=k, p=1.0)
+    g = run_gpu(x, 64, options=q.Options(lds_cap=64, list_cap=list_cap))
+    check(x, g, oracle_for(x, 64), 64, f"spill k {k} list {list_cap}")
+
+
 def test_keep_all_rows_full_order():
     x = w.make_rows(4, 6000, "bf16", "ties16", seed=15, k=0, p=1.0)
     g = run_gpu(x, 6000)

@@ -47,17 +47,22 @@ int64_t next_pow2(int64_t x) {
 
 // Tier table (the summary's tiered block sizes, "Autotuning": large blocks
 // for full rows, small ones for truncated sets). Here it is a static function
-// of the shape: pass 1 gets enough workgroups to cover 256 CUs several times
-// with slices of at least 8192 logits, so the per-workgroup sample stays small
-// next to the streamed bytes; the tail gets one 256-thread workgroup per row
-// over the much smaller candidate set.
-Tier choose_tier(int64_t B, int64_t V, const qrita_options* o) {
+// of the shape: pass 1 gets at least 1024 workgroups (all resident together
+// on 256 CUs); from 512 rows on, long rows get up to eight slices of about
+// 64 KiB, which keeps several rounds of workgroups queued so that the CUs
+// finishing early take more, while the per-workgroup sample stays small next
+// to the streamed bytes (slices of at least 8192 logits); the tail gets one
+// 256-thread workgroup per row over the much smaller candidate set.
+Tier choose_tier(int64_t B, int64_t V, int64_t esize, const qrita_options* o) {
     Tier t;
     int64_t S = std::max<int64_t>(1, (1024 + B - 1) / B);
+    if (B >= 512) S = std::max<int64_t>(S, std::min<int64_t>(8, (V * esize + 65535) / 65536));
     S = std::min<int64_t>(S, 64);
     S = std::min<int64_t>(S, std::max<int64_t>(1, (V + 8191) / 8192));
     if (o && o->slices > 0) S = std::min<int64_t>(o->slices, std::max<int64_t>(1, V));
-    // 256-thread workgroups: 1024 of them stay resident together on 256 CUs
+    // 256-thread workgroups: 1024 of them stay resident together on 256 CUs;
+    // slices are whole tiles of 16 logits per thread (only a row's last slice
+    // ends in a part tile), and after the first they start 16-aligned
     t.threads = 256;
     const int64_t TB = (int64_t)t.threads * 16;
     int64_t L = (V + S - 1) / S;
@@ -103,7 +108,7 @@ hipError_t launch_pass1(const Params& P, const Tier& t, hipStream_t stream) {
     static hipError_t attr = hipSuccess;
     if (allow_lds(kern, once, attr) != hipSuccess) return attr;
     const int64_t groups = ((P.batch + 7) / 8) * 8 * (int64_t)t.slices;
-    const size_t lds = (size_t)t.stage_alloc * sizeof(uint64_t);
+    const size_t lds = ((size_t)t.stage_alloc + (size_t)(THREADS / qrita::kWave) * qrita::kWaveSpill) * sizeof(uint64_t);
     hipLaunchKernelGGL(kern, dim3((unsigned)groups), dim3(THREADS), lds, stream, P);
     return hipGetLastError();
 }
@@ -138,7 +143,7 @@ int select_impl(const void* logits, int64_t batch, int64_t vocab, int dtype, con
     if (!workspace || workspace_bytes < need) return QRITA_EWORKSPACE;
     if ((uintptr_t)workspace & 255u) return QRITA_EWORKSPACE;
 
-    const Tier t = choose_tier(batch, vocab, opt);
+    const Tier t = choose_tier(batch, vocab, dtype == QRITA_BF16 ? 2 : 4, opt);
     Params P;
     P.logits = logits;
     P.mask = out_mask;

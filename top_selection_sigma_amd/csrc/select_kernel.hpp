@@ -95,6 +95,7 @@ struct Shared {
     uint32_t flags;
     uint32_t gather_n;
     uint32_t u32[8];
+    uint32_t wspill[kMaxWaves];  // pass 1: entries left in each wave's spill buffer
 };
 
 extern __shared__ uint64_t qrita_dyn_lds[];
@@ -390,17 +391,52 @@ QRITA_DEV Thresh compute_threshold(const Params& P, const RowMode& md, const voi
 // a3: the single streaming pass over one slice.
 // ---------------------------------------------------------------------------
 
+// Survivors past the LDS stage. Each wave first collects them, already in
+// list form, in its own LDS buffer of kWaveSpill entries (after the stage)
+// and moves a full buffer to the row list with one reservation; what is left
+// joins the stage's reservation at the end of the slice. Only a tile whose
+// spill alone exceeds the buffer reserves list space directly.
+constexpr uint32_t kWaveSpill = 512;
+
+struct Spill {
+    uint32_t kmax;  // largest key spilled by this lane
+    uint32_t n;     // entries in this wave's buffer (wave uniform)
+};
+
+// the stage takes max(stage_cap, kSampleN) entries; the wave buffers follow
+QRITA_DEV uint64_t* wave_spill_buf(const Params& P) {
+    const uint32_t stage = (uint32_t)P.stage_cap > (uint32_t)kSampleN ? (uint32_t)P.stage_cap : (uint32_t)kSampleN;
+    return lds_cands() + stage + (threadIdx.x / kWave) * kWaveSpill;
+}
+
+// Move this wave's n buffered entries to the row list.
+QRITA_DEV void wave_spill_flush(const Params& P, int64_t row, const uint64_t* wb, uint32_t n, Shared& sh) {
+    const uint32_t lane = threadIdx.x & (kWave - 1);
+    uint32_t g = 0;
+    if (lane == 0) g = atomicAdd(&P.hdr[row * H_WORDS + H_LIST], n);
+    g = readlane(g, 0);
+    bool over = false;
+    for (uint32_t j = lane; j < n; j += kWave) {
+        const uint32_t gp = g + j;
+        if (gp < (uint32_t)P.list_cap)
+            P.glist[row * (int64_t)P.list_stride + gp] = wb[j];
+        else
+            over = true;
+    }
+    if (over) atomicOr(&sh.flags, 1u);
+}
+
 // Compact the survivors (f >= tc) of 16 logits per lane into the candidate
 // stage: wavefront ballots count them, one LDS atomic per wave reserves
 // space, mbcnt gives each lane its slot. Logit j of this lane has vocabulary
 // index idx0 + (j / VE) * vstride + (j % VE); bit j of `valid` marks it as
-// present. Survivors past the stage go straight to the row list (with their
+// present. Survivors past the stage go to the wave's spill buffer (with their
 // key, for the list's max). For top-p-only rows (REST) the dropped logits'
 // masses exp(f - tc) are summed per lane in float over the 16 and added to
 // the fixed-point `rest` once, so the total does not depend on lane order.
 template <int THREADS, bool BF16, bool REST, int VE>
 QRITA_DEV void consume16(const Params& P, int64_t row, const float f[16], uint32_t valid, uint32_t idx0,
-                         uint32_t vstride, float tc, Shared& sh, uint64_t& rest, uint32_t& spill_kmax) {
+                         uint32_t vstride, float tc, Shared& sh, uint64_t& rest, Spill& sp) {
     const uint32_t lane = threadIdx.x & (kWave - 1);
     uint32_t tot = 0;
     float dropped = 0.0f;
@@ -436,9 +472,17 @@ QRITA_DEV void consume16(const Params& P, int64_t row, const float f[16], uint32
     }
     const uint32_t spill_from = base > cap ? base : cap;
     const uint32_t nover = base + tot - spill_from;
+    uint64_t* wb = wave_spill_buf(P);
+    if (sp.n + nover > kWaveSpill) {
+        wave_spill_flush(P, row, wb, sp.n, sh);
+        sp.n = 0;
+    }
+    const bool direct = nover > kWaveSpill;
     uint32_t gbase = 0;
-    if (lane == 0) gbase = atomicAdd(&P.hdr[row * H_WORDS + H_LIST], nover);
-    gbase = readlane(gbase, 0);
+    if (direct) {
+        if (lane == 0) gbase = atomicAdd(&P.hdr[row * H_WORDS + H_LIST], nover);
+        gbase = readlane(gbase, 0);
+    }
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
         const bool s = ((valid >> j) & 1u) && f[j] >= tc;
@@ -451,43 +495,68 @@ QRITA_DEV void consume16(const Params& P, int64_t row, const float f[16], uint32
                 if (pos < cap) {
                     a[pos] = ((uint64_t)bits << 32) | idx;
                 } else {
-                    const uint32_t gp = gbase + (pos - spill_from);
+                    const uint32_t off = pos - spill_from;
                     const uint32_t key = f32_key(bits);
-                    spill_kmax = key > spill_kmax ? key : spill_kmax;
-                    if (gp < (uint32_t)P.list_cap)
-                        P.glist[row * (int64_t)P.list_stride + gp] = make_cand(key, idx);
-                    else
+                    sp.kmax = key > sp.kmax ? key : sp.kmax;
+                    const uint64_t c = make_cand(key, idx);
+                    if (!direct) {
+                        wb[sp.n + off] = c;
+                    } else if (gbase + off < (uint32_t)P.list_cap) {
+                        P.glist[row * (int64_t)P.list_stride + gbase + off] = c;
+                    } else {
                         atomicOr(&sh.flags, 1u);
+                    }
                 }
             }
             run += (uint32_t)__popcll(b);
         }
     }
+    if (!direct) sp.n += nover;
 }
 
-// One tile (THREADS * 16 logits from `tile`, all inside the slice): vector
-// loads marked non-temporal (the logits are read once) into f.
+// One tile is THREADS * 16 logits, 16 per lane in 16-byte vectors (two for
+// bf16, four for f32). Tiles are loaded raw, marked non-temporal (the logits
+// are read once), and unpacked to float only when consumed, so that several
+// tiles can be in flight per lane: kTileDepth tiles, 96 bytes of bf16 or
+// 128 bytes of f32 per lane, 96-128 KiB per CU at four workgroups.
+template <bool BF16>
+struct RawTile {
+    u32x4_t v[BF16 ? 2 : 4];
+};
+template <bool BF16>
+constexpr int kTileDepth = BF16 ? 3 : 2;
+
 template <int THREADS, bool BF16>
-QRITA_DEV void load_tile(const void* rowp, int64_t tile, float f[16]) {
+QRITA_DEV void load_raw(const void* rowp, int64_t tile, RawTile<BF16>& r) {
     constexpr int VE = BF16 ? 8 : 4;
     constexpr int NV = 16 / VE;
 #pragma unroll
     for (int q = 0; q < NV; ++q) {
         const int64_t e = tile + (int64_t)q * THREADS * VE + (int64_t)threadIdx.x * VE;
-        if (BF16) {
-            const u32x4_t w = __builtin_nontemporal_load((const u32x4_t*)((const uint16_t*)rowp + e));
-            const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+        const u32x4_t* src = BF16 ? (const u32x4_t*)((const uint16_t*)rowp + e) : (const u32x4_t*)((const float*)rowp + e);
+        r.v[q] = __builtin_nontemporal_load(src);
+    }
+}
+
+template <bool BF16>
+QRITA_DEV void unpack_tile(const RawTile<BF16>& r, float f[16]) {
+    if (BF16) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                f[q * 8 + 2 * r] = __uint_as_float(ws[r] << 16);
-                f[q * 8 + 2 * r + 1] = __uint_as_float(ws[r] & 0xFFFF0000u);
+        for (int q = 0; q < 2; ++q) {
+            const uint32_t ws[4] = {r.v[q].x, r.v[q].y, r.v[q].z, r.v[q].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                f[q * 8 + 2 * i] = __uint_as_float(ws[i] << 16);
+                f[q * 8 + 2 * i + 1] = __uint_as_float(ws[i] & 0xFFFF0000u);
             }
-        } else {
-            const f32x4_t w = __builtin_nontemporal_load((const f32x4_t*)((const float*)rowp + e));
-            f[q * 4 + 0] = w.x;
-            f[q * 4 + 1] = w.y;
-            f[q * 4 + 2] = w.z;
-            f[q * 4 + 3] = w.w;
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            f[q * 4 + 0] = __uint_as_float(r.v[q].x);
+            f[q * 4 + 1] = __uint_as_float(r.v[q].y);
+            f[q * 4 + 2] = __uint_as_float(r.v[q].z);
+            f[q * 4 + 3] = __uint_as_float(r.v[q].w);
         }
     }
 }
@@ -515,11 +584,11 @@ QRITA_DEV int64_t aligned_start(int64_t roff, int64_t e0, int64_t e1) {
     return a > e1 ? e1 : a;
 }
 
-// The streaming pass over [e0, e1); f0 holds the slice's first full tile
-// (loaded before the threshold was known) when there is one.
+// The streaming pass over [e0, e1); ring[j] holds the slice's full tile j
+// for j < kTileDepth (loaded before the threshold was known).
 template <int THREADS, bool BF16, bool REST>
 QRITA_DEV void stream_slice(const Params& P, int64_t row, int64_t e0, int64_t e1, float tc, uint8_t fill,
-                            const float (&f0)[16], Shared& sh, uint64_t& rest, uint32_t& spill_kmax) {
+                            RawTile<BF16> (&ring)[kTileDepth<BF16>], Shared& sh, uint64_t& rest, Spill& sp) {
     const int64_t roff = row * (int64_t)P.vocab;
     const void* rowp = row_ptr<BF16>(P, row);
     uint8_t* mrow = P.mask ? P.mask + roff : nullptr;
@@ -538,46 +607,73 @@ QRITA_DEV void stream_slice(const Params& P, int64_t row, int64_t e0, int64_t e1
             if (mrow) mrow[e] = fill;
         }
         if (tid < kWave)
-            consume16<THREADS, BF16, REST, 16>(P, row, f, valid, (uint32_t)e, 0u, tc, sh, rest, spill_kmax);
+            consume16<THREADS, BF16, REST, 16>(P, row, f, valid, (uint32_t)e, 0u, tc, sh, rest, sp);
     }
     constexpr int VE = BF16 ? 8 : 4;  // logits per 16-byte vector
     constexpr int NV = 16 / VE;       // vectors per thread per tile
     constexpr int TB = THREADS * 16;  // logits per tile
-    // full tiles: the next tile's loads are issued before this one is consumed
+    constexpr int D = kTileDepth<BF16>;
+    // full tiles: tile i sits in ring[i % D]; once unpacked, its slot is
+    // refilled with tile i + D
     const int64_t nfull = (e1 - a) / TB;
-    float f[16];
+    for (int64_t i0 = 0; i0 < nfull; i0 += D) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) f[j] = f0[j];
-    for (int64_t i = 0; i < nfull; ++i) {
-        const int64_t tile = a + i * TB;
-        float g[16];
-        if (i + 1 < nfull) load_tile<THREADS, BF16>(rowp, tile + TB, g);
-        if (mrow) fill_tile<THREADS, BF16>(mrow, tile, fill);
-        consume16<THREADS, BF16, REST, VE>(P, row, f, 0xFFFFu, (uint32_t)(tile + (int64_t)tid * VE),
-                                           (uint32_t)(THREADS * VE), tc, sh, rest, spill_kmax);
-#pragma unroll
-        for (int j = 0; j < 16; ++j) f[j] = g[j];
+        for (int j = 0; j < D; ++j) {
+            const int64_t i = i0 + j;
+            if (i < nfull) {
+                const int64_t tile = a + i * TB;
+                float f[16];
+                unpack_tile<BF16>(ring[j], f);
+                if (i + D < nfull) load_raw<THREADS, BF16>(rowp, tile + (int64_t)D * TB, ring[j]);
+                if (mrow) fill_tile<THREADS, BF16>(mrow, tile, fill);
+                consume16<THREADS, BF16, REST, VE>(P, row, f, 0xFFFFu, (uint32_t)(tile + (int64_t)tid * VE),
+                                                   (uint32_t)(THREADS * VE), tc, sh, rest, sp);
+            }
+        }
     }
-    // ragged last tile, element by element
+    // ragged last tile: vectors wholly inside the slice as in a full tile,
+    // the one that straddles its end element by element
     const int64_t tile = a + nfull * TB;
     if (tile < e1) {
+        float f[16];
         uint32_t valid = 0;
+        const uint64_t fill8 = 0x0101010101010101ull * fill;
 #pragma unroll
         for (int q = 0; q < NV; ++q) {
+            const int64_t ev = tile + (int64_t)q * THREADS * VE + (int64_t)tid * VE;
+            if (ev + VE <= e1) {
+                RawTile<BF16> r1;
+                const u32x4_t* src = BF16 ? (const u32x4_t*)((const uint16_t*)rowp + ev)
+                                          : (const u32x4_t*)((const float*)rowp + ev);
+                r1.v[0] = __builtin_nontemporal_load(src);
+                const uint32_t ws[4] = {r1.v[0].x, r1.v[0].y, r1.v[0].z, r1.v[0].w};
 #pragma unroll
-            for (int r = 0; r < VE; ++r) {
-                const int64_t er = tile + (int64_t)q * THREADS * VE + (int64_t)tid * VE + r;
-                if (er < e1) {
-                    f[q * VE + r] = load_value<BF16>(rowp, er);
-                    valid |= 1u << (q * VE + r);
-                    if (mrow) mrow[er] = fill;
-                } else {
-                    f[q * VE + r] = 0.0f;
+                for (int r = 0; r < VE; ++r)
+                    f[q * VE + r] = BF16 ? __uint_as_float((r & 1) ? (ws[r / 2] & 0xFFFF0000u) : (ws[r / 2] << 16))
+                                         : __uint_as_float(ws[r]);
+                valid |= ((1u << VE) - 1u) << (q * VE);
+                if (mrow) {
+                    if (BF16)
+                        __builtin_nontemporal_store(fill8, (uint64_t*)(mrow + ev));
+                    else
+                        __builtin_nontemporal_store((uint32_t)fill8, (uint32_t*)(mrow + ev));
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < VE; ++r) {
+                    const int64_t er = ev + r;
+                    if (er < e1) {
+                        f[q * VE + r] = load_value<BF16>(rowp, er);
+                        valid |= 1u << (q * VE + r);
+                        if (mrow) mrow[er] = fill;
+                    } else {
+                        f[q * VE + r] = 0.0f;
+                    }
                 }
             }
         }
         consume16<THREADS, BF16, REST, VE>(P, row, f, valid, (uint32_t)(tile + (int64_t)tid * VE),
-                                           (uint32_t)(THREADS * VE), tc, sh, rest, spill_kmax);
+                                           (uint32_t)(THREADS * VE), tc, sh, rest, sp);
     }
 }
 
@@ -585,7 +681,7 @@ QRITA_DEV void stream_slice(const Params& P, int64_t row, int64_t e0, int64_t e1
 // rows are dealt so that all slices of row r share XCD r mod 8 and therefore
 // one L2, which also holds the row list when the row's tail reads it.
 template <int THREADS, bool BF16>
-__global__ __launch_bounds__(THREADS) void pass1_kernel(Params P) {
+__global__ __launch_bounds__(THREADS, 4) void pass1_kernel(Params P) {
     __shared__ Shared sh;
     int rb = 0;
     const uint32_t g = blockIdx.x;
@@ -609,8 +705,8 @@ __global__ __launch_bounds__(THREADS) void pass1_kernel(Params P) {
     if (slice + 1 == (uint32_t)P.slices || e1 > V) e1 = V;
     if (e0 > V) e0 = V;
     // a2: every slice computes the same threshold from the same sample, whose
-    // loads are issued first; the first full tile is loaded before the
-    // threshold is known
+    // loads are issued first; the slice's first kTileDepth full tiles are in
+    // flight while the threshold is computed
     float xs[8];
     bool ins[8];
     float c0 = 0.0f;
@@ -618,10 +714,13 @@ __global__ __launch_bounds__(THREADS) void pass1_kernel(Params P) {
         load_sample<BF16>(rowp, V, xs, ins);
         c0 = load_value<BF16>(rowp, 0);
     }
-    float f0[16];
+    RawTile<BF16> ring[kTileDepth<BF16>];
     {
         const int64_t a = aligned_start(roff, e0, e1);
-        if (e1 - a >= (int64_t)THREADS * 16) load_tile<THREADS, BF16>(rowp, a, f0);
+        const int64_t nfull = (e1 - a) / ((int64_t)THREADS * 16);
+#pragma unroll
+        for (int j = 0; j < kTileDepth<BF16>; ++j)
+            if (j < nfull) load_raw<THREADS, BF16>(rowp, a + (int64_t)j * THREADS * 16, ring[j]);
     }
     const Thresh th = compute_threshold<THREADS, BF16>(P, md, rowp, xs, ins, c0, sh, rb);
     if (slice == 0 && threadIdx.x == 0) {
@@ -636,17 +735,28 @@ __global__ __launch_bounds__(THREADS) void pass1_kernel(Params P) {
     const uint8_t fill = md.keep_all ? 1 : 0;
     const bool rest_on = md.topp && !md.topk;
     uint64_t rest = 0;
-    uint32_t kmax = 0;
+    Spill sp{0u, 0u};
     if (rest_on)
-        stream_slice<THREADS, BF16, true>(P, row, e0, e1, th.tc, fill, f0, sh, rest, kmax);
+        stream_slice<THREADS, BF16, true>(P, row, e0, e1, th.tc, fill, ring, sh, rest, sp);
     else
-        stream_slice<THREADS, BF16, false>(P, row, e0, e1, th.tc, fill, f0, sh, rest, kmax);
+        stream_slice<THREADS, BF16, false>(P, row, e0, e1, th.tc, fill, ring, sh, rest, sp);
+    const uint32_t lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    if (lane == 0) sh.wspill[wave] = sp.n;
     __syncthreads();
-    // publish: the staged candidates go to the row list in one reservation,
-    // whose round trip overlaps the maximum over the stage
+    // publish: the staged candidates and what the spill buffers still hold go
+    // to the row list in one reservation, whose round trip overlaps the
+    // maximum over the stage
     const uint32_t nst = min(sh.ncand, (uint32_t)P.stage_cap);
+    uint32_t wpre = 0, wtot = 0;
+#pragma unroll
+    for (int w = 0; w < THREADS / kWave; ++w) {
+        const uint32_t q = sh.wspill[w];
+        wpre += (uint32_t)w < wave ? q : 0u;
+        wtot += q;
+    }
+    uint32_t kmax = sp.kmax;
     uint32_t gb = 0;
-    if (threadIdx.x == 0 && nst) gb = atomicAdd(&hdr[H_LIST], nst);
+    if (threadIdx.x == 0 && nst + wtot) gb = atomicAdd(&hdr[H_LIST], nst + wtot);
     constexpr int PER = kSampleN / THREADS;  // stage entries per thread (stage_cap <= 2048)
     const uint64_t* a = lds_cands();
     uint32_t keys[PER], lows[PER];
@@ -670,6 +780,16 @@ __global__ __launch_bounds__(THREADS) void pass1_kernel(Params P) {
         if (i < nst) {
             if (gb + i < (uint32_t)P.list_cap)
                 lst[gb + i] = ((uint64_t)keys[u] << 32) | lows[u];
+            else
+                over = true;
+        }
+    }
+    {
+        const uint64_t* wb = wave_spill_buf(P);
+        const uint32_t g = gb + nst + wpre;
+        for (uint32_t j = lane; j < sp.n; j += kWave) {
+            if (g + j < (uint32_t)P.list_cap)
+                lst[g + j] = wb[j];
             else
                 over = true;
         }
