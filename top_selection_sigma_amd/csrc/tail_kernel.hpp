@@ -971,22 +971,22 @@ QRITA_DEV bool bucket_sort(uint64_t* a, uint32_t cnt, const RankOut& ro, uint64_
     const uint32_t sfull = kdrop + lbits;
     const uint32_t scut = sfull > 48u ? sfull - 48u : 0u;
     const uint32_t sbits = sfull - scut;
-    uint32_t code[E];
-    uint64_t sub[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-        const uint32_t fine = (kmx - cand_key(x[e])) >> kz;
-        code[e] = fine >> kdrop;
+    // a word's code and sub-coordinate, recomputed where needed (fewer
+    // registers held across the phases)
+    auto code_of = [&](uint64_t w) { return ((kmx - cand_key(w)) >> kz) >> kdrop; };
+    auto sub_of = [&](uint64_t w) {
+        const uint32_t fine = (kmx - cand_key(w)) >> kz;
         const uint64_t dropped = kdrop ? (uint64_t)(fine & ((1u << kdrop) - 1u)) : 0ull;
-        sub[e] = ((dropped << lbits) | (uint64_t)(lmx - cand_low(x[e]))) >> scut;
-    }
+        return ((dropped << lbits) | (uint64_t)(lmx - cand_low(w))) >> scut;
+    };
     // every code the same run of bins: code bits, then the top sub bits
     const uint32_t lkeep = nbits - (cbits - kdrop);
+    const uint32_t sshift = sbits > lkeep ? sbits - lkeep : 0u;
     uint32_t bin[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-        const uint32_t sc = lkeep ? (uint32_t)(sub[e] >> (sbits > lkeep ? sbits - lkeep : 0u)) : 0u;
-        bin[e] = (uint32_t)e * NT + t < cnt ? ((code[e] << lkeep) | sc) : 0u;
+        const uint32_t sc = lkeep ? (uint32_t)(sub_of(x[e]) >> sshift) : 0u;
+        bin[e] = (uint32_t)e * NT + t < cnt ? ((code_of(x[e]) << lkeep) | sc) : 0u;
     }
     for (uint32_t i = t; i <= nb; i += NT) bins[i] = 0u;
     lds_sync();
@@ -1003,7 +1003,7 @@ QRITA_DEV bool bucket_sort(uint64_t* a, uint32_t cnt, const RankOut& ro, uint64_
         lds_sync();
 #pragma unroll
         for (int e = 0; e < E; ++e)
-            if ((uint32_t)e * NT + t < cnt) atomicAdd(&hc[code[e]], 1u);
+            if ((uint32_t)e * NT + t < cnt) atomicAdd(&hc[code_of(x[e])], 1u);
         lds_sync();
         scan_counts<NT>(hc, ncodes, sh, rb);
         const float ratio = (float)nb / (float)cnt;
@@ -1014,8 +1014,9 @@ QRITA_DEV bool bucket_sort(uint64_t* a, uint32_t cnt, const RankOut& ro, uint64_
         };
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-            const uint32_t f0 = first(code[e]), nsub = first(code[e] + 1u) - f0;
-            const uint32_t off = sbits ? (uint32_t)((sub[e] * nsub) >> sbits) : 0u;
+            const uint32_t c = code_of(x[e]);
+            const uint32_t f0 = first(c), nsub = first(c + 1u) - f0;
+            const uint32_t off = sbits ? (uint32_t)((sub_of(x[e]) * nsub) >> sbits) : 0u;
             bin[e] = (uint32_t)e * NT + t < cnt ? f0 + off : 0u;
         }
         for (uint32_t i = t; i <= nb; i += NT) bins[i] = 0u;
@@ -1097,6 +1098,8 @@ __device__ __attribute__((always_inline)) void sort_emit(uint32_t cnt, RankOut r
         done = bucket_sort<NT, 2>(a, cnt, ro, b, bins, sh, rb);
     else if (cnt <= 8u * NT)
         done = bucket_sort<NT, 8>(a, cnt, ro, b, bins, sh, rb);
+    else if (cnt <= 16u * NT)
+        done = bucket_sort<NT, 16>(a, cnt, ro, b, bins, sh, rb);
     else
         done = bucket_sort<NT, 32>(a, cnt, ro, b, bins, sh, rb);
     if (done) return;
