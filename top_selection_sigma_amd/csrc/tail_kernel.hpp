@@ -1096,6 +1096,8 @@ __device__ __attribute__((always_inline)) void sort_emit(uint32_t cnt, RankOut r
     bool done;
     if (cnt <= 2u * NT)
         done = bucket_sort<NT, 2>(a, cnt, ro, b, bins, sh, rb);
+    else if (cnt <= 4u * NT)
+        done = bucket_sort<NT, 4>(a, cnt, ro, b, bins, sh, rb);
     else if (cnt <= 8u * NT)
         done = bucket_sort<NT, 8>(a, cnt, ro, b, bins, sh, rb);
     else if (cnt <= 16u * NT)
