@@ -954,13 +954,16 @@ QRITA_DEV bool bucket_sort(uint64_t* a, uint32_t cnt, const RankOut& ro, uint64_
     }
     uint32_t ext[5] = {wave_min_u32(kmn), ~wave_max_u32(kmx), wave_min_u32(lmn), ~wave_max_u32(lmx),
                        wave_min_u32(tz)};
+    // the bin counts are cleared before the combination's barrier, which
+    // orders them before the first count
+    const uint32_t nb = min(kSortBins, 2u * next_pow2(cnt));
+    for (uint32_t i = t; i <= nb; i += NT) bins[i] = 0u;
     comb_record<NT, 0, 0, 5>(nullptr, nullptr, ext, sh, rb);
     kmn = uni(ext[0]);
     kmx = ~uni(ext[1]);
     lmn = uni(ext[2]);
     lmx = ~uni(ext[3]);
     const uint32_t kz = min(uni(ext[4]), 31u);
-    const uint32_t nb = min(kSortBins, 2u * next_pow2(cnt));
     const uint32_t nbits = 31u - (uint32_t)__builtin_clz(nb);
     const uint32_t fine_max = (kmx - kmn) >> kz;
     const uint32_t cbits = bits_for((uint64_t)fine_max);
@@ -988,8 +991,6 @@ QRITA_DEV bool bucket_sort(uint64_t* a, uint32_t cnt, const RankOut& ro, uint64_
         const uint32_t sc = lkeep ? (uint32_t)(sub_of(x[e]) >> sshift) : 0u;
         bin[e] = (uint32_t)e * NT + t < cnt ? ((code_of(x[e]) << lkeep) | sc) : 0u;
     }
-    for (uint32_t i = t; i <= nb; i += NT) bins[i] = 0u;
-    lds_sync();
 #pragma unroll
     for (int e = 0; e < E; ++e)
         if ((uint32_t)e * NT + t < cnt) atomicAdd(&bins[bin[e]], 1u);
