@@ -27,9 +27,14 @@ _lock = threading.Lock()
 _lib = None
 
 
+def _stale() -> bool:
+    """True when liboracle.so is missing or older than oracle.c."""
+    return not os.path.exists(_LIB) or os.path.getmtime(_SRC) > os.path.getmtime(_LIB)
+
+
 def build(force: bool = True) -> str:
     """Compile ``oracle.c`` into ``liboracle.so`` with gcc; returns the path."""
-    if force or not os.path.exists(_LIB):
+    if force or _stale():
         tmp = _LIB + ".tmp"
         subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread",
                                "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"])
@@ -41,7 +46,7 @@ def _load():
     global _lib
     with _lock:
         if _lib is None:
-            if not os.path.exists(_LIB):
+            if _stale():
                 build(force=True)
             lib = ctypes.CDLL(_LIB)
             vp, i64, i32p = ctypes.c_void_p, ctypes.c_int64, ctypes.POINTER(ctypes.c_int32)
