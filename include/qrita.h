@@ -34,6 +34,8 @@
  * allocate nothing, do not synchronise, and launch two kernels in stream
  * order: the single streaming pass over the logits and a per-row tail.
  * Argument errors are reported before anything is launched or written.
+ * The library keeps no state between calls: calls on different streams are
+ * safe as long as each in-flight call has a workspace of its own.
  */
 #ifndef QRITA_H
 #define QRITA_H
@@ -62,22 +64,17 @@ typedef enum {
 
 /*
  * Bytes of device workspace qrita_select needs for this shape. The workspace
- * holds a 64-byte header per row and a per-row overflow list of candidates
- * (at most min(vocab, 32768) entries of 8 bytes): O(batch) memory, against the
- * O(batch * vocab) value+index buffers a full sort needs (the summary reports
- * about 50 % lower memory than sort-based selection, "Resultados").
+ * holds a 32-byte record per row, a 16-byte record per (row, slice of the
+ * streaming pass) and a per-row candidate list (at most min(vocab, 32768)
+ * entries of 8 bytes): O(batch) memory, against the O(batch * vocab)
+ * value+index buffers a full sort needs (the summary reports about 50 % lower
+ * memory than sort-based selection, "Resultados").
+ * Every word a call reads from the workspace is written earlier in the same
+ * call: the workspace needs no initialisation and may hold anything when a
+ * call starts. Two calls sharing one workspace must not overlap in time.
  * Returns 0 for an invalid shape.
  */
 size_t qrita_workspace_bytes(int64_t batch, int64_t vocab, int dtype, int64_t idx_cap);
-
-/*
- * Zero-fill `bytes` of workspace on `stream`. A workspace must be zero-filled
- * once before its first use; every completed qrita_select call leaves it
- * zero-filled again, so it can be reused by later calls of any shape that
- * fits. Two calls sharing one workspace must not overlap in time.
- * Returns QRITA_EINVAL for a NULL pointer, QRITA_ELAUNCH on launch failure.
- */
-int qrita_workspace_init(void* workspace, size_t bytes, void* stream);
 
 /*
  * Select the top-k / top-p candidate set of every row.
@@ -96,12 +93,16 @@ int qrita_workspace_init(void* workspace, size_t bytes, void* stream);
  * out_count  device int32 [batch]: number of kept tokens. Required when
  *            out_idx is given; may be NULL otherwise.
  * idx_cap    row stride of out_idx (>= 0).
+ * idx_cap    also the expected range of k: above 4096 the per-row tail takes
+ *            the tier that sorts up to 8192 kept tokens at once.
  * workspace  device scratch of at least qrita_workspace_bytes(...) bytes,
- *            zero-filled before first use (see qrita_workspace_init).
+ *            256-byte aligned; its contents on entry do not matter.
  * stream     hipStream_t to launch on (NULL = default stream).
  *
  * At least one of out_mask, out_idx, out_count must be non-NULL.
- * Returns QRITA_OK, QRITA_EINVAL, QRITA_EWORKSPACE or QRITA_ELAUNCH.
+ * Returns QRITA_OK, QRITA_EINVAL, QRITA_EWORKSPACE, QRITA_EUNSUPPORTED (the
+ * current device is not gfx950; checked after the arguments) or
+ * QRITA_ELAUNCH.
  */
 int qrita_select(const void* logits, int64_t batch, int64_t vocab, int dtype,
                  const int32_t* k, const float* p,
@@ -115,7 +116,10 @@ int qrita_select(const void* logits, int64_t batch, int64_t vocab, int dtype,
  *                full-row fallback (the summary's truncation miss, §1).
  *   delta_scale  multiplies the table delta (0 means 1).
  *   pivot_mode   0: pivots at 25/50/75 % of the key range (§2);
- *                1: the same fractions of the value range.
+ *                1: the same fractions of the value range;
+ *                2: one pivot at 50 % of the key range (a binary search with
+ *                   the same duplicate tracking, for the quaternary-vs-binary
+ *                   ablation of "Resultados").
  *   slices       workgroups per row (0 = automatic tier).
  *   lds_cap      candidate capacity in LDS per workgroup (0 = automatic;
  *                otherwise clamped to [64, automatic]).
@@ -125,6 +129,11 @@ int qrita_select(const void* logits, int64_t batch, int64_t vocab, int dtype,
  *                diagnostics, see QRITA_DIAG_* below.
  *   mid_event    a hipEvent_t or NULL: recorded on the stream between the
  *                streaming pass and the per-row tail, for per-stage timing.
+ *   tier         tail tier: 0 automatic, 1 light (two rows per CU),
+ *                2 heavy (one row per CU, larger capacities).
+ *   mask_mode    0 automatic; 1: pass 1 zero-fills the mask and the tail
+ *                stores the kept bytes one by one (instead of the tail
+ *                writing whole rows from an LDS bitmap).
  */
 typedef struct {
     int32_t force_miss;
@@ -135,6 +144,8 @@ typedef struct {
     int32_t list_cap;
     int32_t* diag;
     void* mid_event;
+    int32_t tier;
+    int32_t mask_mode;
 } qrita_options;
 
 #define QRITA_DIAG_FIELDS 8

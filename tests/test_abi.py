@@ -23,7 +23,7 @@ def _declared_functions():
 def test_header_declares_the_api():
     names = _declared_functions()
     assert names == ["qrita_select", "qrita_select_ex", "qrita_strerror",
-                     "qrita_workspace_bytes", "qrita_workspace_init"]
+                     "qrita_workspace_bytes"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -91,16 +91,13 @@ def test_argument_errors_return_before_launch(kw, code):
 
 
 def test_options_are_validated():
-    bad = [q._Options(0, 0.0, 2, 0, 0, 0, None, None), q._Options(0, 0.0, 0, -1, 0, 0, None, None),
-           q._Options(0, float("nan"), 0, 0, 0, 0, None, None),
-           q._Options(0, 0.0, 0, 0, -3, 0, None, None)]
+    bad = [q._Options(0, 0.0, 3, 0, 0, 0, None, None, 0, 0), q._Options(0, 0.0, 0, -1, 0, 0, None, None, 0, 0),
+           q._Options(0, float("nan"), 0, 0, 0, 0, None, None, 0, 0),
+           q._Options(0, 0.0, 0, 0, -3, 0, None, None, 0, 0),
+           q._Options(0, 0.0, 0, 0, 0, 0, None, None, 3, 0),
+           q._Options(0, 0.0, 0, 0, 0, 0, None, None, 0, 2)]
     for o in bad:
         assert _call(opt=o) == q.QRITA_EINVAL
-
-
-def test_workspace_init_rejects_null():
-    assert q.lib().qrita_workspace_init(None, 1024, None) == q.QRITA_EINVAL
-    assert q.lib().qrita_workspace_init(FAKE, 0, None) == q.QRITA_OK
 
 
 def test_product_path_has_no_cpu_fallback():

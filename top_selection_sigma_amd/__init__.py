@@ -48,6 +48,8 @@ class _Options(ctypes.Structure):
         ("list_cap", ctypes.c_int32),
         ("diag", ctypes.c_void_p),
         ("mid_event", ctypes.c_void_p),
+        ("tier", ctypes.c_int32),
+        ("mask_mode", ctypes.c_int32),
     ]
 
 
@@ -63,12 +65,15 @@ class Options:
     list_cap: int = 0
     diag: object = None       # device int32 tensor [batch, 8] or None
     mid_event: object = None  # torch.cuda.Event (already recorded once) or None
+    tier: int = 0             # 0 automatic, 1 light, 2 heavy
+    mask_mode: int = 0        # 0 automatic, 1 mask bytes stored one by one
 
     def to_c(self) -> _Options:
         return _Options(int(self.force_miss), float(self.delta_scale), int(self.pivot_mode),
                         int(self.slices), int(self.lds_cap), int(self.list_cap),
                         None if self.diag is None else self.diag.data_ptr(),
-                        None if self.mid_event is None else self.mid_event.cuda_event)
+                        None if self.mid_event is None else self.mid_event.cuda_event,
+                        int(self.tier), int(self.mask_mode))
 
 
 def lib() -> ctypes.CDLL:
@@ -83,8 +88,6 @@ def lib() -> ctypes.CDLL:
             i64, vp, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
             L.qrita_workspace_bytes.restype = sz
             L.qrita_workspace_bytes.argtypes = [i64, i64, ctypes.c_int, i64]
-            L.qrita_workspace_init.restype = ctypes.c_int
-            L.qrita_workspace_init.argtypes = [vp, sz, vp]
             sel = [vp, i64, i64, ctypes.c_int, vp, vp, vp, vp, vp, i64, vp, sz, vp]
             L.qrita_select.restype = ctypes.c_int
             L.qrita_select.argtypes = sel
@@ -114,13 +117,6 @@ def _stream_ptr(stream) -> Optional[int]:
 
 def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
-
-
-def qrita_workspace_init(workspace, stream=None) -> None:
-    nbytes = workspace.numel() * workspace.element_size()
-    st = lib().qrita_workspace_init(workspace.data_ptr(), nbytes, _stream_ptr(stream))
-    if st != QRITA_OK:
-        raise QritaError(st, "qrita_workspace_init")
 
 
 def dtype_code(t) -> int:
@@ -160,17 +156,26 @@ def qrita_select_ex(logits, k, p, out_mask, out_idx, out_count, idx_cap: int, wo
 _ws_cache = {}
 
 
-def workspace_for(batch: int, vocab: int, dtype: int, idx_cap: int, device=None):
-    """A zero-initialised workspace large enough for this shape (cached per device)."""
+def workspace_for(batch: int, vocab: int, dtype: int, idx_cap: int, device=None, stream=None):
+    """A workspace large enough for this shape, cached per (device, stream).
+
+    Calls on one stream run in order, so they can share a workspace; calls on
+    different streams get different ones. The workspace is allocated on that
+    stream, so torch reuses its memory only in that stream's order. Its
+    contents never matter to the library.
+    """
     import torch
 
     device = torch.device("cuda", torch.cuda.current_device()) if device is None else device
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
     need = max(qrita_workspace_bytes(batch, vocab, dtype, idx_cap), 256)
-    ws = _ws_cache.get(device)
+    key = (device, stream.cuda_stream)
+    ws = _ws_cache.get(key)
     if ws is None or ws.numel() < need:
-        ws = torch.empty(need, dtype=torch.uint8, device=device)
-        qrita_workspace_init(ws)
-        _ws_cache[device] = ws
+        with torch.cuda.stream(stream):
+            ws = torch.empty(need, dtype=torch.uint8, device=device)
+        _ws_cache[key] = ws
     return ws
 
 
@@ -186,13 +191,17 @@ def select(logits, k=None, p=None, want_mask: bool = True, idx_cap: Optional[int
 
     B, V = logits.shape
     dev = logits.device
-    mask = torch.empty((B, V), dtype=torch.uint8, device=dev) if want_mask else None
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
     idx = None
     cap = 0
-    if idx_cap is not None and idx_cap > 0:
-        cap = int(idx_cap)
-        idx = torch.empty((B, cap), dtype=torch.int32, device=dev)
-    count = torch.empty(B, dtype=torch.int32, device=dev)
-    ws = workspace_for(B, V, dtype_code(logits), cap, dev)
+    # outputs are allocated on the stream the kernels run on
+    with torch.cuda.stream(stream):
+        mask = torch.empty((B, V), dtype=torch.uint8, device=dev) if want_mask else None
+        if idx_cap is not None and idx_cap > 0:
+            cap = int(idx_cap)
+            idx = torch.empty((B, cap), dtype=torch.int32, device=dev)
+        count = torch.empty(B, dtype=torch.int32, device=dev)
+    ws = workspace_for(B, V, dtype_code(logits), cap, dev, stream)
     qrita_select_ex(logits, k, p, mask, idx, count, cap, ws, stream, options)
     return mask, idx, count

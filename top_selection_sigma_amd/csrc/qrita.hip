@@ -1,126 +1,116 @@
-// Host side of libqrita: argument checks, launch-tier choice and the C ABI
-// declared in include/qrita.h.
+// Host side of libqrita: argument checks, the tier table and the C ABI
+// declared in include/qrita.h. The kernels are compiled in their own
+// translation units (pass1.hip, tail_light.hip, tail_heavy.hip).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
-#include <mutex>
+#include <atomic>
+#include <cstring>
 
+#include "launch.hpp"
 #include "qrita.h"
-#include "select_kernel.hpp"
 
 namespace {
 
 using qrita::Params;
 
-constexpr int64_t kHeaderBytes = qrita::H_WORDS * 4;
-constexpr int64_t kListMax = 32768;
-// tail workgroup: one wave per SIMD; up to 64 candidate keys per thread in
-// registers (16384 per row) with their indices in LDS, and an LDS buffer of
-// 8192 candidates for gathering the kept set (sets above 4096 are sorted in
-// windows) that holds the candidates' softmax masses before that
-constexpr int kTailThreads = 256;
-constexpr int kTailRegCap = kTailThreads * qrita::kTailR;
-constexpr int kTailLdsEntries = 8192;
-// tail LDS: gather/sort buffer and masses, the candidates' indices (then the
-// sort's second buffer), and the sort's bin counts
-constexpr size_t kTailLds = (size_t)kTailLdsEntries * 8 + (size_t)kTailRegCap * 4 + (qrita::kSortBins + 4) * 4;
+constexpr int64_t kListMax = 32768;   // per-row candidate list (entries of 8 bytes)
+constexpr int kPass1Threads = 256;
+constexpr int kSampleN = 2048;        // pass 1 sample (its LDS stage holds at least this many entries)
+constexpr int kStageCap = 2048;       // pass 1 LDS candidate stage
+constexpr int kWaveSpill = 512;       // pass 1 per-wave spill buffer entries
 
 int64_t list_stride_for(int64_t vocab) { return std::min<int64_t>(vocab, kListMax); }
+int64_t round256(int64_t x) { return (x + 255) / 256 * 256; }
 
-struct Tier {
-    int threads;      // pass 1 workgroup size
-    int slices;       // pass 1 workgroups per row
-    int slice_len;    // logits per slice
-    int stage_cap;    // pass 1 LDS candidate stage
-    int stage_alloc;  // pass 1 LDS entries (>= the 2048-entry sample)
-    int tail_threads;
-    int tail_cap;     // tail: largest list searched in registers
-    int tail_alloc;   // tail LDS entries for sorting (power of two)
-    int list_cap;
+// Workspace layout: row records, slice records, row lists. Nothing in it is
+// expected to hold any value when a call starts.
+struct WsLayout {
+    int64_t rowrec, slrec, lists, total;
 };
-
-int64_t next_pow2(int64_t x) {
-    int64_t p = 1;
-    while (p < x) p <<= 1;
-    return p;
+WsLayout ws_layout(int64_t B, int64_t V) {
+    WsLayout w;
+    w.rowrec = 0;
+    w.slrec = round256(B * qrita::R_WORDS * 4);
+    w.lists = w.slrec + round256(B * qrita::kMaxSlices * qrita::S_WORDS * 4);
+    w.total = w.lists + B * list_stride_for(V) * 8;
+    return w;
 }
 
-// Tier table (the summary's tiered block sizes, "Autotuning": large blocks
-// for full rows, small ones for truncated sets). Here it is a static function
-// of the shape: pass 1 gets at least 1024 workgroups (all resident together
-// on 256 CUs); from 512 rows on, long rows get up to eight slices of about
-// 64 KiB, which keeps several rounds of workgroups queued so that the CUs
-// finishing early take more, while the per-workgroup sample stays small next
-// to the streamed bytes (slices of at least 8192 logits); the tail gets one
-// 256-thread workgroup per row over the much smaller candidate set.
-Tier choose_tier(int64_t B, int64_t V, int64_t esize, const qrita_options* o) {
-    Tier t;
+struct Plan {
+    int slices;      // pass 1 workgroups per row
+    int slice_len;   // logits per slice
+    int stage_cap;   // pass 1 LDS candidate stage
+    bool heavy;      // tail tier
+    int tail_cap;    // candidates the tail holds in LDS
+    int list_cap;    // usable entries of a row list
+    int sub_cap;     // list entries per slice
+    bool bitmap;     // the tail writes whole mask rows
+};
+
+// The tier table (the summary's tiered block sizes, "Autotuning": large blocks
+// for full rows, small ones for truncated sets), a static function of the
+// call's shape (B rows, V logits of `esize` bytes, idx_cap for the expected
+// top-k range):
+//  - pass 1: 256-thread workgroups, at least 1024 of them (all resident
+//    together on 256 CUs); from 512 rows on, long rows get up to eight slices
+//    of about 64 KiB so several rounds of workgroups balance the CUs; slices of
+//    at least 8192 logits;
+//  - tail: the light tier (two rows per CU) for batches of 256 rows or more
+//    whose index output is at most 4096 ranks, else the heavy tier (one row
+//    per CU, twice the LDS capacities, kept sets up to 8192 sorted at once);
+//  - the mask is written by the tail from an LDS bitmap whenever the row
+//    fits the tier's bitmap, so pass 1 only reads.
+Plan choose_plan(int64_t B, int64_t V, int64_t esize, int64_t idx_cap, const qrita_options* o) {
+    Plan t;
     int64_t S = std::max<int64_t>(1, (1024 + B - 1) / B);
     if (B >= 512) S = std::max<int64_t>(S, std::min<int64_t>(8, (V * esize + 65535) / 65536));
-    S = std::min<int64_t>(S, 64);
+    S = std::min<int64_t>(S, qrita::kMaxSlices);
     S = std::min<int64_t>(S, std::max<int64_t>(1, (V + 8191) / 8192));
-    if (o && o->slices > 0) S = std::min<int64_t>(o->slices, std::max<int64_t>(1, V));
-    // 256-thread workgroups: 1024 of them stay resident together on 256 CUs;
+    if (o && o->slices > 0) S = std::min<int64_t>(std::min<int64_t>(o->slices, qrita::kMaxSlices), std::max<int64_t>(1, V));
     // slices are whole tiles of 16 logits per thread (only a row's last slice
     // ends in a part tile), and after the first they start 16-aligned
-    t.threads = 256;
-    const int64_t TB = (int64_t)t.threads * 16;
+    const int64_t TB = (int64_t)kPass1Threads * 16;
     int64_t L = (V + S - 1) / S;
     L = ((L + TB - 1) / TB) * TB;
     if (o && o->slices > 0) L = ((((V + S - 1) / S) + 15) / 16) * 16;
     S = (V + L - 1) / L;
     t.slices = (int)S;
     t.slice_len = (int)L;
-    int stage = 2048;
-    int tail = kTailRegCap;
-    if (o && o->lds_cap > 0) {
-        stage = std::max(64, std::min(stage, (int)o->lds_cap));
-        tail = std::max(64, std::min(tail, (int)o->lds_cap));
-    }
+    int stage = kStageCap;
+    if (o && o->lds_cap > 0) stage = std::max(64, std::min(stage, (int)o->lds_cap));
     t.stage_cap = stage;
-    t.stage_alloc = std::max(stage, qrita::kSampleN);
-    t.tail_threads = kTailThreads;
+    t.heavy = B < 256 || idx_cap > 4096;
+    if (o && o->tier == 1) t.heavy = false;
+    if (o && o->tier == 2) t.heavy = true;
+    const qrita::TierInfo ti = t.heavy ? qrita::tier_heavy() : qrita::tier_light();
+    int tail = ti.cfull;
+    if (o && o->lds_cap > 0) tail = std::max(64, std::min(tail, (int)o->lds_cap));
     t.tail_cap = tail;
-    t.tail_alloc = kTailLdsEntries;
     int64_t lc = list_stride_for(V);
     if (o && o->list_cap > 0) lc = std::max<int64_t>(1, std::min<int64_t>(lc, o->list_cap));
     t.list_cap = (int)lc;
+    t.sub_cap = (int)std::max<int64_t>(1, lc / S);
+    t.bitmap = (uint64_t)V <= (uint64_t)ti.bitmap_bits && !(o && o->mask_mode == 1);
     return t;
 }
 
-// Dynamic LDS above 64 KiB must be enabled per kernel; the largest request is
-// the tail's (kTailLds, about 144 KiB) next to its static LDS.
-constexpr int kMaxDynLds = 150 * 1024;
+// gfx950 check, once per device (kernels built for gfx950 cannot run elsewhere).
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
 
-template <class Kern>
-hipError_t allow_lds(Kern kern, std::once_flag& once, hipError_t& err) {
-    std::call_once(once, [&] {
-        err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                  kMaxDynLds);
-    });
-    return err;
-}
-
-template <int THREADS, bool BF16>
-hipError_t launch_pass1(const Params& P, const Tier& t, hipStream_t stream) {
-    auto kern = qrita::pass1_kernel<THREADS, BF16>;
-    static std::once_flag once;
-    static hipError_t attr = hipSuccess;
-    if (allow_lds(kern, once, attr) != hipSuccess) return attr;
-    const int64_t groups = ((P.batch + 7) / 8) * 8 * (int64_t)t.slices;
-    const size_t lds = ((size_t)t.stage_alloc + (size_t)(THREADS / qrita::kWave) * qrita::kWaveSpill) * sizeof(uint64_t);
-    hipLaunchKernelGGL(kern, dim3((unsigned)groups), dim3(THREADS), lds, stream, P);
-    return hipGetLastError();
-}
-
-template <int THREADS, bool BF16>
-hipError_t launch_tail(const Params& P, const Tier& t, hipStream_t stream) {
-    auto kern = qrita::tail_kernel<THREADS, BF16>;
-    static std::once_flag once;
-    static hipError_t attr = hipSuccess;
-    if (allow_lds(kern, once, attr) != hipSuccess) return attr;
-    hipLaunchKernelGGL(kern, dim3((unsigned)P.batch), dim3(THREADS), kTailLds, stream, P);
-    return hipGetLastError();
+bool device_supported() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return false;
+    if (dev >= kMaxDevices) return false;
+    int s = g_arch[dev].load(std::memory_order_relaxed);
+    if (s == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return false;
+        s = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        g_arch[dev].store(s, std::memory_order_relaxed);
+    }
+    return s == 1;
 }
 
 int select_impl(const void* logits, int64_t batch, int64_t vocab, int dtype, const int32_t* k,
@@ -142,17 +132,22 @@ int select_impl(const void* logits, int64_t batch, int64_t vocab, int dtype, con
     const size_t need = qrita_workspace_bytes(batch, vocab, dtype, idx_cap);
     if (!workspace || workspace_bytes < need) return QRITA_EWORKSPACE;
     if ((uintptr_t)workspace & 255u) return QRITA_EWORKSPACE;
+    if (!device_supported()) return QRITA_EUNSUPPORTED;
 
-    const Tier t = choose_tier(batch, vocab, dtype == QRITA_BF16 ? 2 : 4, opt);
+    const bool bf16 = dtype == QRITA_BF16;
+    const Plan t = choose_plan(batch, vocab, bf16 ? 2 : 4, out_idx ? idx_cap : 0, opt);
+    const WsLayout w = ws_layout(batch, vocab);
     Params P;
+    std::memset(&P, 0, sizeof P);
     P.logits = logits;
     P.mask = out_mask;
     P.out_idx = out_idx;
     P.out_count = out_count;
     P.k = k;
     P.p = p;
-    P.hdr = (uint32_t*)workspace;
-    P.glist = (uint64_t*)((char*)workspace + ((batch * kHeaderBytes + 255) / 256) * 256);
+    P.rowrec = (uint32_t*)((char*)workspace + w.rowrec);
+    P.slrec = (uint32_t*)((char*)workspace + w.slrec);
+    P.glist = (uint64_t*)((char*)workspace + w.lists);
     P.diag = opt ? opt->diag : nullptr;
     P.batch = batch;
     P.vocab = (int32_t)vocab;
@@ -160,26 +155,24 @@ int select_impl(const void* logits, int64_t batch, int64_t vocab, int dtype, con
     P.slices = t.slices;
     P.slice_len = t.slice_len;
     P.stage_cap = t.stage_cap;
-    P.tail_cap = t.tail_cap;
-    P.tail_alloc = t.tail_alloc;
+    P.sub_cap = t.sub_cap;
     P.list_cap = t.list_cap;
     P.list_stride = (int32_t)list_stride_for(vocab);
+    P.tail_cap = t.tail_cap;
     P.force_miss = opt ? opt->force_miss : 0;
     P.delta_scale = (opt && opt->delta_scale != 0.0f) ? opt->delta_scale : 1.0f;
     P.pivot_mode = opt ? opt->pivot_mode : 0;
+    P.bitmap = t.bitmap ? 1 : 0;
+    P.bf16 = bf16 ? 1 : 0;
 
     hipStream_t s = (hipStream_t)stream;
-    hipError_t err;
-    const bool bf16 = dtype == QRITA_BF16;
-    if (t.threads == 512)
-        err = bf16 ? launch_pass1<512, true>(P, t, s) : launch_pass1<512, false>(P, t, s);
-    else
-        err = bf16 ? launch_pass1<256, true>(P, t, s) : launch_pass1<256, false>(P, t, s);
-    if (err != hipSuccess) return QRITA_ELAUNCH;
+    const unsigned groups = (unsigned)(((batch + 7) / 8) * 8 * (int64_t)t.slices);
+    const size_t lds = ((size_t)std::max(t.stage_cap, kSampleN) + (size_t)(kPass1Threads / 64) * kWaveSpill) * 8;
+    if (qrita::launch_pass1(P, groups, lds, bf16, s) != hipSuccess) return QRITA_ELAUNCH;
     if (opt && opt->mid_event) {
         if (hipEventRecord((hipEvent_t)opt->mid_event, s) != hipSuccess) return QRITA_ELAUNCH;
     }
-    err = bf16 ? launch_tail<kTailThreads, true>(P, t, s) : launch_tail<kTailThreads, false>(P, t, s);
+    const hipError_t err = t.heavy ? qrita::launch_tail_heavy(P, s) : qrita::launch_tail_light(P, s);
     return err == hipSuccess ? QRITA_OK : QRITA_ELAUNCH;
 }
 
@@ -191,19 +184,7 @@ size_t qrita_workspace_bytes(int64_t batch, int64_t vocab, int dtype, int64_t id
     (void)idx_cap;
     if (batch < 0 || vocab <= 0 || vocab > INT32_MAX) return 0;
     if (dtype != QRITA_F32 && dtype != QRITA_BF16) return 0;
-    const int64_t hdr = ((batch * kHeaderBytes + 255) / 256) * 256;
-    return (size_t)(hdr + batch * list_stride_for(vocab) * (int64_t)sizeof(uint64_t));
-}
-
-int qrita_workspace_init(void* workspace, size_t bytes, void* stream) {
-    if (!workspace) return QRITA_EINVAL;
-    if (bytes == 0) return QRITA_OK;
-    if (((uintptr_t)workspace & 3u) || (bytes & 3u)) return QRITA_EINVAL;
-    const uint64_t words = bytes / 4;
-    const unsigned blocks = (unsigned)std::min<uint64_t>((words + 255) / 256, 4096);
-    hipLaunchKernelGGL(qrita::zero_fill_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream,
-                       (uint32_t*)workspace, words);
-    return hipGetLastError() == hipSuccess ? QRITA_OK : QRITA_ELAUNCH;
+    return (size_t)ws_layout(batch, vocab).total;
 }
 
 int qrita_select(const void* logits, int64_t batch, int64_t vocab, int dtype, const int32_t* k,
@@ -217,8 +198,9 @@ int qrita_select_ex(const void* logits, int64_t batch, int64_t vocab, int dtype,
                     const float* p, uint8_t* out_mask, int32_t* out_idx, int32_t* out_count,
                     int64_t idx_cap, void* workspace, size_t workspace_bytes, void* stream,
                     const qrita_options* opt) {
-    if (opt && (((uintptr_t)opt->diag & 3u) || opt->pivot_mode < 0 || opt->pivot_mode > 1 ||
-                opt->slices < 0 || opt->lds_cap < 0 || opt->list_cap < 0 ||
+    if (opt && (((uintptr_t)opt->diag & 3u) || opt->pivot_mode < 0 || opt->pivot_mode > 2 ||
+                opt->slices < 0 || opt->lds_cap < 0 || opt->list_cap < 0 || opt->tier < 0 ||
+                opt->tier > 2 || opt->mask_mode < 0 || opt->mask_mode > 1 ||
                 !(opt->delta_scale == opt->delta_scale)))
         return QRITA_EINVAL;
     return select_impl(logits, batch, vocab, dtype, k, p, out_mask, out_idx, out_count, idx_cap,
@@ -231,7 +213,7 @@ const char* qrita_strerror(int status) {
         case QRITA_EINVAL: return "invalid argument";
         case QRITA_EWORKSPACE: return "workspace missing, misaligned or too small";
         case QRITA_ELAUNCH: return "kernel launch failed";
-        case QRITA_EUNSUPPORTED: return "unsupported device";
+        case QRITA_EUNSUPPORTED: return "unsupported device (the library is built for gfx950)";
         default: return "unknown status";
     }
 }

@@ -29,49 +29,13 @@
 #include <type_traits>
 
 #include "device_common.hpp"
+#include "params.hpp"
 
 namespace qrita {
 
 #include "delta_lut.inc"
 
-struct Params {
-    const void* logits;
-    uint8_t* mask;
-    int32_t* out_idx;
-    int32_t* out_count;
-    const int32_t* k;
-    const float* p;
-    uint32_t* hdr;      // [batch][16] per-row header
-    uint64_t* glist;    // [batch][list_stride] per-row candidate list
-    int32_t* diag;      // [batch][8] or null
-    int64_t batch;
-    int32_t vocab;
-    int32_t idx_cap;
-    int32_t slices;
-    int32_t slice_len;   // logits per slice (multiple of 16)
-    int32_t stage_cap;   // pass 1: candidate capacity of the LDS stage (entries)
-    int32_t tail_cap;    // tail: largest list searched in registers
-    int32_t tail_alloc;  // tail: LDS entries for sorting kept sets (indices follow)
-    int32_t list_cap;    // usable entries of the per-row list
-    int32_t list_stride;
-    int32_t force_miss;
-    float delta_scale;
-    int32_t pivot_mode;
-};
 
-// Per-row header words (all zero between calls).
-enum : int {
-    H_LIST = 1,     // candidates in the row list (pass-1 atomics)
-    H_FLAGS = 2,    // bit 0: list overflow
-    H_KMAX = 3,     // largest candidate key (pass-1 atomics)
-    H_REST = 4,     // two words: fixed-point mass of dropped logits (top-p rows)
-    H_T = 8,        // Gaussian threshold (float bits), written by slice 0
-    H_TC = 9,       // collection threshold (float bits)
-    H_PRED = 10,    // 1 if a miss was predicted
-    H_LAMBDA = 11,  // expected sample count above the K-th value (float bits)
-    H_NS = 12,      // sample size
-    H_WORDS = 16
-};
 
 constexpr int kSampleChunks = 8;
 constexpr int kSampleChunk = 256;
@@ -96,6 +60,9 @@ struct Shared {
     uint32_t gather_n;
     uint32_t u32[8];
     uint32_t wspill[kMaxWaves];  // pass 1: entries left in each wave's spill buffer
+    uint32_t nsub;               // pass 1: entries reserved in the slice's sub-list
+    uint32_t cnt[kMaxSlices];    // tail: candidates per slice
+    uint32_t pre[kMaxSlices + 1];  // tail: prefix of cnt
 };
 
 extern __shared__ uint64_t qrita_dyn_lds[];
@@ -409,21 +376,22 @@ QRITA_DEV uint64_t* wave_spill_buf(const Params& P) {
     return lds_cands() + stage + (threadIdx.x / kWave) * kWaveSpill;
 }
 
-// Move this wave's n buffered entries to the row list.
-QRITA_DEV void wave_spill_flush(const Params& P, int64_t row, const uint64_t* wb, uint32_t n, Shared& sh) {
+// The sub-list a slice owns in its row's list.
+QRITA_DEV uint64_t* sub_list(const Params& P, int64_t row, uint32_t slice) {
+    return P.glist + row * (int64_t)P.list_stride + (int64_t)slice * P.sub_cap;
+}
+
+// Move this wave's n buffered entries to the slice's sub-list (space is
+// reserved with an LDS counter: the sub-list belongs to this workgroup).
+QRITA_DEV void wave_spill_flush(const Params& P, uint64_t* sub, const uint64_t* wb, uint32_t n, Shared& sh) {
     const uint32_t lane = threadIdx.x & (kWave - 1);
     uint32_t g = 0;
-    if (lane == 0) g = atomicAdd(&P.hdr[row * H_WORDS + H_LIST], n);
+    if (lane == 0) g = atomicAdd(&sh.nsub, n);
     g = readlane(g, 0);
-    bool over = false;
     for (uint32_t j = lane; j < n; j += kWave) {
         const uint32_t gp = g + j;
-        if (gp < (uint32_t)P.list_cap)
-            P.glist[row * (int64_t)P.list_stride + gp] = wb[j];
-        else
-            over = true;
+        if (gp < (uint32_t)P.sub_cap) sub[gp] = wb[j];
     }
-    if (over) atomicOr(&sh.flags, 1u);
 }
 
 // Compact the survivors (f >= tc) of 16 logits per lane into the candidate
@@ -435,7 +403,7 @@ QRITA_DEV void wave_spill_flush(const Params& P, int64_t row, const uint64_t* wb
 // masses exp(f - tc) are summed per lane in float over the 16 and added to
 // the fixed-point `rest` once, so the total does not depend on lane order.
 template <int THREADS, bool BF16, bool REST, int VE>
-QRITA_DEV void consume16(const Params& P, int64_t row, const float f[16], uint32_t valid, uint32_t idx0,
+QRITA_DEV void consume16(const Params& P, uint64_t* sub, const float f[16], uint32_t valid, uint32_t idx0,
                          uint32_t vstride, float tc, Shared& sh, uint64_t& rest, Spill& sp) {
     const uint32_t lane = threadIdx.x & (kWave - 1);
     uint32_t tot = 0;
@@ -474,13 +442,13 @@ QRITA_DEV void consume16(const Params& P, int64_t row, const float f[16], uint32
     const uint32_t nover = base + tot - spill_from;
     uint64_t* wb = wave_spill_buf(P);
     if (sp.n + nover > kWaveSpill) {
-        wave_spill_flush(P, row, wb, sp.n, sh);
+        wave_spill_flush(P, sub, wb, sp.n, sh);
         sp.n = 0;
     }
     const bool direct = nover > kWaveSpill;
     uint32_t gbase = 0;
     if (direct) {
-        if (lane == 0) gbase = atomicAdd(&P.hdr[row * H_WORDS + H_LIST], nover);
+        if (lane == 0) gbase = atomicAdd(&sh.nsub, nover);
         gbase = readlane(gbase, 0);
     }
 #pragma unroll
@@ -501,10 +469,8 @@ QRITA_DEV void consume16(const Params& P, int64_t row, const float f[16], uint32
                     const uint64_t c = make_cand(key, idx);
                     if (!direct) {
                         wb[sp.n + off] = c;
-                    } else if (gbase + off < (uint32_t)P.list_cap) {
-                        P.glist[row * (int64_t)P.list_stride + gbase + off] = c;
-                    } else {
-                        atomicOr(&sh.flags, 1u);
+                    } else if (gbase + off < (uint32_t)P.sub_cap) {
+                        sub[gbase + off] = c;
                     }
                 }
             }
@@ -587,11 +553,13 @@ QRITA_DEV int64_t aligned_start(int64_t roff, int64_t e0, int64_t e1) {
 // The streaming pass over [e0, e1); ring[j] holds the slice's full tile j
 // for j < kTileDepth (loaded before the threshold was known).
 template <int THREADS, bool BF16, bool REST>
-QRITA_DEV void stream_slice(const Params& P, int64_t row, int64_t e0, int64_t e1, float tc, uint8_t fill,
-                            RawTile<BF16> (&ring)[kTileDepth<BF16>], Shared& sh, uint64_t& rest, Spill& sp) {
+QRITA_DEV void stream_slice(const Params& P, int64_t row, uint64_t* sub, int64_t e0, int64_t e1, float tc,
+                            uint8_t fill, RawTile<BF16> (&ring)[kTileDepth<BF16>], Shared& sh, uint64_t& rest,
+                            Spill& sp) {
     const int64_t roff = row * (int64_t)P.vocab;
     const void* rowp = row_ptr<BF16>(P, row);
-    uint8_t* mrow = P.mask ? P.mask + roff : nullptr;
+    // the mask slice is filled here only when the tail does not write whole rows
+    uint8_t* mrow = (P.mask && !P.bitmap) ? P.mask + roff : nullptr;
     const int tid = threadIdx.x;
     // head: up to 15 logits before the first 16-element-aligned position
     const int64_t a = aligned_start(roff, e0, e1);
@@ -607,7 +575,7 @@ QRITA_DEV void stream_slice(const Params& P, int64_t row, int64_t e0, int64_t e1
             if (mrow) mrow[e] = fill;
         }
         if (tid < kWave)
-            consume16<THREADS, BF16, REST, 16>(P, row, f, valid, (uint32_t)e, 0u, tc, sh, rest, sp);
+            consume16<THREADS, BF16, REST, 16>(P, sub, f, valid, (uint32_t)e, 0u, tc, sh, rest, sp);
     }
     constexpr int VE = BF16 ? 8 : 4;  // logits per 16-byte vector
     constexpr int NV = 16 / VE;       // vectors per thread per tile
@@ -626,7 +594,7 @@ QRITA_DEV void stream_slice(const Params& P, int64_t row, int64_t e0, int64_t e1
                 unpack_tile<BF16>(ring[j], f);
                 if (i + D < nfull) load_raw<THREADS, BF16>(rowp, tile + (int64_t)D * TB, ring[j]);
                 if (mrow) fill_tile<THREADS, BF16>(mrow, tile, fill);
-                consume16<THREADS, BF16, REST, VE>(P, row, f, 0xFFFFu, (uint32_t)(tile + (int64_t)tid * VE),
+                consume16<THREADS, BF16, REST, VE>(P, sub, f, 0xFFFFu, (uint32_t)(tile + (int64_t)tid * VE),
                                                    (uint32_t)(THREADS * VE), tc, sh, rest, sp);
             }
         }
@@ -672,14 +640,16 @@ QRITA_DEV void stream_slice(const Params& P, int64_t row, int64_t e0, int64_t e1
                 }
             }
         }
-        consume16<THREADS, BF16, REST, VE>(P, row, f, valid, (uint32_t)(tile + (int64_t)tid * VE),
+        consume16<THREADS, BF16, REST, VE>(P, sub, f, valid, (uint32_t)(tile + (int64_t)tid * VE),
                                            (uint32_t)(THREADS * VE), tc, sh, rest, sp);
     }
 }
 
 // Pass 1: one workgroup per (row, slice). Workgroup g runs on XCD g mod 8;
 // rows are dealt so that all slices of row r share XCD r mod 8 and therefore
-// one L2, which also holds the row list when the row's tail reads it.
+// one L2, which also holds the row list when the row's tail (workgroup r of
+// the next launch, on the same XCD) reads it. A slice writes only its own
+// sub-list and record: no global atomics, no state carried between calls.
 template <int THREADS, bool BF16>
 __global__ __launch_bounds__(THREADS, 4) void pass1_kernel(Params P) {
     __shared__ Shared sh;
@@ -692,11 +662,11 @@ __global__ __launch_bounds__(THREADS, 4) void pass1_kernel(Params P) {
     const int32_t V = P.vocab;
     const int64_t roff = row * (int64_t)V;
     const void* rowp = row_ptr<BF16>(P, row);
-    uint32_t* hdr = P.hdr + row * H_WORDS;
+    uint64_t* sub = sub_list(P, row, slice);
     const RowMode md = row_mode(P, row);
     if (threadIdx.x == 0) {
         sh.ncand = 0;
-        sh.flags = 0;
+        sh.nsub = 0;
     }
     // this workgroup's slice; slices after the first start 16-aligned
     const int64_t A = (16 - (roff & 15)) & 15;
@@ -724,11 +694,10 @@ __global__ __launch_bounds__(THREADS, 4) void pass1_kernel(Params P) {
     }
     const Thresh th = compute_threshold<THREADS, BF16>(P, md, rowp, xs, ins, c0, sh, rb);
     if (slice == 0 && threadIdx.x == 0) {
-        hdr[H_T] = __float_as_uint(th.t);
-        hdr[H_TC] = __float_as_uint(th.tc);
-        hdr[H_PRED] = th.predicted ? 1u : 0u;
-        hdr[H_LAMBDA] = __float_as_uint(th.lambda);
-        hdr[H_NS] = th.n_s;
+        uint32_t* rr = P.rowrec + row * R_WORDS;
+        *(uint4*)rr = make_uint4(__float_as_uint(th.t), __float_as_uint(th.tc), th.predicted ? 1u : 0u,
+                                 __float_as_uint(th.lambda));
+        rr[R_NS] = th.n_s;
     }
     __syncthreads();
     // a3: the single streaming pass over the slice
@@ -737,15 +706,14 @@ __global__ __launch_bounds__(THREADS, 4) void pass1_kernel(Params P) {
     uint64_t rest = 0;
     Spill sp{0u, 0u};
     if (rest_on)
-        stream_slice<THREADS, BF16, true>(P, row, e0, e1, th.tc, fill, ring, sh, rest, sp);
+        stream_slice<THREADS, BF16, true>(P, row, sub, e0, e1, th.tc, fill, ring, sh, rest, sp);
     else
-        stream_slice<THREADS, BF16, false>(P, row, e0, e1, th.tc, fill, ring, sh, rest, sp);
+        stream_slice<THREADS, BF16, false>(P, row, sub, e0, e1, th.tc, fill, ring, sh, rest, sp);
     const uint32_t lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     if (lane == 0) sh.wspill[wave] = sp.n;
     __syncthreads();
     // publish: the staged candidates and what the spill buffers still hold go
-    // to the row list in one reservation, whose round trip overlaps the
-    // maximum over the stage
+    // to the sub-list in one reservation
     const uint32_t nst = min(sh.ncand, (uint32_t)P.stage_cap);
     uint32_t wpre = 0, wtot = 0;
 #pragma unroll
@@ -756,7 +724,7 @@ __global__ __launch_bounds__(THREADS, 4) void pass1_kernel(Params P) {
     }
     uint32_t kmax = sp.kmax;
     uint32_t gb = 0;
-    if (threadIdx.x == 0 && nst + wtot) gb = atomicAdd(&hdr[H_LIST], nst + wtot);
+    if (threadIdx.x == 0) gb = atomicAdd(&sh.nsub, nst + wtot);
     constexpr int PER = kSampleN / THREADS;  // stage entries per thread (stage_cap <= 2048)
     const uint64_t* a = lds_cands();
     uint32_t keys[PER], lows[PER];
@@ -772,34 +740,23 @@ __global__ __launch_bounds__(THREADS, 4) void pass1_kernel(Params P) {
     uint32_t d0 = 0, d1 = 0;
     block_sum_min_max<THREADS>(d0, d1, kmax, rest, sh, rb);
     gb = sh.u32[0];
-    uint64_t* lst = P.glist + row * (int64_t)P.list_stride;
-    bool over = false;
+    const uint32_t cap = (uint32_t)P.sub_cap;
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
         const uint32_t i = (uint32_t)u * THREADS + threadIdx.x;
-        if (i < nst) {
-            if (gb + i < (uint32_t)P.list_cap)
-                lst[gb + i] = ((uint64_t)keys[u] << 32) | lows[u];
-            else
-                over = true;
-        }
+        if (i < nst && gb + i < cap) sub[gb + i] = ((uint64_t)keys[u] << 32) | lows[u];
     }
     {
         const uint64_t* wb = wave_spill_buf(P);
         const uint32_t g = gb + nst + wpre;
-        for (uint32_t j = lane; j < sp.n; j += kWave) {
-            if (g + j < (uint32_t)P.list_cap)
-                lst[g + j] = wb[j];
-            else
-                over = true;
-        }
+        for (uint32_t j = lane; j < sp.n; j += kWave)
+            if (g + j < cap) sub[g + j] = wb[j];
     }
-    if (over) atomicOr(&hdr[H_FLAGS], 1u);
-    if (threadIdx.x == 0) {
-        if (kmax) atomicMax(&hdr[H_KMAX], kmax);
-        if (rest) atomicAdd((unsigned long long*)(hdr + H_REST), (unsigned long long)rest);
-        if (sh.flags) atomicOr(&hdr[H_FLAGS], 1u);
-    }
+    // the slice record: its count (above sub_cap: the sub-list overflowed),
+    // largest key and dropped mass
+    if (threadIdx.x == 0)
+        *(uint4*)(P.slrec + (row * kMaxSlices + slice) * S_WORDS) =
+            make_uint4(gb + nst + wtot, kmax, (uint32_t)rest, (uint32_t)(rest >> 32));
 }
 
 // Re-collect the row's candidates >= tr into the per-row list (full-row
@@ -852,12 +809,6 @@ QRITA_DEV uint32_t collect_row(const Params& P, int64_t row, float tr, bool rest
     overflow = sh.flags != 0 || cnt > (uint32_t)P.list_cap;
     __syncthreads();
     return cnt < (uint32_t)P.list_cap ? cnt : (uint32_t)P.list_cap;
-}
-
-__global__ void zero_fill_kernel(uint32_t* p, uint64_t words) {
-    for (uint64_t i = blockIdx.x * (uint64_t)blockDim.x + threadIdx.x; i < words;
-         i += (uint64_t)gridDim.x * blockDim.x)
-        p[i] = 0u;
 }
 
 }  // namespace qrita

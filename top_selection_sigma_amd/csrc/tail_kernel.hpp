@@ -1,18 +1,59 @@
 // The tail of the path (steps a4-a7): one workgroup of four waves per row,
-// launched after pass 1 has completed for every row.
+// launched after the streaming pass has completed for every row.
 //
-// No thread of a tail workgroup reads global memory that another one wrote
-// (outside the re-collection of the fallback, which synchronises fully), so
-// its barriers order LDS only and never wait for the mask and index stores.
+// The row's candidates (the slices' sub-lists) are loaded once into LDS as
+// keys. Every pivot evaluation of the quaternary search is one loop over the
+// candidates still in play followed by one combination across the four waves.
+// After an evaluation each wave moves its candidates inside the new search
+// range to a segment of LDS of its own (no barrier: a wave only ever reads its
+// own segment), so later evaluations visit a quarter of the keys or fewer.
+// Rows whose candidates do not fit LDS are searched from the lists in global
+// memory the same way; a truncation miss re-collects the row or, last, searches
+// the whole row ("Metodología" §1).
 //
-// The row's candidate list is held in registers (RegSet: up to 64 keys per
-// thread, 16384 per row) and every pivot evaluation of the quaternary search
-// is one pass over those registers followed by one combination across the
-// four waves. Longer lists, overflowed lists and truncation misses take the
-// out-of-line fallback, which streams the candidates from memory (MemSrc).
+// All visits are loops, so the code of one search step stays small enough to
+// remain in the instruction cache while the step repeats.
 #pragma once
 
 namespace qrita {
+
+// ---------------------------------------------------------------------------
+// Tiers of the tail (the summary's tiered block sizes, "Autotuning"): the
+// light tier fits two workgroups per CU (rows of large batches overlap their
+// latencies), the heavy one holds twice the candidates and sorts kept sets of
+// up to 8192 in one piece.
+// ---------------------------------------------------------------------------
+template <int CFULL_, int SEG_, int CSORT_, int NB_>
+struct TailTier {
+    static constexpr int NT = 256;         // threads per row
+    static constexpr int NW = NT / kWave;  // waves
+    static constexpr int CFULL = CFULL_;   // candidate keys held in LDS
+    static constexpr int SEG = SEG_;       // 8-byte entries of one wave's search segment
+    static constexpr int CSORT = CSORT_;   // largest set sorted in one piece
+    static constexpr int NB = NB_;         // bucket-sort bins
+    static constexpr int WAVES_PER_SIMD = CFULL_ <= 12288 ? 2 : 1;  // rows resident per CU
+    // LDS layout (bytes). Search phase: keys, then the wave segments. Emit
+    // phase (after the search): the words to sort, the sort's position array,
+    // its per-position results (ranks' kept indices), bin counts and code
+    // starts; the mask bitmap reuses the words' region.
+    static constexpr size_t A_OFF = 0;
+    static constexpr size_t W_OFF = A_OFF + (size_t)CFULL * 4;
+    static constexpr size_t SEARCH_END = W_OFF + (size_t)NW * SEG * 8;
+    static constexpr size_t SA_OFF = 0;
+    static constexpr size_t SB_OFF = SA_OFF + (size_t)(CSORT + 8) * 8;
+    static constexpr size_t SR_OFF = SB_OFF + (size_t)CSORT * 4;
+    static constexpr size_t BINS_OFF = SR_OFF + (size_t)CSORT * 4;
+    static constexpr size_t HC_OFF = BINS_OFF + (size_t)(NB + 4) * 4;
+    static constexpr size_t EMIT_END = HC_OFF + (size_t)(NB + 4) * 4;
+    static constexpr size_t LDS = SEARCH_END > EMIT_END ? SEARCH_END : EMIT_END;
+    static constexpr uint32_t BITMAP_BITS = (uint32_t)((CSORT + 8) * 64);
+    static_assert(SEARCH_END % 16 == 0 && SB_OFF % 16 == 0 && BINS_OFF % 16 == 0, "alignment");
+};
+using TierLight = TailTier<12288, 768, 4096, 1024>;
+using TierHeavy = TailTier<24576, 1536, 8192, 2048>;
+
+extern __shared__ uint64_t qrita_dyn_lds[];
+QRITA_DEV char* dyn_lds() { return (char*)qrita_dyn_lds; }
 
 // ---------------------------------------------------------------------------
 // Block combination. Every wave reduces its lanes with DPP; lane 0 stores the
@@ -29,47 +70,8 @@ QRITA_DEV uint64_t uni(uint64_t x) {
     return ((uint64_t)uni((uint32_t)(x >> 32)) << 32) | uni((uint32_t)x);
 }
 
-// Exclusive prefix over the waves of per-wave counts c (wave uniform):
-// returns the sum over the lower waves and sets total to the sum over all.
-template <int NT>
-QRITA_DEV uint32_t wave_prefix(uint32_t c, uint32_t& total, Shared& sh, int& rb) {
-    constexpr int NW = NT / kWave;
-    if (NW == 1) {
-        total = c;
-        return 0u;
-    }
-    const uint32_t lane = tid_here() & (kWave - 1), wave = wave_base_here() / kWave;
-    if (lane == 0) sh.slot[rb][wave][0] = c;
-    lds_sync();
-    uint32_t before = 0, all = 0;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-        const uint32_t q = sh.slot[rb][w][0];
-        before += (uint32_t)w < wave ? q : 0u;
-        all += q;
-    }
-    rb ^= 1;
-    total = uni(all);
-    return uni(before);
-}
-
-template <int NT>
-QRITA_DEV uint32_t comb_sum32(uint32_t v, Shared& sh, int& rb) {
-    uint32_t total = 0;
-    wave_prefix<NT>(wave_sum_u32(v), total, sh, rb);
-    return total;
-}
-
-template <int NT>
-QRITA_DEV uint32_t comb_max32(uint32_t v, Shared& sh, int& rb) {
-    uint32_t mn[1] = {~wave_max_u32(v)};
-    comb_record<NT, 0, 0, 1>(nullptr, nullptr, mn, sh, rb);
-    return ~mn[0];
-}
-
 // Records of N32 u32 sums, N64 u64 sums and NMIN u32 minima (wave totals on
-// entry, block totals on return). A record takes at most 32 words and a
-// workgroup at most 8 waves: the records of one buffer fill slot[rb].
+// entry, block totals on return).
 template <int NT, int N32, int N64, int NMIN>
 QRITA_DEV void comb_record(uint32_t* s32, uint64_t* s64, uint32_t* mn, Shared& sh, int& rb) {
     constexpr int NW = NT / kWave;
@@ -131,216 +133,356 @@ QRITA_DEV void comb_record(uint32_t* s32, uint64_t* s64, uint32_t* mn, Shared& s
     }
 }
 
-// Calls f(std::integral_constant<int, C>) for C = B .. E-1 (compile-time
-// register indices).
-template <int B, int E, class F>
-QRITA_DEV void unroll_rows(F& f) {
-    if constexpr (B < E) {
-        f(std::integral_constant<int, B>{});
-        unroll_rows<B + 1, E>(f);
+// Exclusive prefix over the waves of per-wave counts c (wave uniform):
+// returns the sum over the lower waves and sets total to the sum over all.
+template <int NT>
+QRITA_DEV uint32_t wave_prefix(uint32_t c, uint32_t& total, Shared& sh, int& rb) {
+    constexpr int NW = NT / kWave;
+    const uint32_t lane = tid_here() & (kWave - 1), wave = wave_base_here() / kWave;
+    if (lane == 0) sh.slot[rb][wave][0] = c;
+    lds_sync();
+    uint32_t before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        const uint32_t q = sh.slot[rb][w][0];
+        before += (uint32_t)w < wave ? q : 0u;
+        all += q;
+    }
+    rb ^= 1;
+    total = uni(all);
+    return uni(before);
+}
+
+template <int NT>
+QRITA_DEV uint32_t comb_sum32(uint32_t v, Shared& sh, int& rb) {
+    uint32_t s[1] = {wave_sum_u32(v)};
+    comb_record<NT, 1, 0, 0>(s, nullptr, nullptr, sh, rb);
+    return s[0];
+}
+
+// ---------------------------------------------------------------------------
+// Candidate sources. A source hands every candidate to a visitor f(key, low):
+// key 0 marks an empty slot (every real key is nonzero); low is the
+// complemented vocabulary index (sources with kLows only). Visits are
+// wave-uniform loops: every lane calls f the same number of times, so
+// visitors may use ballots.
+// ---------------------------------------------------------------------------
+
+// The row's candidate keys in LDS, interleaved over the block's threads in
+// 16-byte groups (zero padded to a multiple of four keys).
+template <int NT>
+struct SrcLds {
+    static constexpr bool kLows = false;
+    const uint32_t* a;
+    uint32_t n;
+    template <class F>
+    QRITA_DEV void visit(F&& f) const {
+        const uint32_t n4 = (n + 3u) / 4u;
+        const uint32_t lane = tid_here() & (kWave - 1);
+        for (uint32_t v0 = wave_base_here(); v0 < n4; v0 += NT) {
+            const uint32_t v = v0 + lane;
+            const uint4 q = v < n4 ? ((const uint4*)a)[v] : make_uint4(0u, 0u, 0u, 0u);
+            f(q.x, 0u);
+            f(q.y, 0u);
+            f(q.z, 0u);
+            f(q.w, 0u);
+        }
+    }
+    // this wave's share of the candidates (for sizing decisions)
+    QRITA_DEV uint32_t wave_share() const { return (n + (uint32_t)(NT / kWave) - 1u) / (uint32_t)(NT / kWave); }
+};
+
+// The row's candidate lists in global memory: S sub-lists, sub-list s holding
+// cnt[s] (LDS) entries at base + s * stride. Sub-list s is read by a group of
+// NT >> gshift threads; eight loads per thread are in flight.
+template <int NT>
+struct SrcList {
+    static constexpr bool kLows = true;
+    const uint64_t* base;
+    uint32_t stride;
+    uint32_t S;
+    uint32_t gshift;       // log2(threads per sub-list group)
+    const uint32_t* cnt;   // LDS
+    uint32_t n;            // total
+    template <class F>
+    QRITA_DEV void visit(F&& f) const {
+        constexpr int U = 8;
+        const uint32_t t = tid_here();
+        const uint32_t tps = 1u << gshift;
+        const uint32_t s = t >> gshift, g = t & (tps - 1u);
+        const uint32_t cs = s < S ? cnt[s] : 0u;
+        const uint64_t* p = base + (size_t)s * stride;
+        // wave-uniform trip count: the longest group of this wave
+        const uint32_t trips = wave_max_u32((cs + tps * U - 1u) / (tps * U));
+        for (uint32_t it = 0; it < trips; ++it) {
+            uint64_t c[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t j = g + (it * U + (uint32_t)u) * tps;
+                c[u] = j < cs ? p[j] : 0ull;
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) f(cand_key(c[u]), cand_low(c[u]));
+        }
+    }
+    QRITA_DEV uint32_t wave_share() const { return (n + (uint32_t)(NT / kWave) - 1u) / (uint32_t)(NT / kWave); }
+};
+
+// The row's logits themselves (the full-row fallback).
+template <int NT>
+struct SrcRow {
+    static constexpr bool kLows = true;
+    const void* row;
+    uint32_t V;
+    bool bf16;
+    uint32_t n;
+    template <class F>
+    QRITA_DEV void visit(F&& f) const {
+        constexpr int U = 8;
+        const uint32_t lane = tid_here() & (kWave - 1);
+        for (uint32_t i0 = wave_base_here(); i0 < V; i0 += NT * U) {
+            uint32_t b[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t i = i0 + (uint32_t)u * NT + lane;
+                b[u] = i < V ? (bf16 ? ((uint32_t)((const uint16_t*)row)[i] << 16) : ((const uint32_t*)row)[i]) : 0u;
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t i = i0 + (uint32_t)u * NT + lane;
+                f(i < V ? f32_key(b[u]) : 0u, ~i);
+            }
+        }
+    }
+    QRITA_DEV uint32_t wave_share() const { return (n + (uint32_t)(NT / kWave) - 1u) / (uint32_t)(NT / kWave); }
+};
+
+// ---------------------------------------------------------------------------
+// Per-wave search state. A wave visits either its share of the base source or
+// its own LDS segment, which holds the wave's candidates inside the range of
+// the last compaction (keys, or keys with their softmax masses). Candidates
+// above that range were dropped and are added back as counts (and masses).
+// ---------------------------------------------------------------------------
+struct WaveSet {
+    uint32_t on_seg;  // 1: the wave visits its segment
+    uint32_t n;       // entries in the segment
+    uint32_t above;   // this wave's dropped candidates above the segment's range
+    uint64_t above_m; // and their fixed-point mass
+};
+
+QRITA_DEV WaveSet wave_set_base() { return WaveSet{0u, 0u, 0u, 0ull}; }
+
+// Visit the wave's current set: f(key, low, mass). Segment entries are keys
+// (MASS false, four per 16 bytes) or (key, mass) pairs (two per 16 bytes);
+// base entries carry no mass (mass = -1: compute it).
+template <bool MASS, class S, class F>
+QRITA_DEV void visit_set(const S& src, const WaveSet& ws, const uint32_t* seg, F&& f) {
+    if (ws.on_seg) {
+        const uint32_t lane = tid_here() & (kWave - 1);
+        const uint32_t nv = MASS ? (ws.n + 1u) / 2u : (ws.n + 3u) / 4u;
+        for (uint32_t v0 = 0; v0 < nv; v0 += kWave) {
+            const uint32_t v = v0 + lane;
+            const uint4 q = v < nv ? ((const uint4*)seg)[v] : make_uint4(0u, 0u, 0u, 0u);
+            if (MASS) {
+                f(q.x, 0u, __uint_as_float(q.y));
+                f(q.z, 0u, __uint_as_float(q.w));
+            } else {
+                f(q.x, 0u, -1.0f);
+                f(q.y, 0u, -1.0f);
+                f(q.z, 0u, -1.0f);
+                f(q.w, 0u, -1.0f);
+            }
+        }
+    } else {
+        src.visit([&](uint32_t key, uint32_t low) { f(key, low, -1.0f); });
     }
 }
 
 // ---------------------------------------------------------------------------
-// Candidate sources. A source hands every candidate to a visitor as
-// (key, low, e, r): key 0 marks an empty slot or a candidate outside the
-// current set (every real key is nonzero); low is the complemented vocabulary
-// index (passed only to visits that ask for it); e is the candidate's cached
-// softmax mass (register sets, visits that ask for it); r is the register row.
+// One pivot evaluation of the quaternary search (§2), in one pass over the
+// wave sets and one block combination. With t_0 the current lower end and
+// t_1 <= t_2 <= t_3 the pivots it returns G_i = #{f > t_i} (and for the mass
+// search M_i, the fixed-point mass above t_i), and for each pivot the smallest
+// value above it (the z_mn of §2) and the largest value at or below it. The
+// minima come from wrap-around differences: f - (p + 1) is small exactly for
+// values above p, p - f exactly for values at or below it, so no lane masks
+// are needed. NP = 1 evaluates a single pivot (a binary search step); its
+// results are copied to all three pivot slots.
 //
-// RegSet keeps up to NT * R candidate keys in registers, slot (r, thread t)
-// holding candidate r * NT + t; the complemented indices and the softmax
-// masses wait in LDS under the same slot numbering. Each wave skips the
-// register rows past its last candidate, four rows per uniform branch.
+// FIELD 1 searches the complemented indices of the candidates whose key is
+// v_eq (duplicate resolution); FIELD 0 searches keys.
+//
+// With MASS, a candidate's mass exp(z - m) is taken from the segment or
+// computed (only for keys above t_0). With FILL (a mass search's first
+// evaluation on the base source), the wave also writes its candidates above
+// t_0 with their masses into its segment, as far as they fit.
 // ---------------------------------------------------------------------------
-template <int NT, int R>
-struct RegSet {
-    static constexpr int kChunk = 4;
-    static_assert(R % kChunk == 0, "register rows come in chunks");
-    uint32_t key[R];
-    uint32_t* lows;   // LDS, [R * NT]
-    float* em;        // LDS, [R * NT]: exp(z - m) once a mass search has started
-    uint32_t nslots;  // slots r * NT + t < nslots may hold candidates
+struct Eval4 {
+    uint32_t G[4];
+    uint64_t M[4];
+    uint32_t mn[3];  // smallest value above pivot i
+    uint32_t mx[3];  // largest value at or below pivot i (0: none)
+    uint32_t Gw[4];  // this wave's counts
+    uint32_t filled; // FILL: candidates the wave wrote to its segment (may exceed the segment)
+};
 
-    // number of register rows holding candidates of this thread's wave
-    QRITA_DEV int rows_here() const {
-        const uint32_t wb = wave_base_here();
-        const uint32_t ns = __builtin_amdgcn_readfirstlane(nslots);
-        return wb < ns ? (int)((ns - wb + NT - 1) / NT) : 0;
-    }
-    template <int C, class F>
-    QRITA_DEV void chunks_from(F& f, int nr) const {
-        if constexpr (C < R) {
-            if (C < nr) {
-                unroll_rows<C, C + kChunk>(f);
-                chunks_from<C + kChunk>(f, nr);
+template <int FIELD>
+QRITA_DEV uint32_t field_of(uint32_t key, uint32_t low, uint32_t v_eq) {
+    if (FIELD == 0) return key;
+    return key == v_eq ? low : 0u;
+}
+
+template <int NT, int NP, bool MASS, bool FILL, int FIELD, class S>
+QRITA_DEV Eval4 evaluate(const S& src, const WaveSet& ws, uint32_t* seg, uint32_t segcap, uint32_t v_eq, uint32_t t0,
+                         uint32_t p0, uint32_t p1, uint32_t p2, float m, Shared& sh, int rb) {
+    uint32_t g0 = 0, g1 = 0, g2 = 0, g3 = 0;
+    uint32_t a0 = 0xFFFFFFFFu, a1 = 0xFFFFFFFFu, a2 = 0xFFFFFFFFu;
+    uint32_t c0 = 0xFFFFFFFFu, c1 = 0xFFFFFFFFu, c2 = 0xFFFFFFFFu;
+    uint64_t q0 = 0, q1 = 0, q2 = 0, q3 = 0;
+    uint32_t run = 0;
+    const uint32_t s0 = p0 + 1u, s1 = p1 + 1u, s2 = p2 + 1u;
+    visit_set<MASS>(src, ws, seg, [&](uint32_t key, uint32_t low, float ec) {
+        const uint32_t f = field_of<FIELD>(key, low, v_eq);
+        const uint32_t b0 = gt01(f, t0), b1 = gt01(f, p0);
+        g0 += b0;
+        g1 += b1;
+        const uint32_t u0 = f - s0;
+        a0 = u0 < a0 ? u0 : a0;
+        const uint32_t w0 = p0 - f;
+        c0 = w0 < c0 ? w0 : c0;
+        uint32_t b2 = 0, b3 = 0;
+        if constexpr (NP == 3) {
+            b2 = gt01(f, p1);
+            b3 = gt01(f, p2);
+            g2 += b2;
+            g3 += b3;
+            const uint32_t u1 = f - s1, u2 = f - s2;
+            a1 = u1 < a1 ? u1 : a1;
+            a2 = u2 < a2 ? u2 : a2;
+            const uint32_t w1 = p1 - f, w2 = p2 - f;
+            c1 = w1 < c1 ? w1 : c1;
+            c2 = w2 < c2 ? w2 : c2;
+        }
+        if constexpr (MASS) {
+            float e = ec;
+            if (e < 0.0f) e = b0 ? mass_f32(key, m) : 0.0f;
+            const uint64_t x = fx_from_unit_f32(e);
+            q0 += b0 ? x : 0ull;
+            q1 += b1 ? x : 0ull;
+            if constexpr (NP == 3) {
+                q2 += b2 ? x : 0ull;
+                q3 += b3 ? x : 0ull;
+            }
+            if constexpr (FILL) {
+                const uint64_t bb = __ballot(b0 != 0u);
+                const uint32_t pos = run + lanes_below(bb);
+                if (b0 && pos < segcap) *(uint2*)(seg + 2 * pos) = make_uint2(key, __float_as_uint(e));
+                run += (uint32_t)__popcll(bb);
             }
         }
+    });
+    uint32_t s32[4] = {wave_sum_u32(g0) + ws.above, wave_sum_u32(g1) + ws.above, 0u, 0u};
+    uint32_t mn[6] = {wave_min_u32(a0), 0xFFFFFFFFu, 0xFFFFFFFFu, wave_min_u32(c0), 0xFFFFFFFFu, 0xFFFFFFFFu};
+    if constexpr (NP == 3) {
+        s32[2] = wave_sum_u32(g2) + ws.above;
+        s32[3] = wave_sum_u32(g3) + ws.above;
+        mn[1] = wave_min_u32(a1);
+        mn[2] = wave_min_u32(a2);
+        mn[4] = wave_min_u32(c1);
+        mn[5] = wave_min_u32(c2);
     }
-    // f(row) for the rows of every chunk holding this wave's candidates; rows
-    // past the last candidate inside the last chunk hold key 0
-    template <class F>
-    QRITA_DEV void for_rows(F&& f) const {
-        chunks_from<0>(f, rows_here());
-    }
-
-    // f(key, low, e, r); the indices (LOWS) and masses (EM) of the visited
-    // rows are read from LDS in one batch first
-    template <bool LOWS, bool EM, class F>
-    QRITA_DEV void visit(F&& f) const {
-        const uint32_t t = tid_here();
-        uint32_t lw[R];
-        float ev[R];
-        if constexpr (LOWS || EM) {
-            for_rows([&](auto rc) {
-                constexpr int r = decltype(rc)::value;
-                if (LOWS) lw[r] = lows[t + r * NT];
-                if (EM) ev[r] = em[t + r * NT];
-            });
+    Eval4 E;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) E.Gw[i] = s32[i];
+    E.filled = run;
+    if constexpr (MASS) {
+        uint64_t s64[4] = {wave_sum_u64(q0) + ws.above_m, wave_sum_u64(q1) + ws.above_m, 0ull, 0ull};
+        if constexpr (NP == 3) {
+            s64[2] = wave_sum_u64(q2) + ws.above_m;
+            s64[3] = wave_sum_u64(q3) + ws.above_m;
         }
-        for_rows([&](auto rc) {
-            constexpr int r = decltype(rc)::value;
-            f(key[r], LOWS ? lw[r] : 0u, EM ? ev[r] : 0.0f, r);
-        });
+        comb_record<NT, 4, 4, 6>(s32, s64, mn, sh, rb);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) E.M[i] = s64[i];
+    } else {
+        comb_record<NT, 4, 0, 6>(s32, nullptr, mn, sh, rb);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) E.M[i] = 0ull;
     }
-    QRITA_DEV void put_mass(int r, float e) const { em[tid_here() + r * NT] = e; }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) E.G[i] = s32[i];
+    E.mn[0] = mn[0] + s0;
+    E.mn[1] = mn[1] + s1;
+    E.mn[2] = mn[2] + s2;
+    E.mx[0] = mn[3] <= p0 ? p0 - mn[3] : 0u;
+    E.mx[1] = mn[4] <= p1 ? p1 - mn[4] : 0u;
+    E.mx[2] = mn[5] <= p2 ? p2 - mn[5] : 0u;
+    if constexpr (NP == 1) {
+        E.G[2] = E.G[3] = E.G[1];
+        E.Gw[2] = E.Gw[3] = E.Gw[1];
+        E.M[2] = E.M[3] = E.M[1];
+        E.mn[1] = E.mn[2] = E.mn[0];
+        E.mx[1] = E.mx[2] = E.mx[0];
+    }
+    return E;
+}
 
-    // The n candidates of a row list in list order; the first PR rows were
-    // read already (pre). Every load is issued before the first index is
-    // stored.
-    template <int PR>
-    QRITA_DEV void load(const uint64_t* lst, uint32_t n, const uint64_t (&pre)[PR]) {
-        nslots = n;
-        const uint32_t t = tid_here();
-        uint32_t lw[R];
-        for_rows([&](auto rc) {
-            constexpr int r = decltype(rc)::value;
-            const uint32_t i = (uint32_t)r * NT + t;
-            uint64_t c;
-            if constexpr (r < PR)
-                c = pre[r];
+// Move the wave's candidates with lo < f <= hi into its segment (in place
+// when the wave already visits its segment: entries only move down, and a
+// wave reads each group of entries before it writes any of them); the
+// candidates above hi are dropped and counted. With MASS the entries carry
+// their masses (computed here for base entries). Returns false, changing
+// nothing, when the candidates do not fit the segment.
+template <bool MASS, class S>
+QRITA_DEV bool compact_wave(const S& src, WaveSet& ws, uint32_t* seg, uint32_t segcap, uint32_t lo, uint32_t hi,
+                            float m) {
+    uint32_t run = 0, above = 0;
+    uint64_t above_m = 0;
+    visit_set<MASS>(src, ws, seg, [&](uint32_t key, uint32_t, float ec) {
+        const bool keep = key > lo && key <= hi;
+        const bool up = key > hi;
+        float e = ec;
+        if (MASS && e < 0.0f && (keep || up)) e = mass_f32(key, m);
+        if (MASS && up) above_m += fx_from_unit_f32(e);
+        above += up ? 1u : 0u;
+        const uint64_t bb = __ballot(keep);
+        const uint32_t pos = run + lanes_below(bb);
+        if (keep && pos < segcap) {
+            if (MASS)
+                *(uint2*)(seg + 2 * pos) = make_uint2(key, __float_as_uint(e));
             else
-                c = lst[i < n ? i : n - 1];
-            key[r] = i < n ? cand_key(c) : 0u;
-            lw[r] = cand_low(c);
-        });
-        for_rows([&](auto rc) {
-            constexpr int r = decltype(rc)::value;
-            lows[t + r * NT] = lw[r];
-        });
-        block_sync<NT>();
-    }
-    // drop the candidates with key below v
-    QRITA_DEV void restrict_ge(uint32_t v) {
-        for_rows([&](auto rc) {
-            constexpr int r = decltype(rc)::value;
-            key[r] = key[r] >= v ? key[r] : 0u;
-        });
-    }
-    // drop the candidates c < B
-    QRITA_DEV void restrict_to(uint64_t B) {
-        const uint32_t bk = cand_key(B), bl = cand_low(B);
-        visit<true, false>([&](uint32_t, uint32_t lw, float, int r) {
-            const uint32_t k = key[r];
-            key[r] = (k > bk || (k == bk && lw >= bl)) ? k : 0u;
-        });
-    }
-    // Move the candidates still in the set (key != 0) to the first slots, in
-    // slot order, through the mass buffer (which holds no masses yet); later
-    // visits skip the emptied rows.
-    QRITA_DEV void compact(Shared& sh, int& rb) {
-        uint32_t c = 0;
-        for_rows([&](auto rc) {
-            constexpr int r = decltype(rc)::value;
-            c += (uint32_t)__popcll(__ballot(key[r] != 0u));
-        });
-        uint32_t total = 0;
-        uint32_t run = wave_prefix<NT>(c, total, sh, rb);
-        const uint32_t t = tid_here();
-        uint32_t lw[R];
-        for_rows([&](auto rc) {
-            constexpr int r = decltype(rc)::value;
-            lw[r] = lows[t + r * NT];
-        });
-        block_sync<NT>();  // every index is read before any slot is rewritten
-        uint32_t* kb = (uint32_t*)em;
-        for_rows([&](auto rc) {
-            constexpr int r = decltype(rc)::value;
-            const uint32_t k = key[r];
-            const uint64_t b = __ballot(k != 0u);
-            if (k != 0u) {
-                const uint32_t pos = run + lanes_below(b);
-                kb[pos] = k;
-                lows[pos] = lw[r];
-            }
-            run += (uint32_t)__popcll(b);
-        });
-        block_sync<NT>();
-        nslots = total;
-        for_rows([&](auto rc) {
-            constexpr int r = decltype(rc)::value;
-            const uint32_t i = (uint32_t)r * NT + t;
-            const uint32_t k = kb[i];  // inside the buffer for every visited row
-            key[r] = i < total ? k : 0u;
-        });
-        block_sync<NT>();  // the staged keys are read before the buffer is reused
-    }
-    // chunks of rows that a set of n candidates occupies in the busiest wave
-    QRITA_DEV static uint32_t chunks_for(uint32_t n) {
-        return (n + (uint32_t)(NT * kChunk) - 1) / (uint32_t)(NT * kChunk);
-    }
-    static constexpr bool kRegs = true;
-};
-
-// MemSrc streams the candidates from memory on every visit: the row list, or
-// (ROW) the row's logits themselves for the full-row fallback (§1). Four
-// loads per thread are kept in flight.
-template <int NT, bool ROW, bool BF16>
-struct MemSrc {
-    const uint64_t* p;  // candidate array (global)
-    const void* row;    // row logits (ROW)
-    uint32_t n;
-    uint64_t filter;
-
-    QRITA_DEV uint64_t get(uint32_t i) const {
-        if (ROW) return make_cand(f32_key(__float_as_uint(load_value<BF16>(row, i))), i);
-        return p[i];
-    }
-    template <bool LOWS, bool EM, class F>
-    QRITA_DEV void visit(F&& f) const {
-        constexpr int U = 4;
-        const uint32_t t = tid_here();
-        for (uint32_t base = 0; base < n; base += NT * U) {
-            uint64_t c[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const uint32_t i = base + (uint32_t)u * NT + t;
-                c[u] = i < n ? get(i) : 0ull;
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const uint32_t i = base + (uint32_t)u * NT + t;
-                const bool ok = i < n && c[u] >= filter;
-                f(ok ? cand_key(c[u]) : 0u, cand_low(c[u]), 0.0f, 0);
-            }
+                seg[pos] = key;
         }
+        run += (uint32_t)__popcll(bb);
+    });
+    if (run > segcap) return false;  // only a base source can overflow (nothing of the segment was overwritten)
+    // zero padding after the last entry, up to the next 16-byte group
+    const uint32_t lane = tid_here() & (kWave - 1);
+    if (MASS) {
+        if (lane == 0 && (run & 1u) && run < segcap) *(uint2*)(seg + 2 * run) = make_uint2(0u, 0u);
+    } else {
+        if (lane < 3 && run + lane < ((run + 3u) & ~3u) && run + lane < segcap) seg[run + lane] = 0u;
     }
-    QRITA_DEV void put_mass(int, float) const {}
-    QRITA_DEV void restrict_ge(uint32_t v) {
-        const uint64_t b = (uint64_t)v << 32;
-        filter = b > filter ? b : filter;
-    }
-    QRITA_DEV void restrict_to(uint64_t B) { filter = B > filter ? B : filter; }
-    QRITA_DEV void compact(Shared&, int&) {}
-    QRITA_DEV static uint32_t chunks_for(uint32_t) { return 0u; }
-    static constexpr bool kRegs = false;
-};
+    ws.on_seg = 1u;
+    ws.n = run;
+    ws.above += wave_sum_u32(above);
+    if (MASS) ws.above_m += wave_sum_u64(above_m);
+    return true;
+}
 
 // Three pivots at 25/50/75 % of the open range (lo, hi) of field values
 // (hi - lo >= 2): of the key range (mode 0), or of the value range (mode 1,
 // keys only, finite ends). Pivots lie strictly inside and do not descend.
+// Mode 2 is the binary search's single pivot at 50 % of the key range.
 QRITA_DEV void make_pivots(uint32_t lo, uint32_t hi, int mode, int field, uint32_t piv[3]) {
     const uint32_t span = hi - lo;
+    if (mode == 2) {
+        uint32_t pm = lo + (span >> 1);
+        pm = pm <= lo ? lo + 1 : pm;
+        pm = pm >= hi ? hi - 1 : pm;
+        piv[0] = piv[1] = piv[2] = pm;
+        return;
+    }
     bool done = false;
     if (mode == 1 && field == 0) {
         const float a = key_value(lo), b = key_value(hi);
@@ -370,135 +512,47 @@ QRITA_DEV void make_pivots(uint32_t lo, uint32_t hi, int mode, int field, uint32
     }
 }
 
-// Field 0 searches keys; field 1 searches the complemented indices of the
-// candidates whose key is v_eq (duplicate resolution).
-template <int FIELD>
-QRITA_DEV uint32_t field_of(uint32_t key, uint32_t low, uint32_t v_eq) {
-    if (FIELD == 0) return key;
-    return key == v_eq ? low : 0u;
-}
-
-// One pivot evaluation of the quaternary search, in one pass over the source
-// and one block combination. With t_0 the current lower end and t_1 < t_2 <
-// t_3 the three pivots, it returns G_i = #{f > t_i} (and for the mass search
-// M_i, the fixed-point mass above t_i), and for each pivot the smallest value
-// above it (the z_mn of §2) and the largest value at or below it. The minima
-// come from wrap-around differences: f - (p + 1) is small exactly for values
-// above p, p - f exactly for values at or below it, so no lane masks are
-// needed.
-//
-// MM = 0 counts only; MM = 1 computes each candidate's mass exp(z - m) and
-// caches it; MM = 2 reads the cached masses.
-struct Eval4 {
-    uint32_t G[4];
-    uint64_t M[4];
-    uint32_t mn[3];  // smallest value above pivot i
-    uint32_t mx[3];  // largest value at or below pivot i (0: none)
-};
-
-template <int NT, int FIELD, int MM, class S>
-QRITA_DEV Eval4 eval4(const S& src, uint32_t v_eq, uint32_t t0, const uint32_t piv[3], float m, Shared& sh,
-                      int& rb) {
-    constexpr bool MASS = MM != 0;
-    constexpr bool CACHED = MM == 2 && S::kRegs;
-    uint32_t g0 = 0, g1 = 0, g2 = 0, g3 = 0;
-    uint32_t a0 = 0xFFFFFFFFu, a1 = 0xFFFFFFFFu, a2 = 0xFFFFFFFFu;
-    uint32_t c0 = 0xFFFFFFFFu, c1 = 0xFFFFFFFFu, c2 = 0xFFFFFFFFu;
-    // register sets: 32-bit halves of the fixed-point masses; streamed
-    // sources: 64-bit sums (any number of candidates per lane)
-    uint32_t h0 = 0, h1 = 0, h2 = 0, h3 = 0, l0 = 0, l1 = 0, l2 = 0, l3 = 0;
-    uint64_t q0 = 0, q1 = 0, q2 = 0, q3 = 0;
-    const uint32_t p0 = piv[0], p1 = piv[1], p2 = piv[2];
-    const uint32_t s0 = p0 + 1u, s1 = p1 + 1u, s2 = p2 + 1u;
-    src.template visit<FIELD == 1, CACHED>([&](uint32_t key, uint32_t low, float ec, int r) {
-        const uint32_t f = field_of<FIELD>(key, low, v_eq);
-        const uint32_t b0 = gt01(f, t0), b1 = gt01(f, p0), b2 = gt01(f, p1), b3 = gt01(f, p2);
-        g0 += b0;
-        g1 += b1;
-        g2 += b2;
-        g3 += b3;
-        const uint32_t u0 = f - s0, u1 = f - s1, u2 = f - s2;
-        a0 = u0 < a0 ? u0 : a0;
-        a1 = u1 < a1 ? u1 : a1;
-        a2 = u2 < a2 ? u2 : a2;
-        const uint32_t w0 = p0 - f, w1 = p1 - f, w2 = p2 - f;
-        c0 = w0 < c0 ? w0 : c0;
-        c1 = w1 < c1 ? w1 : c1;
-        c2 = w2 < c2 ? w2 : c2;
-        if constexpr (MASS) {
-            float e = ec;
-            if constexpr (!CACHED) {
-                // computed where the visit runs: hoisted out of the row-chunk
-                // branches it would be paid for every register row
-                uint32_t kk = key;
-                asm volatile("" : "+v"(kk));
-                e = kk ? mass_f32(kk, m) : 0.0f;
-            }
-            if constexpr (MM == 1) src.put_mass(r, e);
-            if constexpr (S::kRegs) {
-                uint32_t eh, el;
-                fx_split(e, eh, el);
-                h0 += __umul24(b0, eh);
-                l0 += __umul24(b0, el);
-                h1 += __umul24(b1, eh);
-                l1 += __umul24(b1, el);
-                h2 += __umul24(b2, eh);
-                l2 += __umul24(b2, el);
-                h3 += __umul24(b3, eh);
-                l3 += __umul24(b3, el);
-            } else {
-                const uint64_t x = fx_from_unit_f32(e);
-                q0 += b0 ? x : 0ull;
-                q1 += b1 ? x : 0ull;
-                q2 += b2 ? x : 0ull;
-                q3 += b3 ? x : 0ull;
-            }
-        }
-    });
-    uint32_t s32[4] = {wave_sum_u32(g0), wave_sum_u32(g1), wave_sum_u32(g2), wave_sum_u32(g3)};
-    uint32_t mn[6] = {wave_min_u32(a0), wave_min_u32(a1), wave_min_u32(a2),
-                      wave_min_u32(c0), wave_min_u32(c1), wave_min_u32(c2)};
-    Eval4 E;
-    if constexpr (MASS) {
-        uint64_t s64[4];
-        if constexpr (S::kRegs) {
-            s64[0] = wave_sum_split(h0, l0);
-            s64[1] = wave_sum_split(h1, l1);
-            s64[2] = wave_sum_split(h2, l2);
-            s64[3] = wave_sum_split(h3, l3);
-        } else {
-            s64[0] = wave_sum_u64(q0);
-            s64[1] = wave_sum_u64(q1);
-            s64[2] = wave_sum_u64(q2);
-            s64[3] = wave_sum_u64(q3);
-        }
-        comb_record<NT, 4, 4, 6>(s32, s64, mn, sh, rb);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) E.M[i] = s64[i];
-    } else {
-        comb_record<NT, 4, 0, 6>(s32, nullptr, mn, sh, rb);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) E.M[i] = 0ull;
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) E.G[i] = s32[i];
-    E.mn[0] = mn[0] + s0;
-    E.mn[1] = mn[1] + s1;
-    E.mn[2] = mn[2] + s2;
-    E.mx[0] = mn[3] <= p0 ? p0 - mn[3] : 0u;
-    E.mx[1] = mn[4] <= p1 ? p1 - mn[4] : 0u;
-    E.mx[2] = mn[5] <= p2 ? p2 - mn[5] : 0u;
-    return E;
-}
-
 template <class T>
 QRITA_DEV T pick4(int j, T a, T b, T c, T d) {
     return j == 3 ? d : (j == 2 ? c : (j == 1 ? b : a));
 }
 
+// The search context of one row: its candidate source and LDS regions.
+template <class T, class S>
+struct Ctx {
+    S src;
+    uint32_t* seg;     // this wave's segment
+    uint32_t segcap;   // entries of 8 bytes
+    int mode;          // pivot placement
+    Shared* sh;
+    int rb;
+    int iters;
+};
+
+template <class T>
+QRITA_DEV uint32_t* wave_segment() {
+    return (uint32_t*)(dyn_lds() + T::W_OFF + (size_t)(wave_base_here() / kWave) * T::SEG * 8);
+}
+
 struct CountOut {
     uint32_t v, n_gt, N;
 };
+
+// Dispatch of the evaluation: one pivot for mode 2, three otherwise.
+template <int NT, bool MASS, bool FILL, int FIELD, class C>
+QRITA_DEV Eval4 eval_step(C& c, const WaveSet& ws, uint32_t segcap, uint32_t v_eq, uint32_t t0, const uint32_t piv[3],
+                          float m) {
+    Eval4 E;
+    if (c.mode == 2)
+        E = evaluate<NT, 1, MASS, FILL, FIELD>(c.src, ws, c.seg, segcap, v_eq, t0, piv[0], piv[1], piv[2], m, *c.sh,
+                                               c.rb);
+    else
+        E = evaluate<NT, 3, MASS, FILL, FIELD>(c.src, ws, c.seg, segcap, v_eq, t0, piv[0], piv[1], piv[2], m, *c.sh,
+                                               c.rb);
+    c.rb ^= 1;
+    ++c.iters;
+    return E;
+}
 
 // Quaternary pivot search for the K-th largest field value (K >= 1) among
 // the source's candidates, with duplicates (§2): returns v, n_gt = #{> v} and
@@ -513,22 +567,25 @@ struct CountOut {
 // becomes the lower end, and its multiplicity N_zmn = G(t_j*) - G(z_mn) comes
 // from the next evaluation, which counts above the lower end as well: if then
 // G(z_mn) < K, the search ends at v = z_mn (the termination test of §2,
-// #{> z_mn} < K <= #{>= z_mn}).
-template <int NT, int FIELD, class S>
-QRITA_DEV CountOut qsearch_count(const S& src, uint32_t v_eq, uint32_t K, int64_t lo_in, uint32_t G_lo,
-                                 int64_t hi_in, uint32_t G_hi, int mode, Shared& sh, int& rb, int& iters) {
+// #{> z_mn} < K <= #{>= z_mn}). After each step every wave keeps only its
+// candidates inside the new range (FIELD 0).
+template <int NT, int FIELD, class C>
+QRITA_DEV CountOut search_count(C& c, uint32_t v_eq, uint32_t K, int64_t lo_in, uint32_t G_lo, int64_t hi_in,
+                                uint32_t G_hi) {
     // every field value is nonzero, so a lower end below 0 is the same as 0
     uint32_t lo = lo_in > 0 ? (uint32_t)lo_in : 0u;
     uint32_t hi = (uint32_t)hi_in;
     bool conf = true;   // G(lo) = G_lo is known (then G_lo >= K)
     uint32_t G_up = 0;  // lo not confirmed: G at the pivot below lo
+    WaveSet ws = wave_set_base();
+    const uint32_t kcap = 2u * c.segcap;  // keys fit two per 8-byte entry
+    uint32_t share = c.src.wave_share();
 #pragma unroll 1
     for (int guard = 0; guard < 80; ++guard) {
         if (conf && hi - lo <= 1) return CountOut{hi, G_hi, G_lo - G_hi};
         uint32_t piv[3] = {hi, hi, hi};
-        if (hi - lo >= 2) make_pivots(lo, hi, mode, FIELD, piv);
-        const Eval4 E = eval4<NT, FIELD, 0>(src, v_eq, lo, piv, 0.0f, sh, rb);
-        ++iters;
+        if (hi - lo >= 2) make_pivots(lo, hi, c.mode, FIELD, piv);
+        const Eval4 E = eval_step<NT, false, false, FIELD>(c, ws, kcap, v_eq, lo, piv, 0.0f);
         if (!conf) {
             if (E.G[0] < K) return CountOut{lo, E.G[0], G_up - E.G[0]};
             conf = true;
@@ -548,6 +605,15 @@ QRITA_DEV CountOut qsearch_count(const S& src, uint32_t v_eq, uint32_t K, int64_
         if (js < 3) {
             hi = up;
             G_hi = G_n;
+        }
+        if constexpr (FIELD == 0) {
+            // this wave's candidates in the new range (lo, hi] are among those
+            // in (t_js, t_js+1]
+            const uint32_t bound = pick4(js, E.Gw[0], E.Gw[1], E.Gw[2], E.Gw[3]) -
+                                   pick4(js, E.Gw[1], E.Gw[2], E.Gw[3], ws.above);
+            if (bound <= kcap && bound * 4u <= share * 3u) {
+                if (compact_wave<false>(c.src, ws, c.seg, kcap, lo, hi, 0.0f)) share = ws.n;
+            }
         }
     }
     return CountOut{hi, G_hi, G_lo - G_hi};  // not reached for consistent inputs
@@ -572,18 +638,21 @@ struct MassSet {
 
 // The quaternary search over softmax mass (top-p): finds the key v with
 // M(> v) < T <= M(>= v), T = p * (M(set) + rest). The masses are integers, so
-// M >= T is tested as M >= Tq = ceil(T). The first evaluation also computes
-// and caches every candidate's mass and the set's total. Returns false on a
-// miss (need_all and the source holds less than T).
-template <int NT, class S>
-QRITA_DEV bool qsearch_mass(const S& src, const MassSet& ms, float m, int64_t lo_in, int64_t hi_in, int mode,
-                            Shared& sh, int& rb, int& iters, MassOut& out, uint64_t& Tq) {
+// M >= T is tested as M >= Tq = ceil(T). The first evaluation computes every
+// candidate's mass, the set's total and, where they fit, writes the
+// candidates with their masses to the wave segments. Returns false on a miss
+// (need_all and the source holds less than T).
+template <int NT, class C>
+QRITA_DEV bool search_mass(C& c, const MassSet& ms, float m, int64_t lo_in, int64_t hi_in, MassOut& out,
+                           uint64_t& Tq) {
     uint32_t lo = lo_in > 0 ? (uint32_t)lo_in : 0u;
     uint32_t hi = (uint32_t)hi_in;
     const uint64_t ex = ms.dN ? (uint64_t)ms.dN * mass_fx(ms.vx, m) : 0ull;
     uint64_t M_hi = 0;
     uint32_t G_hi = 0, G_lo = 0, G_up = 0;
     bool conf = true;
+    WaveSet ws = wave_set_base();
+    uint32_t share = c.src.wave_share();
 #pragma unroll 1
     for (int guard = 0; guard < 80; ++guard) {
         if (guard > 0 && conf && hi - lo <= 1) {
@@ -591,13 +660,21 @@ QRITA_DEV bool qsearch_mass(const S& src, const MassSet& ms, float m, int64_t lo
             return true;
         }
         uint32_t piv[3] = {hi, hi, hi};
-        if (hi - lo >= 2) make_pivots(lo, hi, mode, 0, piv);
+        if (hi - lo >= 2) make_pivots(lo, hi, c.mode, 0, piv);
         Eval4 E;
-        if (guard == 0)
-            E = eval4<NT, 0, 1>(src, 0u, lo, piv, m, sh, rb);
-        else
-            E = eval4<NT, 0, 2>(src, 0u, lo, piv, m, sh, rb);
-        ++iters;
+        if (guard == 0) {
+            E = eval_step<NT, true, true, 0>(c, ws, c.segcap, 0u, lo, piv, m);
+            // the candidates above lo now sit in the wave's segment, if they fit
+            if (E.filled <= c.segcap) {
+                if ((tid_here() & (kWave - 1)) == 0 && (E.filled & 1u) && E.filled < c.segcap)
+                    *(uint2*)(c.seg + 2 * E.filled) = make_uint2(0u, 0u);
+                ws.on_seg = 1u;
+                ws.n = E.filled;
+                share = E.filled;
+            }
+        } else {
+            E = eval_step<NT, true, false, 0>(c, ws, c.segcap, 0u, lo, piv, m);
+        }
         if (lo < ms.vx) {
             E.G[0] -= ms.dN;
             E.M[0] -= ex;
@@ -634,93 +711,22 @@ QRITA_DEV bool qsearch_mass(const S& src, const MassSet& ms, float m, int64_t lo
             G_hi = G_n;
             M_hi = M_n;
         }
+        // keep the wave's candidates in (lo, hi] (with masses); the
+        // correction for the duplicates at vx stays valid: it applies only
+        // while lo < vx, and until then the candidates at vx are kept
+        const uint32_t bound = pick4(js, E.Gw[0], E.Gw[1], E.Gw[2], E.Gw[3]) -
+                                   pick4(js, E.Gw[1], E.Gw[2], E.Gw[3], ws.above);
+        if (bound <= c.segcap && bound * 4u <= share * 3u) {
+            if (compact_wave<true>(c.src, ws, c.seg, c.segcap, lo, hi, m)) share = ws.n;
+        }
     }
     out = MassOut{hi, G_hi, G_lo - G_hi, M_hi};  // not reached for consistent inputs
     return true;
 }
 
-// Boundary of "the `need` lowest-index candidates with key v, plus everything
-// above v" among the source's candidates (N of them have key v), never below
-// `floor`. A small tie group is ranked directly in LDS; a large one by a
-// quaternary search over the tied candidates' indices.
-template <int NT, class S>
-QRITA_DEV uint64_t tie_boundary(const S& src, uint32_t v, uint32_t need, uint32_t N, uint32_t V,
-                                uint64_t floor, Shared& sh, int& rb, int& iters) {
-    uint64_t b = (uint64_t)v << 32;
-    if (need < N) {
-        if (N <= kTieDirect) {
-            const uint32_t lane = tid_here() & (kWave - 1);
-            block_sync<NT>();
-            if (threadIdx.x == 0) sh.gather_n = 0;
-            // zeros after the ties (below every complemented index) round the
-            // list up to whole uint4 reads
-            if (threadIdx.x < 4u && N + threadIdx.x < (uint32_t)kTieDirect) sh.ties[N + threadIdx.x] = 0u;
-            if constexpr (S::kRegs) {
-                // slots from per-wave counts, no atomics
-                uint32_t c = 0;
-                src.template visit<false, false>(
-                    [&](uint32_t key, uint32_t, float, int) { c += (uint32_t)__popcll(__ballot(key == v)); });
-                uint32_t total = 0;
-                uint32_t run = wave_prefix<NT>(c, total, sh, rb);
-                src.template visit<true, false>([&](uint32_t key, uint32_t low, float, int) {
-                    const bool tie = key == v;
-                    const uint64_t bb = __ballot(tie);
-                    const uint32_t pos = run + lanes_below(bb);
-                    if (tie && pos < (uint32_t)kTieDirect) sh.ties[pos] = low;
-                    run += (uint32_t)__popcll(bb);
-                });
-            } else {
-                block_sync<NT>();
-                src.template visit<true, false>([&](uint32_t key, uint32_t low, float, int) {
-                    const bool tie = key == v;
-                    const uint64_t bb = __ballot(tie);
-                    if (bb) {
-                        uint32_t base = 0;
-                        if (lane == 0) base = atomicAdd(&sh.gather_n, (uint32_t)__popcll(bb));
-                        base = readlane(base, 0);
-                        const uint32_t pos = base + lanes_below(bb);
-                        if (tie && pos < (uint32_t)kTieDirect) sh.ties[pos] = low;
-                    }
-                });
-            }
-            block_sync<NT>();
-            // the tie whose complemented index has exactly need - 1 larger ones
-            const uint32_t n4 = (N + 3u) / 4u;
-            for (uint32_t i = threadIdx.x; i < N; i += NT) {
-                const uint32_t x = sh.ties[i];
-                uint32_t above = 0;
-                for (uint32_t j = 0; j < n4; ++j) {
-                    const uint4 q = *(const uint4*)&sh.ties[4 * j];
-                    above += (q.x > x ? 1u : 0u) + (q.y > x ? 1u : 0u) + (q.z > x ? 1u : 0u) + (q.w > x ? 1u : 0u);
-                }
-                if (above == need - 1) sh.u32[6] = x;
-            }
-            block_sync<NT>();
-            b |= uni(sh.u32[6]);
-        } else {
-            const int64_t lo = (int64_t)(0xFFFFFFFFu - (uint32_t)(V - 1)) - 1;
-            const CountOut t = qsearch_count<NT, 1>(src, v, need, lo, N, (int64_t)0xFFFFFFFFu, 0u, 0, sh, rb,
-                                                    iters);
-            b |= t.v;
-        }
-    }
-    return b > floor ? b : floor;
-}
-
-// Boundary B of the K largest of the source's `total` candidates, whose keys
-// lie in (lo_key, kmax].
-template <int NT, class S>
-QRITA_DEV uint64_t select_boundary(const S& src, uint32_t K, uint32_t total, int64_t lo_key, uint32_t kmax,
-                                   uint32_t V, int mode, uint64_t floor, Shared& sh, int& rb, int& iters) {
-    const CountOut r =
-        qsearch_count<NT, 0>(src, 0u, K, lo_key, total, (int64_t)kmax, 0u, mode, sh, rb, iters);
-    return tie_boundary<NT>(src, r.v, K - r.n_gt, r.N, V, floor, sh, rb, iters);
-}
-
 // ---------------------------------------------------------------------------
-// Rank order of the kept set (a7). The candidates to order sit in LDS as
-// (key << 32 | ~index), so descending words are descending values with ties
-// by ascending index, a total order.
+// Rank order of a set of distinct words (key << 32 | ~index): descending
+// words are descending values with ties by ascending index, a total order.
 // ---------------------------------------------------------------------------
 QRITA_DEV uint32_t next_pow2(uint32_t x) {
     uint32_t p = 1;
@@ -728,137 +734,13 @@ QRITA_DEV uint32_t next_pow2(uint32_t x) {
     return p;
 }
 
-// Where a sort puts the candidate of rank r: index r of the index output
-// (r < lout) and, for r < lmask, its mask byte.
-struct RankOut {
-    int32_t* out;
-    uint32_t lout;
-    uint8_t* mrow;
-    uint32_t lmask;
-    QRITA_DEV void put(uint32_t r, uint32_t idx) const {
-        if (r < lout) out[r] = (int32_t)idx;
-        if (r < lmask) mrow[idx] = 1;
-    }
-};
+QRITA_DEV uint32_t bits_for(uint64_t x) { return x ? 64u - (uint32_t)__builtin_clzll(x) : 0u; }
 
-// Up to NT entries: each entry's rank is the number of larger entries,
-// counted by NT / next_pow2(cnt) threads per entry over a share of the
-// entries each, the shares added in LDS. The entries are read eight at a time
-// (zero padding after the last one is below every entry).
-template <int NT>
-QRITA_DEV void rank_sort(uint64_t* a, uint32_t cnt, const RankOut& ro, Shared& sh) {
-    const uint32_t P = (uint32_t)NT / next_pow2(cnt);
-    const uint32_t t = threadIdx.x, e = t / P, q = t % P;
-    const uint32_t span = (((cnt + P - 1) / P) + 7u) & ~7u;
-    if (t < 8u) a[cnt + t] = 0ull;
-    if (q == 0 && e < cnt) sh.ties[e] = 0u;
-    lds_sync();
-    uint64_t x = 0;
-    if (e < cnt) {
-        x = a[e];
-        const uint32_t j0 = q * span, j1 = min(j0 + span, (cnt + 7u) & ~7u);
-        uint32_t above = 0;
-#pragma unroll 4
-        for (uint32_t j = j0; j < j1; j += 8) {
-            const uint4* v = (const uint4*)(a + j);
-            const uint4 v0 = v[0], v1 = v[1], v2 = v[2], v3 = v[3];
-            const uint64_t y[8] = {((uint64_t)v0.y << 32) | v0.x, ((uint64_t)v0.w << 32) | v0.z,
-                                   ((uint64_t)v1.y << 32) | v1.x, ((uint64_t)v1.w << 32) | v1.z,
-                                   ((uint64_t)v2.y << 32) | v2.x, ((uint64_t)v2.w << 32) | v2.z,
-                                   ((uint64_t)v3.y << 32) | v3.x, ((uint64_t)v3.w << 32) | v3.z};
-#pragma unroll
-            for (int u = 0; u < 8; ++u) above += y[u] > x ? 1u : 0u;
-        }
-        if (above) atomicAdd(&sh.ties[e], above);
-    }
-    lds_sync();
-    if (q == 0 && e < cnt) ro.put(sh.ties[e], cand_idx(x));
-}
-
-// Bitonic sort, descending, of the NT * E entries a[0 .. NT*E) (any order),
-// then out[g] = index of rank g for g < cnt. Thread t holds the logical
-// elements g = t * E + e in registers. By partner distance j a stage runs in
-// the thread's registers (j < E), across lanes of the wave with shuffles
-// (E <= j < 64 E) or across waves through LDS (j >= 64 E; element (t, e) at
-// a[e * NT + t], so the accesses of a wave are consecutive).
-template <int NT, int E>
-QRITA_DEV void bitonic_sort(uint64_t* a, const RankOut& ro, uint32_t cnt) {
-    constexpr uint32_t NP = (uint32_t)NT * E;
-    const uint32_t t = tid_here() % NT;
-    uint64_t x[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) x[e] = a[e * NT + t];
-    for (uint32_t k = 2; k <= NP; k <<= 1) {
-        for (uint32_t j = k >> 1; j >= 64u * E; j >>= 1) {
-            block_sync<NT>();
-#pragma unroll
-            for (int e = 0; e < E; ++e) a[e * NT + t] = x[e];
-            block_sync<NT>();
-            const uint32_t pt = t ^ (j / E);
-            const uint32_t g0 = t * E;
-            // the lower position of a descending pair keeps the larger value
-            const bool keep_max = ((g0 & j) == 0) == ((g0 & k) == 0);
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                const uint64_t y = a[e * NT + pt];
-                x[e] = ((x[e] > y) == keep_max) ? x[e] : y;
-            }
-        }
-        for (uint32_t j = min(k >> 1, 32u * E); j >= (uint32_t)E; j >>= 1) {
-            const uint32_t g0 = t * E;
-            const bool keep_max = ((g0 & j) == 0) == ((g0 & k) == 0);
-            const uint32_t d = j / E;
-            {
-                // every exchange of the stage is issued before the first compare
-                const int src_lane = (int)(((t ^ d) & (kWave - 1)) << 2);
-                uint32_t ylo[E], yhi[E];
-#pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    ylo[e] = (uint32_t)__builtin_amdgcn_ds_bpermute(src_lane, (int)(uint32_t)x[e]);
-                    yhi[e] = (uint32_t)__builtin_amdgcn_ds_bpermute(src_lane, (int)(uint32_t)(x[e] >> 32));
-                }
-#pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    const uint64_t y = ((uint64_t)yhi[e] << 32) | ylo[e];
-                    x[e] = ((x[e] > y) == keep_max) ? x[e] : y;
-                }
-            }
-        }
-        // direction of element e: descending iff bit k of t * E + e is clear;
-        // for k >= E that is one lane mask for all e, below it depends on e only
-        const bool desc_t = ((t * E) & k) == 0;
-#pragma unroll
-        for (int j = E / 2; j >= 1; j >>= 1) {
-            if ((uint32_t)j < k) {
-#pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    if ((e & j) == 0) {
-                        const bool desc = k >= (uint32_t)E ? desc_t : (((uint32_t)e & k) == 0);
-                        const uint64_t p = x[e], q = x[e | j];
-                        // equal entries (only padding) may swap either way
-                        const bool sw = (p < q) == desc;
-                        x[e] = sw ? q : p;
-                        x[e | j] = sw ? p : q;
-                    }
-                }
-            }
-        }
-    }
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-        const uint32_t g = t * E + e;
-        if (g < cnt) ro.put(g, cand_idx(x[e]));
-    }
-}
-
-// Exclusive prefix sum, in place, of the n <= kSortBins counts v[0 .. n)
-// (thread t owns entries [t * per, (t + 1) * per)); v[n] becomes the total.
-// Returns the largest count (uniform). One block round.
-constexpr uint32_t kSortBins = 4096;
-
-template <int NT>
+// Exclusive prefix sum, in place, of the n counts v[0 .. n) (n <= NB); v[n]
+// becomes the total. Returns the largest count (uniform). One block round.
+template <int NT, int NB>
 QRITA_DEV uint32_t scan_counts(uint32_t* v, uint32_t n, Shared& sh, int& rb) {
-    constexpr int PER = (int)(kSortBins / NT);
+    constexpr int PER = NB / NT;
     const uint32_t t = threadIdx.x;
     const uint32_t per = (n + NT - 1) / NT;
     uint32_t c[PER];
@@ -885,16 +767,16 @@ QRITA_DEV uint32_t scan_counts(uint32_t* v, uint32_t n, Shared& sh, int& rb) {
         uint32_t* rec = &sh.slot[rb][0][0];
         if (lane == 0) *(uint2*)(rec + wave * 2) = make_uint2(wtot, wbig);
         lds_sync();
-        uint32_t m = 0;
+        uint32_t mm = 0;
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
             const uint2 q = *(const uint2*)(rec + w * 2);
             run += (uint32_t)w < wave ? q.x : 0u;
             total += q.x;
-            m = q.y > m ? q.y : m;
+            mm = q.y > mm ? q.y : mm;
         }
         rb ^= 1;
-        big = uni(m);
+        big = uni(mm);
     }
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
@@ -907,56 +789,119 @@ QRITA_DEV uint32_t scan_counts(uint32_t* v, uint32_t n, Shared& sh, int& rb) {
     return big;
 }
 
-// Bucket sort, descending, of the cnt <= E * NT distinct words a[0 .. cnt)
-// into out[rank] = index. Thread t holds words e * NT + t in registers.
-//
+// Where a sort puts the word of rank r: index r of the index output
+// (r < lout); with `kept`, the position p of the word in the sort's position
+// array records its index when r < lmask (else ~0), for the mask afterwards;
+// without it, the mask byte is set directly.
+struct RankOut {
+    int32_t* out;
+    uint32_t lout;
+    uint8_t* mrow;    // scattered mask bytes (null: none)
+    uint32_t* kept;   // LDS, [cnt] (null: none)
+    uint32_t lmask;
+    QRITA_DEV void put(uint32_t r, uint32_t idx, uint32_t p) const {
+        if (r < lout) out[r] = (int32_t)idx;
+        if (mrow && r < lmask) mrow[idx] = 1;
+        if (kept) kept[p] = r < lmask ? idx : 0xFFFFFFFFu;
+    }
+};
+
+// Up to NT words: each word's rank is the number of larger words, counted by
+// NT / next_pow2(cnt) threads per word over a share of the words each, the
+// shares added in LDS.
+template <int NT>
+QRITA_DEV void rank_sort(uint64_t* a, uint32_t cnt, const RankOut& ro, uint32_t* acc) {
+    const uint32_t P = (uint32_t)NT / next_pow2(cnt);
+    const uint32_t t = threadIdx.x, e = t / P, q = t % P;
+    const uint32_t span = (((cnt + P - 1) / P) + 7u) & ~7u;
+    if (t < 8u) a[cnt + t] = 0ull;
+    if (q == 0 && e < cnt) acc[e] = 0u;
+    lds_sync();
+    uint64_t x = 0;
+    if (e < cnt) {
+        x = a[e];
+        const uint32_t j0 = q * span, j1 = min(j0 + span, (cnt + 7u) & ~7u);
+        uint32_t above = 0;
+        for (uint32_t j = j0; j < j1; j += 8) {
+            const uint4* v = (const uint4*)(a + j);
+            const uint4 v0 = v[0], v1 = v[1], v2 = v[2], v3 = v[3];
+            const uint64_t y[8] = {((uint64_t)v0.y << 32) | v0.x, ((uint64_t)v0.w << 32) | v0.z,
+                                   ((uint64_t)v1.y << 32) | v1.x, ((uint64_t)v1.w << 32) | v1.z,
+                                   ((uint64_t)v2.y << 32) | v2.x, ((uint64_t)v2.w << 32) | v2.z,
+                                   ((uint64_t)v3.y << 32) | v3.x, ((uint64_t)v3.w << 32) | v3.z};
+#pragma unroll
+            for (int u = 0; u < 8; ++u) above += y[u] > x ? 1u : 0u;
+        }
+        if (above) atomicAdd(&acc[e], above);
+    }
+    lds_sync();
+    if (q == 0 && e < cnt) ro.put(acc[e], cand_idx(x), e);
+    lds_sync();
+}
+
+// Bitonic sort, descending, of the np (a power of two, <= the words' region)
+// words a[0 .. np) in LDS, one barrier per stage; then the rank of position g
+// is g. For sets the bucket sort cannot split.
+template <int NT>
+QRITA_DEV void bitonic_lds(uint64_t* a, uint32_t np, uint32_t cnt, const RankOut& ro) {
+    const uint32_t t = threadIdx.x;
+    for (uint32_t k = 2; k <= np; k <<= 1) {
+        for (uint32_t j = k >> 1; j >= 1; j >>= 1) {
+            for (uint32_t i = t; i < np / 2; i += NT) {
+                // the i-th pair of this stage: lower position x, partner x | j
+                const uint32_t x = ((i & ~(j - 1u)) << 1) | (i & (j - 1u));
+                const uint32_t y = x | j;
+                const uint64_t u = a[x], v = a[y];
+                const bool desc = (x & k) == 0;
+                if ((u < v) == desc) {
+                    a[x] = v;
+                    a[y] = u;
+                }
+            }
+            lds_sync();
+        }
+    }
+    for (uint32_t g = t; g < cnt; g += NT) ro.put(g, cand_idx(a[g]), g);
+    lds_sync();
+}
+
+// Bucket sort, descending, of the cnt distinct words a[0 .. cnt) (LDS).
 // Bins ascend as words descend. Keys are coded exactly as (kmax - key) >> z,
 // z the number of low bits all keys share (16 for bf16 logits), coarsened by
 // dropping low code bits if the codes outnumber the bins. Within a code,
 // words spread by a sub-coordinate: the dropped code bits, then the index
 // (lmax - low), so tie groups spread too. First every code gets the same
 // number of bins; if a bin then holds more than kMaxBin words, each code
-// instead gets a run of bins in proportion to how many words it holds (from
-// a histogram over the codes). A word's rank is its bin's start plus the
-// number of larger words in its bin, counted directly, so the result does
-// not depend on the order of the LDS atomics that fill the bins. Returns
-// false, having written nothing, when a bin still holds more than kMaxBin
-// words.
+// instead gets a run of bins in proportion to how many words it holds (code
+// starts in hc). The words' positions are scattered into bins (pos array,
+// LDS); a word's rank is its bin's start plus the number of larger words in
+// its bin, counted directly, so the result does not depend on the order of
+// the LDS atomics that fill the bins. Returns false, having written nothing,
+// when a bin still holds more than kMaxBin words.
 constexpr uint32_t kMaxBin = 96;
 
-QRITA_DEV uint32_t bits_for(uint64_t x) { return x ? 64u - (uint32_t)__builtin_clzll(x) : 0u; }
-
-template <int NT, int E>
-QRITA_DEV bool bucket_sort(uint64_t* a, uint32_t cnt, const RankOut& ro, uint64_t* b, uint32_t* bins, Shared& sh,
-                           int& rb) {
+template <int NT, int NB>
+QRITA_DEV bool bucket_sort(const uint64_t* a, uint32_t cnt, const RankOut& ro, uint32_t* pos, uint32_t* bins,
+                           uint32_t* hc, Shared& sh, int& rb) {
     const uint32_t t = threadIdx.x;
-    uint64_t x[E];
     const uint32_t key0 = uni(cand_key(a[0]));
     uint32_t kmn = 0xFFFFFFFFu, kmx = 0u, lmn = 0xFFFFFFFFu, lmx = 0u, tz = 32u;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-        const uint32_t i = (uint32_t)e * NT + t;
-        x[e] = i < cnt ? a[i] : 0ull;
-    }
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-        const uint32_t i = (uint32_t)e * NT + t;
-        if (i < cnt) {
-            const uint32_t k = cand_key(x[e]), l = cand_low(x[e]);
-            kmn = k < kmn ? k : kmn;
-            kmx = k > kmx ? k : kmx;
-            lmn = l < lmn ? l : lmn;
-            lmx = l > lmx ? l : lmx;
-            const uint32_t d = k ^ key0;
-            const uint32_t z = d ? (uint32_t)__builtin_ctz(d) : 32u;
-            tz = z < tz ? z : tz;
-        }
+    for (uint32_t i = t; i < cnt; i += NT) {
+        const uint64_t w = a[i];
+        const uint32_t k = cand_key(w), l = cand_low(w);
+        kmn = k < kmn ? k : kmn;
+        kmx = k > kmx ? k : kmx;
+        lmn = l < lmn ? l : lmn;
+        lmx = l > lmx ? l : lmx;
+        const uint32_t d = k ^ key0;
+        const uint32_t z = d ? (uint32_t)__builtin_ctz(d) : 32u;
+        tz = z < tz ? z : tz;
     }
     uint32_t ext[5] = {wave_min_u32(kmn), ~wave_max_u32(kmx), wave_min_u32(lmn), ~wave_max_u32(lmx),
                        wave_min_u32(tz)};
     // the bin counts are cleared before the combination's barrier, which
     // orders them before the first count
-    const uint32_t nb = min(kSortBins, 2u * next_pow2(cnt));
+    const uint32_t nb = min((uint32_t)NB, 2u * next_pow2(cnt));
     for (uint32_t i = t; i <= nb; i += NT) bins[i] = 0u;
     comb_record<NT, 0, 0, 5>(nullptr, nullptr, ext, sh, rb);
     kmn = uni(ext[0]);
@@ -974,8 +919,6 @@ QRITA_DEV bool bucket_sort(uint64_t* a, uint32_t cnt, const RankOut& ro, uint64_
     const uint32_t sfull = kdrop + lbits;
     const uint32_t scut = sfull > 48u ? sfull - 48u : 0u;
     const uint32_t sbits = sfull - scut;
-    // a word's code and sub-coordinate, recomputed where needed (fewer
-    // registers held across the phases)
     auto code_of = [&](uint64_t w) { return ((kmx - cand_key(w)) >> kz) >> kdrop; };
     auto sub_of = [&](uint64_t w) {
         const uint32_t fine = (kmx - cand_key(w)) >> kz;
@@ -985,242 +928,152 @@ QRITA_DEV bool bucket_sort(uint64_t* a, uint32_t cnt, const RankOut& ro, uint64_
     // every code the same run of bins: code bits, then the top sub bits
     const uint32_t lkeep = nbits - (cbits - kdrop);
     const uint32_t sshift = sbits > lkeep ? sbits - lkeep : 0u;
-    uint32_t bin[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-        const uint32_t sc = lkeep ? (uint32_t)(sub_of(x[e]) >> sshift) : 0u;
-        bin[e] = (uint32_t)e * NT + t < cnt ? ((code_of(x[e]) << lkeep) | sc) : 0u;
-    }
-#pragma unroll
-    for (int e = 0; e < E; ++e)
-        if ((uint32_t)e * NT + t < cnt) atomicAdd(&bins[bin[e]], 1u);
+    bool prop = false;
+    const float ratio = (float)nb / (float)cnt;
+    auto first = [&](uint32_t cc) {
+        if (cc >= ncodes) return nb;
+        const uint32_t f = (uint32_t)((float)hc[cc] * ratio);
+        return f < nb - 1u ? f : nb - 1u;
+    };
+    auto bin_of = [&](uint64_t w) {
+        if (!prop) {
+            const uint32_t sc = lkeep ? (uint32_t)(sub_of(w) >> sshift) : 0u;
+            return (code_of(w) << lkeep) | sc;
+        }
+        const uint32_t cc = code_of(w);
+        const uint32_t f0 = first(cc), nsub = first(cc + 1u) - f0;
+        const uint32_t off = sbits ? (uint32_t)((sub_of(w) * nsub) >> sbits) : 0u;
+        return f0 + off;
+    };
+    for (uint32_t i = t; i < cnt; i += NT) atomicAdd(&bins[bin_of(a[i])], 1u);
     lds_sync();
-    uint32_t big = scan_counts<NT>(bins, nb, sh, rb);
+    uint32_t big = scan_counts<NT, NB>(bins, nb, sh, rb);
     if (big > kMaxBin) {
-        // runs of bins in proportion to the codes' sizes; the code histogram
-        // sits in the second buffer (free until the scatter)
-        uint32_t* hc = (uint32_t*)b;
+        // runs of bins in proportion to the codes' sizes
         for (uint32_t i = t; i <= ncodes; i += NT) hc[i] = 0u;
         lds_sync();
-#pragma unroll
-        for (int e = 0; e < E; ++e)
-            if ((uint32_t)e * NT + t < cnt) atomicAdd(&hc[code_of(x[e])], 1u);
+        for (uint32_t i = t; i < cnt; i += NT) atomicAdd(&hc[code_of(a[i])], 1u);
         lds_sync();
-        scan_counts<NT>(hc, ncodes, sh, rb);
-        const float ratio = (float)nb / (float)cnt;
-        auto first = [&](uint32_t c) {
-            if (c >= ncodes) return nb;
-            const uint32_t f = (uint32_t)((float)hc[c] * ratio);
-            return f < nb - 1u ? f : nb - 1u;
-        };
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-            const uint32_t c = code_of(x[e]);
-            const uint32_t f0 = first(c), nsub = first(c + 1u) - f0;
-            const uint32_t off = sbits ? (uint32_t)((sub_of(x[e]) * nsub) >> sbits) : 0u;
-            bin[e] = (uint32_t)e * NT + t < cnt ? f0 + off : 0u;
-        }
+        scan_counts<NT, NB>(hc, ncodes, sh, rb);
+        prop = true;
         for (uint32_t i = t; i <= nb; i += NT) bins[i] = 0u;
-        lds_sync();  // the code starts are read before the scatter reuses the buffer
-#pragma unroll
-        for (int e = 0; e < E; ++e)
-            if ((uint32_t)e * NT + t < cnt) atomicAdd(&bins[bin[e]], 1u);
         lds_sync();
-        big = scan_counts<NT>(bins, nb, sh, rb);
+        for (uint32_t i = t; i < cnt; i += NT) atomicAdd(&bins[bin_of(a[i])], 1u);
+        lds_sync();
+        big = scan_counts<NT, NB>(bins, nb, sh, rb);
         if (big > kMaxBin) return false;
     }
-    // scatter, with each word's bin beside it (in the first buffer, whose
-    // words are all in registers now); afterwards bins[i] is the end of bin i
-    uint32_t* binp = (uint32_t*)a;
-    uint32_t pos[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e)
-        pos[e] = (uint32_t)e * NT + t < cnt ? atomicAdd(&bins[bin[e]], 1u) : 0u;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-        if ((uint32_t)e * NT + t < cnt) {
-            b[pos[e]] = x[e];
-            binp[pos[e]] = bin[e];
-        }
-    }
+    // scatter the positions; afterwards bins[i] is the end of bin i
+    for (uint32_t i = t; i < cnt; i += NT) pos[atomicAdd(&bins[bin_of(a[i])], 1u)] = i;
     lds_sync();
     // ranks, by position in the binned order: the lanes of a wave mostly
     // share a bin, so their scans take the same number of steps
     for (uint32_t p = t; p < cnt; p += NT) {
-        const uint64_t w = b[p];
-        const uint32_t bi = binp[p];
+        const uint64_t w = a[pos[p]];
+        const uint32_t bi = bin_of(w);
         const uint32_t s0 = bi ? bins[bi - 1] : 0u, e0 = bins[bi];
         uint32_t r = s0;
-        if (e0 - s0 > 1) {
-            // eight words per step from 16-byte reads; words outside the bin
-            // (up to 7 past its end, still inside the LDS allocation) do not count
-            for (uint32_t q = s0 & ~1u; q < e0; q += 8) {
-                const uint4* v = (const uint4*)(b + q);
-                const uint4 v0 = v[0], v1 = v[1], v2 = v[2], v3 = v[3];
-                const uint64_t y[8] = {((uint64_t)v0.y << 32) | v0.x, ((uint64_t)v0.w << 32) | v0.z,
-                                       ((uint64_t)v1.y << 32) | v1.x, ((uint64_t)v1.w << 32) | v1.z,
-                                       ((uint64_t)v2.y << 32) | v2.x, ((uint64_t)v2.w << 32) | v2.z,
-                                       ((uint64_t)v3.y << 32) | v3.x, ((uint64_t)v3.w << 32) | v3.z};
-#pragma unroll
-                for (int u = 0; u < 8; ++u) r += (q + u >= s0 && q + u < e0 && y[u] > w) ? 1u : 0u;
-            }
-        }
-        ro.put(r, cand_idx(w));
+        for (uint32_t q = s0; q < e0; ++q) r += a[pos[q]] > w ? 1u : 0u;
+        ro.put(r, cand_idx(w), p);
     }
     lds_sync();
     return true;
 }
 
-// Largest kept set one sort handles; larger ones are sorted in windows.
-template <int NT>
-QRITA_DEV uint32_t sort_cap(const Params& P) {
-    return min((uint32_t)P.tail_alloc, 32u * NT);
-}
-
-// Rank order of the cnt <= sort_cap<NT>() candidates in a[0 .. cnt): a
-// handful by ranking, more by the bucket sort, and sets with heavy ties by
-// the bitonic sort. The LDS past the candidates (the index store and the bin
-// counts) is free by now. Kept out of line: the sort's registers are then
-// allocated on their own instead of on top of everything live at its call
-// sites.
-template <int NT>
-__device__ __attribute__((always_inline)) void sort_emit(uint32_t cnt, RankOut ro, uint32_t alloc, Shared& sh, int rb) {
-    cnt = uni(cnt);
-    alloc = uni(alloc);
-    uint64_t* a = lds_cands();
+// Rank order of the cnt <= CSORT words at the start of the sort region: a
+// handful by ranking, more by the bucket sort, sets it cannot split by the
+// bitonic sort. RankOut::kept (when used) is the sort's position array.
+template <class T>
+QRITA_DEV void sort_words(uint32_t cnt, RankOut ro, Shared& sh, int& rb) {
+    constexpr int NT = T::NT;
+    uint64_t* a = (uint64_t*)(dyn_lds() + T::SA_OFF);
+    uint32_t* pos = (uint32_t*)(dyn_lds() + T::SB_OFF);
+    uint32_t* bins = (uint32_t*)(dyn_lds() + T::BINS_OFF);
+    uint32_t* hc = (uint32_t*)(dyn_lds() + T::HC_OFF);
+    cnt = min(uni(cnt), (uint32_t)T::CSORT);  // more only for inputs outside the contract (NaN logits)
+    if (cnt == 0) return;
     if (cnt <= (uint32_t)NT) {
-        rank_sort<NT>(a, cnt, ro, sh);
+        rank_sort<NT>(a, cnt, ro, bins);
         return;
     }
-    uint64_t* b = a + alloc;
-    uint32_t* bins = (uint32_t*)(a + 2 * alloc);
-    bool done;
-    if (cnt <= 2u * NT)
-        done = bucket_sort<NT, 2>(a, cnt, ro, b, bins, sh, rb);
-    else if (cnt <= 4u * NT)
-        done = bucket_sort<NT, 4>(a, cnt, ro, b, bins, sh, rb);
-    else if (cnt <= 8u * NT)
-        done = bucket_sort<NT, 8>(a, cnt, ro, b, bins, sh, rb);
-    else if (cnt <= 16u * NT)
-        done = bucket_sort<NT, 16>(a, cnt, ro, b, bins, sh, rb);
-    else
-        done = bucket_sort<NT, 32>(a, cnt, ro, b, bins, sh, rb);
-    if (done) return;
-    uint32_t np = next_pow2(cnt);
-    if (np < 2u * NT) np = 2u * NT;
+    if (bucket_sort<NT, T::NB>(a, cnt, ro, pos, bins, hc, sh, rb)) return;
+    const uint32_t np = next_pow2(cnt);
     for (uint32_t i = cnt + threadIdx.x; i < np; i += NT) a[i] = 0ull;
     lds_sync();
-    switch (np / NT) {
-        case 2: bitonic_sort<NT, 2>(a, ro, cnt); break;
-        case 4: bitonic_sort<NT, 4>(a, ro, cnt); break;
-        case 8: bitonic_sort<NT, 8>(a, ro, cnt); break;
-        case 16: bitonic_sort<NT, 16>(a, ro, cnt); break;
-        default: bitonic_sort<NT, 32>(a, ro, cnt); break;
-    }
+    bitonic_lds<NT>(a, np, cnt, ro);
+}
+
+// ---------------------------------------------------------------------------
+// Gathering words from a source into the sort region, and the mask.
+// ---------------------------------------------------------------------------
+
+// Words c with lo_w <= c < hi_w from the source (with indices) into
+// a[0 .. ), reserved per wave in LDS; returns the count (uniform). At most
+// cap are written.
+template <int NT, class L>
+QRITA_DEV uint32_t gather_words(const L& lsrc, uint64_t* a, uint32_t cap, uint64_t lo_w, uint64_t hi_w, Shared& sh) {
+    block_sync<NT>();
+    if (threadIdx.x == 0) sh.gather_n = 0;
     lds_sync();
+    const uint32_t lane = tid_here() & (kWave - 1);
+    lsrc.visit([&](uint32_t key, uint32_t low) {
+        const uint64_t w = ((uint64_t)key << 32) | low;
+        const bool take = key != 0 && w >= lo_w && w < hi_w;
+        const uint64_t b = __ballot(take);
+        if (b) {
+            uint32_t r0 = 0;
+            if (lane == 0) r0 = atomicAdd(&sh.gather_n, (uint32_t)__popcll(b));
+            const uint32_t pos = readlane(r0, 0) + lanes_below(b);
+            if (take && pos < cap) a[pos] = w;
+        }
+    });
+    lds_sync();
+    return uni(sh.gather_n);
 }
 
-// Mask bytes of the kept set {c >= B} (when mask is set) and, when cnt > 0,
-// the indices of the cnt candidates c >= Bo (Bo >= B) in rank order at
-// out_idx[row][off ...]: one visit counts them per wave, a second writes the
-// mask and gathers them into LDS at prefix positions (no atomics).
-template <int NT, class S>
-QRITA_DEV void emit_out(const Params& P, int64_t row, const S& src, uint64_t B, bool mask, uint64_t Bo,
-                        uint32_t cnt, uint32_t off, Shared& sh, int& rb) {
-    uint8_t* mrow = P.mask + row * (int64_t)P.vocab;
-    const uint32_t bk = cand_key(B), bl = cand_low(B);
-    const uint32_t ok = cand_key(Bo), ol = cand_low(Bo);
-    auto keeps = [&](uint32_t key, uint32_t lw) { return key != 0 && (key > bk || (key == bk && lw >= bl)); };
-    auto takes = [&](uint32_t key, uint32_t lw) { return key != 0 && (key > ok || (key == ok && lw >= ol)); };
-    if (cnt == 0) {
-        if (mask)
-            src.template visit<true, false>([&](uint32_t key, uint32_t lw, float, int) {
-                if (keeps(key, lw)) mrow[~lw] = 1;
-            });
-        return;
-    }
-    uint64_t* a = lds_cands();
-    const uint32_t cap = (uint32_t)P.tail_alloc;
-    uint32_t run = 0;
-    if constexpr (S::kRegs) {
-        uint32_t c = 0;
-        src.template visit<true, false>(
-            [&](uint32_t key, uint32_t lw, float, int) { c += (uint32_t)__popcll(__ballot(takes(key, lw))); });
-        uint32_t total = 0;
-        run = wave_prefix<NT>(c, total, sh, rb);
-    } else {
-        block_sync<NT>();
-        if (threadIdx.x == 0) sh.gather_n = 0;
-    }
-    block_sync<NT>();  // the masses in the gather buffer are no longer read
-    const uint32_t lane = tid_here() & (kWave - 1);
-    src.template visit<true, false>([&](uint32_t key, uint32_t lw, float, int) {
-        if (mask && keeps(key, lw)) mrow[~lw] = 1;
-        const bool take = takes(key, lw);
-        const uint64_t b = __ballot(take);
-        uint32_t base = run;
-        if constexpr (!S::kRegs) {
-            if (b) {
-                uint32_t r0 = 0;
-                if (lane == 0) r0 = atomicAdd(&sh.gather_n, (uint32_t)__popcll(b));
-                base = readlane(r0, 0);
-            }
+// Write the mask row from an LDS bitmap of the kept indices (whole row,
+// 16-byte stores; one byte per logit, 1 = kept).
+template <int NT>
+QRITA_DEV void write_mask_row(uint8_t* mrow, const uint32_t* bm, uint32_t V) {
+    const uint32_t t = threadIdx.x;
+    const uint32_t head = (uint32_t)((16u - ((uintptr_t)mrow & 15u)) & 15u);
+    const uint32_t h = head < V ? head : V;
+    for (uint32_t i = t; i < h; i += NT) mrow[i] = (uint8_t)((bm[i >> 5] >> (i & 31u)) & 1u);
+    const uint32_t nv = (V - h) / 16u;
+    for (uint32_t v = t; v < nv; v += NT) {
+        const uint32_t i = h + v * 16u;
+        // the 16 bits of logits i .. i+15 (i need not be a multiple of 32;
+        // the word after the last one lies inside the bitmap's region)
+        const uint64_t two = ((uint64_t)bm[(i >> 5) + 1] << 32) | bm[i >> 5];
+        const uint32_t bits = (uint32_t)(two >> (i & 31u)) & 0xFFFFu;
+        uint32_t wd[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t nib = (bits >> (4 * q)) & 15u;
+            wd[q] = (nib & 1u) | ((nib & 2u) << 7) | ((nib & 4u) << 14) | ((nib & 8u) << 21);
         }
-        const uint32_t pos = base + lanes_below(b);
-        if (take && pos < cap) a[pos] = ((uint64_t)key << 32) | lw;
-        if constexpr (S::kRegs) run += (uint32_t)__popcll(b);
-    });
-    block_sync<NT>();
-    sort_emit<NT>(cnt, RankOut{P.out_idx + row * (int64_t)P.idx_cap + off, cnt, nullptr, 0u}, (uint32_t)P.tail_alloc,
-                  sh, rb);
+        const u32x4_t wv = {wd[0], wd[1], wd[2], wd[3]};
+        __builtin_nontemporal_store(wv, (u32x4_t*)(mrow + i));
+    }
+    for (uint32_t i = h + nv * 16u + t; i < V; i += NT) mrow[i] = (uint8_t)((bm[i >> 5] >> (i & 31u)) & 1u);
 }
 
-// The candidates c >= lo_w (every candidate at or above the final boundary
-// value, so the kept set and its boundary duplicates) gathered into LDS and
-// sorted; the sort then writes the mask bytes of ranks < lmask and the
-// indices of ranks < lout directly, so the boundary duplicates are resolved
-// by their rank order (lower index first) without a separate search. The
-// caller guarantees at most sort_cap<NT>() such candidates.
-template <int NT, class S>
-QRITA_DEV void emit_ranked(const Params& P, int64_t row, const S& src, uint64_t lo_w, uint32_t lmask,
-                           uint32_t lout, Shared& sh, int& rb) {
-    const uint32_t lk = cand_key(lo_w), ll = cand_low(lo_w);
-    auto takes = [&](uint32_t key, uint32_t lw) { return key != 0 && (key > lk || (key == lk && lw >= ll)); };
-    uint64_t* a = lds_cands();
-    const uint32_t cap = sort_cap<NT>(P);
-    uint32_t run = 0, cnt = 0;
-    if constexpr (S::kRegs) {
-        uint32_t c = 0;
-        src.template visit<true, false>(
-            [&](uint32_t key, uint32_t lw, float, int) { c += (uint32_t)__popcll(__ballot(takes(key, lw))); });
-        run = wave_prefix<NT>(c, cnt, sh, rb);
-    } else {
-        block_sync<NT>();
-        if (threadIdx.x == 0) sh.gather_n = 0;
-    }
-    block_sync<NT>();  // the masses in the gather buffer are no longer read
-    const uint32_t lane = tid_here() & (kWave - 1);
-    src.template visit<true, false>([&](uint32_t key, uint32_t lw, float, int) {
-        const bool take = takes(key, lw);
-        const uint64_t b = __ballot(take);
-        uint32_t base = run;
-        if constexpr (!S::kRegs) {
-            if (b) {
-                uint32_t r0 = 0;
-                if (lane == 0) r0 = atomicAdd(&sh.gather_n, (uint32_t)__popcll(b));
-                base = readlane(r0, 0);
-            }
-        }
-        const uint32_t pos = base + lanes_below(b);
-        if (take && pos < cap) a[pos] = ((uint64_t)key << 32) | lw;
-        if constexpr (S::kRegs) run += (uint32_t)__popcll(b);
-    });
-    block_sync<NT>();
-    if constexpr (!S::kRegs) cnt = uni(sh.gather_n);
-    cnt = min(cnt, cap);
-    RankOut ro{P.out_idx ? P.out_idx + row * (int64_t)P.idx_cap : nullptr, lout,
-               P.mask ? P.mask + row * (int64_t)P.vocab : nullptr, lmask};
-    sort_emit<NT>(cnt, ro, (uint32_t)P.tail_alloc, sh, rb);
+// A whole mask row of ones (keep-all rows).
+template <int NT>
+QRITA_DEV void fill_mask_row(uint8_t* mrow, uint32_t V, uint8_t val) {
+    const uint32_t t = threadIdx.x;
+    const uint32_t head = (uint32_t)((16u - ((uintptr_t)mrow & 15u)) & 15u);
+    const uint32_t h = head < V ? head : V;
+    for (uint32_t i = t; i < h; i += NT) mrow[i] = val;
+    const uint32_t nv = (V - h) / 16u;
+    const uint32_t w = 0x01010101u * val;
+    const u32x4_t wv = {w, w, w, w};
+    for (uint32_t v = t; v < nv; v += NT) __builtin_nontemporal_store(wv, (u32x4_t*)(mrow + h + v * 16u));
+    for (uint32_t i = h + nv * 16u + t; i < V; i += NT) mrow[i] = val;
+}
+
+QRITA_DEV void clear_words(uint32_t* p, uint32_t n, uint32_t NT) {
+    for (uint32_t i = threadIdx.x; i < n; i += NT) p[i] = 0u;
 }
 
 struct TailDiag {
@@ -1228,64 +1081,180 @@ struct TailDiag {
     int32_t iters;
 };
 
-// Rank windows of sort_cap entries of the kept set {c >= B} (Lout of its
-// `setn` candidates, keys in (lo_b, kmax]), each window found by its own
-// boundary.
-template <int NT, class S>
-QRITA_DEV void emit_windows_src(const Params& P, int64_t row, const S& src, uint64_t B, uint32_t Lout,
-                                uint32_t setn, int64_t lo_b, uint32_t kmax, Shared& sh, int& rb, TailDiag& dg) {
-    const uint32_t cap = sort_cap<NT>(P);
-    uint64_t prev = ~0ull;
-    for (uint32_t done = 0; done < Lout;) {
-        const uint32_t cnt = min(cap, Lout - done);
-        const uint64_t Bn = select_boundary<NT>(src, done + cnt, setn, lo_b, kmax, (uint32_t)P.vocab,
-                                                P.pivot_mode, B, sh, rb, dg.iters);
-        // the window: Bn <= c < prev
-        S w = src;
-        w.restrict_to(Bn);
-        const uint32_t ok = cand_key(prev), ol = cand_low(prev);
-        uint64_t* a = lds_cands();
+// Boundary word B of "the `need` lowest-index candidates with key v, plus
+// everything above v" (so the kept set is {c >= B}). A small tie group is
+// ranked directly in LDS; a large one by a quaternary search over the tied
+// candidates' indices.
+template <class T, class L>
+QRITA_DEV uint64_t tie_boundary(const L& lsrc, uint32_t v, uint32_t need, uint32_t N, uint32_t V, int mode,
+                                Shared& sh, int& rb, int& iters) {
+    constexpr int NT = T::NT;
+    uint64_t b = (uint64_t)v << 32;
+    if (need >= N) return b;
+    if (N <= kTieDirect) {
         const uint32_t lane = tid_here() & (kWave - 1);
         block_sync<NT>();
         if (threadIdx.x == 0) sh.gather_n = 0;
-        block_sync<NT>();
-        w.template visit<true, false>([&](uint32_t key, uint32_t lw, float, int) {
-            const bool take = key != 0 && (key < ok || (key == ok && lw < ol));
-            const uint64_t b = __ballot(take);
-            if (b) {
-                uint32_t r0 = 0;
-                if (lane == 0) r0 = atomicAdd(&sh.gather_n, (uint32_t)__popcll(b));
-                const uint32_t pos = readlane(r0, 0) + lanes_below(b);
-                if (take && pos < cap) a[pos] = ((uint64_t)key << 32) | lw;
+        // zeros after the ties (below every complemented index) round the
+        // list up to whole uint4 reads
+        if (threadIdx.x < 4u && N + threadIdx.x < (uint32_t)kTieDirect + 4u) sh.ties[N + threadIdx.x] = 0u;
+        lds_sync();
+        lsrc.visit([&](uint32_t key, uint32_t low) {
+            const bool tie = key == v;
+            const uint64_t bb = __ballot(tie);
+            if (bb) {
+                uint32_t base = 0;
+                if (lane == 0) base = atomicAdd(&sh.gather_n, (uint32_t)__popcll(bb));
+                base = readlane(base, 0);
+                const uint32_t pos = base + lanes_below(bb);
+                if (tie && pos < (uint32_t)kTieDirect) sh.ties[pos] = low;
             }
         });
-        block_sync<NT>();
-        sort_emit<NT>(cnt, RankOut{P.out_idx + row * (int64_t)P.idx_cap + done, cnt, nullptr, 0u},
-                      (uint32_t)P.tail_alloc, sh, rb);
+        lds_sync();
+        // the tie whose complemented index has exactly need - 1 larger ones
+        const uint32_t n4 = (N + 3u) / 4u;
+        for (uint32_t i = threadIdx.x; i < N; i += NT) {
+            const uint32_t x = sh.ties[i];
+            uint32_t above = 0;
+            for (uint32_t j = 0; j < n4; ++j) {
+                const uint4 q = *(const uint4*)&sh.ties[4 * j];
+                above += (q.x > x ? 1u : 0u) + (q.y > x ? 1u : 0u) + (q.z > x ? 1u : 0u) + (q.w > x ? 1u : 0u);
+            }
+            if (above == need - 1) sh.u32[6] = x;
+        }
+        lds_sync();
+        return b | uni(sh.u32[6]);
+    }
+    // complemented indices of a row lie in [~(V - 1), 0xFFFFFFFF]
+    Ctx<T, L> c{lsrc, wave_segment<T>(), (uint32_t)T::SEG, mode == 2 ? 2 : 0, &sh, rb, 0};
+    const int64_t lo = (int64_t)(0xFFFFFFFFu - (V - 1u)) - 1;
+    const CountOut t = search_count<NT, 1>(c, v, need, lo, N, (int64_t)0xFFFFFFFFu, 0u);
+    rb = c.rb;
+    iters += c.iters;
+    return b | t.v;
+}
+
+// Where the outputs of a row go.
+struct RowOut {
+    int32_t* idx;    // out_idx row or null
+    uint32_t idx_cap;
+    uint8_t* mrow;   // mask row or null (keep-all rows: filled elsewhere)
+    bool bitmap;     // mask written whole from an LDS bitmap
+    uint32_t V;
+};
+
+// Mask of the kept set {c >= B} from a pass over the candidates: bitmap, or
+// bytes scattered into the row that pass 1 zero-filled.
+template <class T, class L>
+QRITA_DEV void mask_from_boundary(const L& lsrc, uint64_t B, const RowOut& o) {
+    constexpr int NT = T::NT;
+    if (!o.mrow) return;
+    if (o.bitmap) {
+        uint32_t* bm = (uint32_t*)(dyn_lds() + T::SA_OFF);
+        lds_sync();
+        clear_words(bm, (o.V + 31u) / 32u, NT);
+        lds_sync();
+        lsrc.visit([&](uint32_t key, uint32_t low) {
+            const uint64_t w = ((uint64_t)key << 32) | low;
+            if (key != 0 && w >= B) atomicOr(&bm[(~low) >> 5], 1u << ((~low) & 31u));
+        });
+        lds_sync();
+        write_mask_row<NT>(o.mrow, bm, o.V);
+    } else {
+        lsrc.visit([&](uint32_t key, uint32_t low) {
+            const uint64_t w = ((uint64_t)key << 32) | low;
+            if (key != 0 && w >= B) o.mrow[~low] = 1;
+        });
+    }
+}
+
+// Mask from the kept indices the sort recorded in its position array.
+template <class T>
+QRITA_DEV void mask_from_sorted(uint32_t cnt, const RowOut& o) {
+    constexpr int NT = T::NT;
+    if (!o.mrow || !o.bitmap) return;
+    uint32_t* bm = (uint32_t*)(dyn_lds() + T::SA_OFF);
+    const uint32_t* kept = (const uint32_t*)(dyn_lds() + T::SR_OFF);
+    lds_sync();
+    clear_words(bm, (o.V + 31u) / 32u, NT);
+    lds_sync();
+    for (uint32_t p = threadIdx.x; p < cnt; p += NT) {
+        const uint32_t i = kept[p];
+        if (i != 0xFFFFFFFFu) atomicOr(&bm[i >> 5], 1u << (i & 31u));
+    }
+    lds_sync();
+    write_mask_row<NT>(o.mrow, bm, o.V);
+}
+
+// The outputs (a7) of a row whose kept set is {> vf} and the needf
+// lowest-index of its Nf duplicates at vf (L = ngt + needf tokens), with
+// `all` for rows that keep everything. The first Lout = min(L, idx_cap)
+// ranks go to the index output. When every candidate at or above the value
+// that bounds the index output fits one sort, the sort's rank order resolves
+// the duplicates and writes the outputs; otherwise the duplicates are
+// resolved by tie_boundary and the indices sorted in windows.
+template <class T, class C, class L>
+QRITA_DEV void emit_row(C& c, const L& lsrc, const RowOut& o, bool all, uint32_t vf, uint32_t ngt, uint32_t needf,
+                        uint32_t Nf, uint32_t L_, int64_t key_lo, uint32_t n, uint32_t kmax, TailDiag& dg) {
+    constexpr int NT = T::NT;
+    Shared& sh = *c.sh;
+    const uint32_t Lout = o.idx ? (L_ < o.idx_cap ? L_ : o.idx_cap) : 0u;
+    const bool mask = o.mrow != nullptr && !all;
+    if (!mask && Lout == 0) return;
+    // the boundary of the index output's last rank
+    uint32_t vo = vf, ngo = ngt, needo = needf, No = Nf;
+    if (Lout > 0 && (all || Lout < L_)) {
+        // every candidate >= vf counts above vf - 1, the unkept duplicates too
+        const CountOut r = search_count<NT, 0>(c, 0u, Lout, all ? key_lo : (int64_t)vf - 1, all ? n : ngt + Nf,
+                                               (int64_t)kmax, 0u);
+        vo = r.v;
+        ngo = r.n_gt;
+        needo = Lout - r.n_gt;
+        No = r.N;
+    }
+    uint64_t* a = (uint64_t*)(dyn_lds() + T::SA_OFF);
+    const uint32_t Gi = Lout > 0 ? ngo + No : ngt + Nf;
+    const bool same = Lout == 0 || (!all && Lout == L_);  // the index boundary is the kept set's boundary
+    if (Gi <= (uint32_t)T::CSORT && same) {
+        // one sort over every candidate at or above the boundary value
+        const uint32_t cnt = gather_words<NT>(lsrc, a, T::CSORT, (uint64_t)(Lout > 0 ? vo : vf) << 32, ~0ull, sh);
+        RankOut ro{o.idx, Lout, (mask && !o.bitmap) ? o.mrow : nullptr,
+                   (mask && o.bitmap) ? (uint32_t*)(dyn_lds() + T::SR_OFF) : nullptr, mask ? L_ : 0u};
+        sort_words<T>(cnt, ro, sh, c.rb);
+        if (mask) mask_from_sorted<T>(min(cnt, (uint32_t)T::CSORT), o);
+        return;
+    }
+    // the kept set's boundary word, for the mask
+    if (mask) {
+        const uint64_t B = tie_boundary<T>(lsrc, vf, needf, Nf, o.V, c.mode, sh, c.rb, dg.iters);
+        mask_from_boundary<T>(lsrc, B, o);
+    }
+    if (Lout == 0) return;
+    if (Gi <= (uint32_t)T::CSORT) {
+        const uint32_t cnt = gather_words<NT>(lsrc, a, T::CSORT, (uint64_t)vo << 32, ~0ull, sh);
+        sort_words<T>(cnt, RankOut{o.idx, Lout, nullptr, nullptr, 0u}, sh, c.rb);
+        return;
+    }
+    // windows of CSORT ranks, each bounded by its own boundary word
+    const uint64_t Bo = tie_boundary<T>(lsrc, vo, needo, No, o.V, c.mode, sh, c.rb, dg.iters);
+    uint64_t prev = ~0ull;
+    for (uint32_t done = 0; done < Lout;) {
+        const uint32_t cnt = min((uint32_t)T::CSORT, Lout - done);
+        uint64_t Bn = Bo;
+        if (done + cnt < Lout) {
+            const CountOut r = search_count<NT, 0>(c, 0u, done + cnt, (int64_t)vo - 1, ngo + No, (int64_t)kmax, 0u);
+            Bn = tie_boundary<T>(lsrc, r.v, done + cnt - r.n_gt, r.N, o.V, c.mode, sh, c.rb, dg.iters);
+        }
+        const uint32_t got = gather_words<NT>(lsrc, a, T::CSORT, Bn, prev, sh);
+        sort_words<T>(got, RankOut{o.idx + done, cnt, nullptr, nullptr, 0u}, sh, c.rb);
         prev = Bn;
         done += cnt;
     }
 }
 
-// The same over the row's list in memory (the n candidates the register set
-// was loaded from), for kept sets larger than one sort. Returns the
-// iterations spent in iters and the record-buffer parity in n_t. (The
-// out-of-line functions take the parameters by value: a reference would make
-// the kernel keep its parameters in scratch memory and read them per lane.)
-template <int NT>
-__device__ __attribute__((noinline)) TailDiag emit_windows(const Params P, int64_t row, uint32_t n, uint64_t B,
-                                                           uint32_t Lout, uint32_t setn, int64_t lo_b,
-                                                           uint32_t kmax, Shared& sh, int rb) {
-    MemSrc<NT, false, false> src{P.glist + row * (int64_t)P.list_stride, nullptr, n, B};
-    TailDiag dg{0, 0};
-    emit_windows_src<NT>(P, row, src, B, Lout, setn, lo_b, kmax, sh, rb, dg);
-    dg.n_t = rb;
-    return dg;
-}
-
-// Steps a4-a7 on one candidate source holding n candidates (list entries
-// 0 .. n-1 of the row), all with keys in (key_lo, kmax]; rest_fx is the
-// fixed-point mass, relative to rest_ref, of the logits left out of the
+// Steps a4-a7 on one candidate source holding n candidates, all with keys in
+// (key_lo, kmax]; lsrc is the same candidates with their indices. rest_fx is
+// the fixed-point mass, relative to rest_ref, of the logits left out of the
 // source (top-p-only rows). Returns false when the source does not contain
 // the answer (a truncation miss); then nothing has been written.
 //
@@ -1295,16 +1264,17 @@ __device__ __attribute__((noinline)) TailDiag emit_windows(const Params P, int64
 // of those at v (their masses are equal, so which ones does not matter for
 // the mass); the final boundary value and count then pick the lowest
 // indices among its duplicates.
-template <int NT, class S>
-QRITA_DEV bool finish_row(const Params& P, int64_t row, const RowMode& md, S& src, uint32_t n, int64_t key_lo,
-                          uint32_t kmax, uint64_t rest_fx, float rest_ref, float t_gauss, Shared& sh, int& rb,
-                          TailDiag& dg) {
+template <class T, class S, class L>
+QRITA_DEV bool finish_row(const Params& P, int64_t row, const RowMode& md, const S& src, const L& lsrc, uint32_t n,
+                          int64_t key_lo, uint32_t kmax, uint64_t rest_fx, float rest_ref, float t_gauss, Shared& sh,
+                          int& rb, TailDiag& dg) {
+    constexpr int NT = T::NT;
     const uint32_t V = (uint32_t)P.vocab;
     if (P.diag) {  // #{z >= Gaussian t} among the candidates, for diagnostics
         const uint32_t key_t = f32_key(__float_as_uint(t_gauss));
-        uint32_t c = 0;
-        src.template visit<false, false>([&](uint32_t key, uint32_t, float, int) { c += key >= key_t ? 1u : 0u; });
-        dg.n_t = (int32_t)comb_sum32<NT>(c, sh, rb);
+        uint32_t cc = 0;
+        src.visit([&](uint32_t key, uint32_t) { cc += key >= key_t ? 1u : 0u; });
+        dg.n_t = (int32_t)comb_sum32<NT>(cc, sh, rb);
     }
     bool topk = md.topk, topp = md.topp;
     uint32_t K = md.K;
@@ -1317,13 +1287,13 @@ QRITA_DEV bool finish_row(const Params& P, int64_t row, const RowMode& md, S& sr
         topk = true;
         K = 1;
     }
+    Ctx<T, S> c{src, wave_segment<T>(), (uint32_t)T::SEG, P.pivot_mode, &sh, rb, 0};
     // kept set: {> vf} and the needf lowest-index of the Nf candidates at vf
     bool all = true;
     uint32_t vf = 0, ngt = 0, needf = 0, Nf = 0;
     // a5: top-k
     if (topk) {
-        const CountOut r = qsearch_count<NT, 0>(src, 0u, K, key_lo, n, (int64_t)kmax, 0u, P.pivot_mode, sh, rb,
-                                                dg.iters);
+        const CountOut r = search_count<NT, 0>(c, 0u, K, key_lo, n, (int64_t)kmax, 0u);
         all = false;
         vf = r.v;
         ngt = r.n_gt;
@@ -1335,10 +1305,6 @@ QRITA_DEV bool finish_row(const Params& P, int64_t row, const RowMode& md, S& sr
         MassSet ms{md.p, 0.0, !topk, 0u, 0u};
         int64_t lo = key_lo;
         if (topk) {
-            src.restrict_ge(vf);
-            if constexpr (S::kRegs) {
-                if (S::chunks_for(ngt + Nf) < S::chunks_for(src.nslots)) src.compact(sh, rb);
-            }
             ms.vx = vf;
             ms.dN = Nf - needf;
             lo = (int64_t)vf - 1;
@@ -1348,7 +1314,11 @@ QRITA_DEV bool finish_row(const Params& P, int64_t row, const RowMode& md, S& sr
         }
         MassOut mo;
         uint64_t Tq = 0;
-        if (!qsearch_mass<NT>(src, ms, m, lo, (int64_t)kmax, P.pivot_mode, sh, rb, dg.iters, mo, Tq)) return false;
+        if (!search_mass<NT>(c, ms, m, lo, (int64_t)kmax, mo, Tq)) {
+            rb = c.rb;
+            dg.iters += c.iters;
+            return false;
+        }
         // smallest number of duplicates at v that reaches T: ceil((Tq - M_gt) / e)
         // (M_gt < Tq <= M_gt + N e), clamped to [1, N]
         const uint64_t e = mass_fx(mo.v, m);
@@ -1367,76 +1337,38 @@ QRITA_DEV bool finish_row(const Params& P, int64_t row, const RowMode& md, S& sr
         ngt = mo.n_gt;
         needf = need;
     }
-    const uint32_t L = all ? V : ngt + needf;
-    const bool mask = P.mask && !md.keep_all;
-    // a7: when every candidate at or above the final boundary value fits one
-    // sort, the sort's rank order resolves the duplicates and writes the
-    // outputs
-    {
-        const bool want_idx = P.out_idx && P.idx_cap > 0;
-        const uint32_t Lout = want_idx ? (L < (uint32_t)P.idx_cap ? L : (uint32_t)P.idx_cap) : 0u;
-        const uint32_t Gn = all ? n : ngt + Nf;
-        if ((mask || Lout > 0) && Gn <= sort_cap<NT>(P)) {
-            emit_ranked<NT>(P, row, src, all ? 0ull : (uint64_t)vf << 32, mask ? L : 0u, Lout, sh, rb);
-            if (P.out_count && threadIdx.x == 0) P.out_count[row] = (int32_t)L;
-            return true;
-        }
-    }
-    // a7: duplicate resolution at the final boundary value
-    const uint64_t B = all ? 0ull : tie_boundary<NT>(src, vf, needf, Nf, V, 0ull, sh, rb, dg.iters);
-    // a7: mask (pass 1 zero-filled the row; keep-all rows were filled there)
-    // and the indices in rank order
-    if (P.out_idx && P.idx_cap > 0) {
-        const uint32_t Lout = L < (uint32_t)P.idx_cap ? L : (uint32_t)P.idx_cap;
-        const int64_t lo_b = B ? (int64_t)cand_key(B) - 1 : key_lo;
-        const uint32_t setn = all ? n : L;
-        if (Lout <= sort_cap<NT>(P)) {
-            uint64_t Bo = B;
-            if (Lout < L) {
-                if (mask) emit_out<NT>(P, row, src, B, true, B, 0u, 0u, sh, rb);
-                src.restrict_to(B);
-                Bo = select_boundary<NT>(src, Lout, setn, lo_b, kmax, V, P.pivot_mode, B, sh, rb, dg.iters);
-                emit_out<NT>(P, row, src, B, false, Bo, Lout, 0u, sh, rb);
-            } else {
-                emit_out<NT>(P, row, src, B, mask, Bo, Lout, 0u, sh, rb);
-            }
-        } else {
-            if (mask) emit_out<NT>(P, row, src, B, true, B, 0u, 0u, sh, rb);
-            if constexpr (S::kRegs) {
-                // a kept set larger than one sort: windows over the row list
-                const TailDiag w = emit_windows<NT>(P, row, n, B, Lout, setn, lo_b, kmax, sh, rb);
-                dg.iters += w.iters;
-                rb = w.n_t;
-            } else {
-                src.restrict_to(B);
-                emit_windows_src<NT>(P, row, src, B, Lout, setn, lo_b, kmax, sh, rb, dg);
-            }
-        }
-    } else if (mask) {
-        emit_out<NT>(P, row, src, B, true, B, 0u, 0u, sh, rb);
-    }
-    if (P.out_count && threadIdx.x == 0) P.out_count[row] = (int32_t)L;
+    const uint32_t Lk = all ? V : ngt + needf;
+    RowOut o{(P.out_idx && P.idx_cap > 0) ? P.out_idx + row * (int64_t)P.idx_cap : nullptr, (uint32_t)P.idx_cap,
+             (P.mask && !md.keep_all) ? P.mask + row * (int64_t)V : nullptr, P.bitmap != 0, V};
+    emit_row<T>(c, lsrc, o, all, vf, ngt, needf, Nf, Lk, key_lo, n, kmax, dg);
+    if (P.out_count && threadIdx.x == 0) P.out_count[row] = (int32_t)Lk;
+    rb = c.rb;
+    dg.iters += c.iters;
     return true;
 }
 
 // r-th largest key of the sample (1 <= r <= number of sample entries), by the
-// same quaternary search over the sample held in registers.
-template <int THREADS, bool BF16>
-QRITA_DEV float sample_rank_value(const void* rowp, int32_t V, uint32_t r, Shared& sh, int& rb) {
+// same quaternary search over the sample's keys in LDS.
+template <class T>
+QRITA_DEV float sample_rank_value(const Params& P, const void* rowp, uint32_t r, Shared& sh, int& rb) {
+    constexpr int NT = T::NT;
+    const int32_t V = P.vocab;
     float x[8];
     bool in[8];
-    load_sample<BF16>(rowp, V, x, in);
-    // only keys are searched: the indices (duplicate order) are never read
-    RegSet<THREADS, 8> s;
-    s.nslots = 8u * THREADS;
-    s.lows = nullptr;
-    s.em = nullptr;
+    if (P.bf16)
+        load_sample<true>(rowp, V, x, in);
+    else
+        load_sample<false>(rowp, V, x, in);
+    uint32_t* a = (uint32_t*)(dyn_lds() + T::A_OFF);
+    lds_sync();
 #pragma unroll
-    for (int i = 0; i < 8; ++i) s.key[i] = in[i] ? f32_key(__float_as_uint(x[i])) : 0u;
+    for (int i = 0; i < 8; ++i) a[threadIdx.x * 8 + i] = in[i] ? f32_key(__float_as_uint(x[i])) : 0u;
+    lds_sync();
     const uint32_t ns = (uint32_t)min(V, kSampleN);
-    int it = 0;
-    const CountOut o =
-        qsearch_count<THREADS, 0>(s, 0u, r, (int64_t)0, ns, (int64_t)0xFFFFFFFFu, 0u, 0, sh, rb, it);
+    Ctx<T, SrcLds<NT>> c{SrcLds<NT>{a, 8u * NT}, wave_segment<T>(), (uint32_t)T::SEG, 0, &sh, rb, 0};
+    const CountOut o = search_count<NT, 0>(c, 0u, r, (int64_t)0, ns, (int64_t)0xFFFFFFFFu, 0u);
+    rb = c.rb;
+    lds_sync();
     return key_value(o.v);
 }
 
@@ -1444,27 +1376,36 @@ struct TailOut {
     int32_t done, path, n_t, iters, rb;
 };
 
-// The tail's slow paths, kept out of line so their registers are allocated
-// apart from the register-set path: a row list too long for registers
+// The row's list (S sub-lists) as a source; gshift from the slice count.
+template <int NT>
+QRITA_DEV SrcList<NT> list_source(const Params& P, int64_t row, uint32_t S, uint32_t stride, const uint32_t* cnt,
+                                  uint32_t n) {
+    const uint32_t s2 = next_pow2(S);
+    const uint32_t gshift = 31u - (uint32_t)__builtin_clz((uint32_t)NT / s2);
+    return SrcList<NT>{P.glist + row * (int64_t)P.list_stride, stride, S, gshift, cnt, n};
+}
+
+// The tail's slow paths, kept out of line: a candidate list too long for LDS
 // (searched in memory), and after a truncation miss the re-collection of the
 // row with thresholds lowered to sample order statistics and, as the last
 // resort, the search of the full row (§1).
-template <int NT, bool BF16>
-__device__ __attribute__((noinline)) TailOut tail_fallback(const Params P, int64_t row, RowMode md, float t,
-                                                           float tc, uint32_t nlist, uint32_t kmax, uint64_t rest,
-                                                           bool overflow, bool list_tried, float lambda,
-                                                           uint32_t ns_h, int32_t n_t, Shared& sh, int rb) {
+template <class T>
+__device__ __attribute__((noinline)) TailOut tail_fallback(const Params P, int64_t row, RowMode md, float t, float tc,
+                                                           uint32_t nlist, uint32_t kmax, uint64_t rest,
+                                                           bool overflow, bool lds_tried, float lambda, uint32_t ns_h,
+                                                           int32_t n_t, Shared& sh, int rb) {
+    constexpr int NT = T::NT;
     const int32_t V = P.vocab;
-    const void* rowp = row_ptr<BF16>(P, row);
-    uint64_t* lst = P.glist + row * (int64_t)P.list_stride;
+    const void* rowp = P.bf16 ? (const void*)((const uint16_t*)P.logits + row * (int64_t)V)
+                              : (const void*)((const float*)P.logits + row * (int64_t)V);
     const float kInf = __builtin_inff();
     TailDiag dg{n_t, 0};
     int path = 1;
     bool done = false;
-    if (!list_tried && !overflow) {
-        MemSrc<NT, false, BF16> src{lst, nullptr, nlist, 0ull};
-        done = finish_row<NT>(P, row, md, src, nlist, (int64_t)f32_key(__float_as_uint(tc)) - 1, kmax, rest, tc,
-                              t, sh, rb, dg);
+    if (!lds_tried && !overflow) {
+        const SrcList<NT> src = list_source<NT>(P, row, (uint32_t)P.slices, (uint32_t)P.sub_cap, sh.cnt, nlist);
+        done = finish_row<T>(P, row, md, src, src, nlist, (int64_t)f32_key(__float_as_uint(tc)) - 1, kmax, rest, tc,
+                             t, sh, rb, dg);
     }
     if (!done) {
         path = 2;
@@ -1476,7 +1417,7 @@ __device__ __attribute__((noinline)) TailOut tail_fallback(const Params P, int64
             const float rr = r0 * (float)(1u << (2 * attempt));
             float tr;
             if (rr < (float)ns)
-                tr = sample_rank_value<NT, BF16>(rowp, V, (uint32_t)rr, sh, rb);
+                tr = sample_rank_value<T>(P, rowp, (uint32_t)rr, sh, rb);
             else if (prev > -kInf)
                 tr = -kInf;
             else
@@ -1486,82 +1427,116 @@ __device__ __attribute__((noinline)) TailOut tail_fallback(const Params P, int64
             uint64_t rest2 = 0;
             uint32_t kmax2 = 0;
             bool ovf = false;
-            const uint32_t cnt =
-                collect_row<NT, BF16>(P, row, tr, md.topp && !md.topk, sh, rb, rest2, kmax2, ovf);
+            uint32_t cnt;
+            if (P.bf16)
+                cnt = collect_row<NT, true>(P, row, tr, md.topp && !md.topk, sh, rb, rest2, kmax2, ovf);
+            else
+                cnt = collect_row<NT, false>(P, row, tr, md.topp && !md.topk, sh, rb, rest2, kmax2, ovf);
             if (ovf) break;
-            MemSrc<NT, false, BF16> src{lst, nullptr, cnt, 0ull};
-            done = finish_row<NT>(P, row, md, src, cnt, (int64_t)f32_key(__float_as_uint(tr)) - 1, kmax2, rest2,
-                                  tr, t, sh, rb, dg);
+            if (threadIdx.x == 0) sh.cnt[0] = cnt;
+            lds_sync();
+            const SrcList<NT> src = list_source<NT>(P, row, 1u, (uint32_t)P.list_stride, sh.cnt, cnt);
+            done = finish_row<T>(P, row, md, src, src, cnt, (int64_t)f32_key(__float_as_uint(tr)) - 1, kmax2, rest2,
+                                 tr, t, sh, rb, dg);
             if (tr == -kInf) break;
         }
     }
     if (!done) {
         path = 3;
-        uint32_t kr = 0, d0 = 0, d1 = 0;
-        uint64_t d2 = 0;
-        for (int64_t e = threadIdx.x; e < V; e += NT) {
-            const uint32_t key = f32_key(__float_as_uint(load_value<BF16>(rowp, e)));
-            kr = key > kr ? key : kr;
-        }
-        block_sum_min_max<NT>(d0, d1, kr, d2, sh, rb);
-        MemSrc<NT, true, BF16> src{nullptr, rowp, (uint32_t)V, 0ull};
-        done = finish_row<NT>(P, row, md, src, (uint32_t)V, -1, kr, 0ull, 0.0f, t, sh, rb, dg);
+        uint32_t kr = 0;
+        const SrcRow<NT> src{rowp, (uint32_t)V, P.bf16 != 0, (uint32_t)V};
+        src.visit([&](uint32_t key, uint32_t) { kr = key > kr ? key : kr; });
+        uint32_t mn[1] = {~wave_max_u32(kr)};
+        comb_record<NT, 0, 0, 1>(nullptr, nullptr, mn, sh, rb);
+        kr = ~mn[0];
+        done = finish_row<T>(P, row, md, src, src, (uint32_t)V, -1, kr, 0ull, 0.0f, t, sh, rb, dg);
     }
     return TailOut{done ? 1 : 0, path, dg.n_t, dg.iters, rb};
 }
 
-// Tail: one workgroup per row. A row list of up to tail_cap candidates is
-// searched with the candidates in registers; everything else takes
-// tail_fallback.
-template <int NT, bool BF16>
-__global__ __launch_bounds__(NT) void tail_kernel(Params P) {
+// Tail: one workgroup per row. The row's sub-lists are loaded into LDS when
+// they fit and did not overflow; everything else takes tail_fallback.
+template <class T>
+__global__ __launch_bounds__(T::NT, T::WAVES_PER_SIMD) void tail_kernel(Params P) {
+    constexpr int NT = T::NT;
     __shared__ Shared sh;
     int rb = 0;
     const int64_t row = blockIdx.x;
     if (row >= P.batch) return;
     const int32_t V = P.vocab;
-    uint32_t* hdr = P.hdr + row * H_WORDS;
-    const uint64_t* lst = P.glist + row * (int64_t)P.list_stride;
-    // the head of the row list is read before the header tells how much of
-    // it is filled (entries past the fill are ignored)
-    uint64_t pre[kTailPre];
-    {
-        const uint32_t lim = min((uint32_t)P.list_stride, (uint32_t)(kTailPre * NT));
-#pragma unroll
-        for (int r = 0; r < kTailPre; ++r) {
-            const uint32_t i = (uint32_t)r * NT + threadIdx.x;
-            pre[r] = i < lim ? lst[i] : 0ull;
-        }
-    }
+    const uint32_t S = (uint32_t)P.slices;
     const RowMode md = row_mode(P, row);
-    const float t = __uint_as_float(uni(hdr[H_T]));
-    const float tc = __uint_as_float(uni(hdr[H_TC]));
-    const uint32_t nlist = uni(hdr[H_LIST]);
-    const uint32_t kmax = uni(hdr[H_KMAX]);
-    const bool overflow = uni(hdr[H_FLAGS]) != 0 || nlist > (uint32_t)P.list_cap;
-    const uint64_t rest = (uint64_t)uni(hdr[H_REST]) | ((uint64_t)uni(hdr[H_REST + 1]) << 32);
-    const bool predicted = uni(hdr[H_PRED]) != 0;
+    const uint32_t* rr = P.rowrec + row * R_WORDS;
+    const uint4 r4 = *(const uint4*)rr;
+    const float t = __uint_as_float(uni(r4.x));
+    const float tc = __uint_as_float(uni(r4.y));
+    const bool predicted = uni(r4.z) != 0;
+    const float lambda = __uint_as_float(uni(r4.w));
+    const uint32_t ns_h = uni(rr[R_NS]);
+    // the slice records: every wave combines them (lane s reads slice s)
+    const uint32_t lane = threadIdx.x & (kWave - 1);
+    uint4 q = make_uint4(0u, 0u, 0u, 0u);
+    if (lane < S) q = *(const uint4*)(P.slrec + (row * kMaxSlices + lane) * S_WORDS);
+    const uint32_t cnt_s = q.x;
+    const uint32_t nlist = uni(wave_sum_u32(cnt_s));
+    const uint32_t kmax = uni(wave_max_u32(q.y));
+    const uint64_t rest = uni(wave_sum_u64((uint64_t)q.z | ((uint64_t)q.w << 32)));
+    const bool overflow = uni(wave_max_u32(cnt_s)) > (uint32_t)P.sub_cap;
+    if (threadIdx.x < S) sh.cnt[threadIdx.x] = cnt_s;
+    if (threadIdx.x < kWave) {
+        // exclusive prefix of the counts over the slices (lanes)
+        uint32_t x = cnt_s;
+        QRITA_WAVE_STEPS(op_add, 0u)
+        if (lane < S) sh.pre[lane] = x - cnt_s;
+    }
+    lds_sync();
 
     TailDiag dg{-1, 0};
     int path = 0;
     bool done = false;
+    uint8_t* mrow = P.mask ? P.mask + row * (int64_t)V : nullptr;
     if (!md.need_cand) {
         if (P.out_count && threadIdx.x == 0) P.out_count[row] = V;
         done = true;
     } else {
-        const bool in_regs = !overflow && nlist <= (uint32_t)P.tail_cap;
-        if (in_regs) {
+        const bool in_lds = !overflow && nlist <= (uint32_t)P.tail_cap;
+        if (in_lds) {
             // every candidate has z >= tc, so its key exceeds key(tc) - 1
             const int64_t key_lo = (int64_t)f32_key(__float_as_uint(tc)) - 1;
-            RegSet<NT, kTailR> src;
-            src.em = (float*)lds_cands();  // shares the sort buffer: masses are dead by the sort
-            src.lows = (uint32_t*)(lds_cands() + P.tail_alloc);
-            src.load(lst, nlist, pre);
-            done = finish_row<NT>(P, row, md, src, nlist, key_lo, kmax, rest, tc, t, sh, rb, dg);
+            uint32_t* a = (uint32_t*)(dyn_lds() + T::A_OFF);
+            // sub-list s is copied by a group of NT / next_pow2(S) threads to
+            // a[pre[s] ..]; eight loads per thread in flight
+            {
+                const uint32_t s2 = next_pow2(S);
+                const uint32_t gshift = 31u - (uint32_t)__builtin_clz((uint32_t)NT / s2);
+                const uint32_t tps = 1u << gshift;
+                const uint32_t s = threadIdx.x >> gshift, g = threadIdx.x & (tps - 1u);
+                const uint32_t cs = s < S ? sh.cnt[s] : 0u, ps = s < S ? sh.pre[s] : 0u;
+                const uint64_t* p = P.glist + row * (int64_t)P.list_stride + (int64_t)s * P.sub_cap;
+                constexpr int U = 8;
+                for (uint32_t j0 = g; j0 < cs; j0 += tps * U) {
+                    uint64_t cv[U];
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        const uint32_t j = j0 + (uint32_t)u * tps;
+                        cv[u] = j < cs ? p[j] : 0ull;
+                    }
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        const uint32_t j = j0 + (uint32_t)u * tps;
+                        if (j < cs) a[ps + j] = cand_key(cv[u]);
+                    }
+                }
+                if (threadIdx.x < 4u && nlist + threadIdx.x < ((nlist + 3u) & ~3u)) a[nlist + threadIdx.x] = 0u;
+            }
+            lds_sync();
+            const SrcLds<NT> src{a, nlist};
+            const SrcList<NT> lsrc = list_source<NT>(P, row, S, (uint32_t)P.sub_cap, sh.cnt, nlist);
+            done = finish_row<T>(P, row, md, src, lsrc, nlist, key_lo, kmax, rest, tc, t, sh, rb, dg);
         }
         if (!done) {
-            const TailOut o = tail_fallback<NT, BF16>(P, row, md, t, tc, nlist, kmax, rest, overflow, in_regs,
-                                                      __uint_as_float(hdr[H_LAMBDA]), hdr[H_NS], dg.n_t, sh, rb);
+            const TailOut o = tail_fallback<T>(P, row, md, t, tc, nlist, kmax, rest, overflow, in_lds, lambda, ns_h,
+                                               dg.n_t, sh, rb);
             done = o.done != 0;
             path = o.path;
             dg.n_t = o.n_t;
@@ -1569,20 +1544,19 @@ __global__ __launch_bounds__(NT) void tail_kernel(Params P) {
             rb = o.rb;
         }
     }
-    lds_sync();
-    if (threadIdx.x == 0) {
-        for (int w = 0; w < H_WORDS; ++w) hdr[w] = 0u;
-        if (P.diag) {
-            int32_t* d = P.diag + row * 8;
-            d[0] = (int32_t)__float_as_uint(t);
-            d[1] = (int32_t)__float_as_uint(tc);
-            d[2] = dg.n_t;
-            d[3] = (int32_t)nlist;
-            d[4] = path;
-            d[5] = (md.K_t > 0 && dg.n_t >= 0) ? (dg.n_t >= (int32_t)md.K_t) : (path <= 1 ? 1 : 0);
-            d[6] = dg.iters;
-            d[7] = predicted ? 1 : 0;
-        }
+    // keep-all rows: the whole mask row is ones (pass 1 wrote it unless the
+    // tail writes masks)
+    if (md.keep_all && mrow && P.bitmap) fill_mask_row<NT>(mrow, (uint32_t)V, 1);
+    if (threadIdx.x == 0 && P.diag) {
+        int32_t* d = P.diag + row * 8;
+        d[0] = (int32_t)__float_as_uint(t);
+        d[1] = (int32_t)__float_as_uint(tc);
+        d[2] = dg.n_t;
+        d[3] = (int32_t)nlist;
+        d[4] = path;
+        d[5] = (md.K_t > 0 && dg.n_t >= 0) ? (dg.n_t >= (int32_t)md.K_t) : (path <= 1 ? 1 : 0);
+        d[6] = dg.iters;
+        d[7] = predicted ? 1 : 0;
     }
 }
 
