@@ -59,8 +59,11 @@ struct Plan {
 //  - tail: the light tier (two rows per CU) for batches of 256 rows or more
 //    whose index output is at most 4096 ranks, else the heavy tier (one row
 //    per CU, twice the LDS capacities, kept sets up to 8192 sorted at once);
-//  - the mask is written by the tail from an LDS bitmap whenever the row
-//    fits the tier's bitmap, so pass 1 only reads.
+//  - from 512 rows on, the mask is written by the tail from an LDS bitmap
+//    whenever the row fits the tier's bitmap, so pass 1 only reads (with
+//    fewer rows, the whole-row writes would fall on too few CUs: pass 1
+//    zero-fills the mask at streaming bandwidth and the tail stores the kept
+//    bytes).
 Plan choose_plan(int64_t B, int64_t V, int64_t esize, int64_t idx_cap, const qrita_options* o) {
     Plan t;
     int64_t S = std::max<int64_t>(1, (1024 + B - 1) / B);
@@ -91,7 +94,7 @@ Plan choose_plan(int64_t B, int64_t V, int64_t esize, int64_t idx_cap, const qri
     if (o && o->list_cap > 0) lc = std::max<int64_t>(1, std::min<int64_t>(lc, o->list_cap));
     t.list_cap = (int)lc;
     t.sub_cap = (int)std::max<int64_t>(1, lc / S);
-    t.bitmap = (uint64_t)V <= (uint64_t)ti.bitmap_bits && !(o && o->mask_mode == 1);
+    t.bitmap = B >= 512 && (uint64_t)V <= (uint64_t)ti.bitmap_bits && !(o && o->mask_mode == 1);
     return t;
 }
 

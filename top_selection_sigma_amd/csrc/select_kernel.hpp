@@ -58,7 +58,7 @@ struct Shared {
     uint32_t ncand;
     uint32_t flags;
     uint32_t gather_n;
-    uint32_t u32[8];
+    alignas(8) uint32_t u32[8];
     uint32_t wspill[kMaxWaves];  // pass 1: entries left in each wave's spill buffer
     uint32_t nsub;               // pass 1: entries reserved in the slice's sub-list
     uint32_t cnt[kMaxSlices];    // tail: candidates per slice

@@ -21,7 +21,7 @@ namespace qrita {
 // Tiers of the tail (the summary's tiered block sizes, "Autotuning"): the
 // light tier fits two workgroups per CU (rows of large batches overlap their
 // latencies), the heavy one holds twice the candidates and sorts kept sets of
-// up to 8192 in one piece.
+// up to 8704 (8192 and their boundary duplicates) in one piece.
 // ---------------------------------------------------------------------------
 template <int CFULL_, int SEG_, int CSORT_, int NB_>
 struct TailTier {
@@ -33,24 +33,26 @@ struct TailTier {
     static constexpr int NB = NB_;         // bucket-sort bins
     static constexpr int WAVES_PER_SIMD = CFULL_ <= 12288 ? 2 : 1;  // rows resident per CU
     // LDS layout (bytes). Search phase: keys, then the wave segments. Emit
-    // phase (after the search): the words to sort, the sort's position array,
-    // its per-position results (ranks' kept indices), bin counts and code
-    // starts; the mask bitmap reuses the words' region.
+    // phase (after the search): the words to sort, the bucket sort's
+    // positions in bin order (16 bits each), bin counts and code starts. After
+    // the sort, everything past the words holds the mask bitmap; the bitonic
+    // fallback sorts in everything from the words on.
     static constexpr size_t A_OFF = 0;
     static constexpr size_t W_OFF = A_OFF + (size_t)CFULL * 4;
     static constexpr size_t SEARCH_END = W_OFF + (size_t)NW * SEG * 8;
     static constexpr size_t SA_OFF = 0;
     static constexpr size_t SB_OFF = SA_OFF + (size_t)(CSORT + 8) * 8;
-    static constexpr size_t SR_OFF = SB_OFF + (size_t)CSORT * 4;
-    static constexpr size_t BINS_OFF = SR_OFF + (size_t)CSORT * 4;
+    static constexpr size_t BINS_OFF = SB_OFF + ((size_t)CSORT * 2 + 15) / 16 * 16;
     static constexpr size_t HC_OFF = BINS_OFF + (size_t)(NB + 4) * 4;
     static constexpr size_t EMIT_END = HC_OFF + (size_t)(NB + 4) * 4;
     static constexpr size_t LDS = SEARCH_END > EMIT_END ? SEARCH_END : EMIT_END;
-    static constexpr uint32_t BITMAP_BITS = (uint32_t)((CSORT + 8) * 64);
+    static constexpr uint32_t BITMAP_BITS = (uint32_t)((LDS - SB_OFF) * 8);
+    static_assert(CSORT <= 65536, "16-bit positions");
+    static_assert(LDS - SA_OFF >= (size_t)2 * CSORT * 8, "bitonic fallback region");
     static_assert(SEARCH_END % 16 == 0 && SB_OFF % 16 == 0 && BINS_OFF % 16 == 0, "alignment");
 };
-using TierLight = TailTier<12288, 768, 4096, 1024>;
-using TierHeavy = TailTier<24576, 1536, 8192, 2048>;
+using TierLight = TailTier<12288, 768, 4096, 2048>;
+using TierHeavy = TailTier<24576, 1536, 8704, 4096>;
 
 extern __shared__ uint64_t qrita_dyn_lds[];
 QRITA_DEV char* dyn_lds() { return (char*)qrita_dyn_lds; }
@@ -194,7 +196,7 @@ struct SrcLds {
 
 // The row's candidate lists in global memory: S sub-lists, sub-list s holding
 // cnt[s] (LDS) entries at base + s * stride. Sub-list s is read by a group of
-// NT >> gshift threads; eight loads per thread are in flight.
+// NT >> gshift threads; sixteen loads per thread are in flight.
 template <int NT>
 struct SrcList {
     static constexpr bool kLows = true;
@@ -206,7 +208,7 @@ struct SrcList {
     uint32_t n;            // total
     template <class F>
     QRITA_DEV void visit(F&& f) const {
-        constexpr int U = 8;
+        constexpr int U = 16;
         const uint32_t t = tid_here();
         const uint32_t tps = 1u << gshift;
         const uint32_t s = t >> gshift, g = t & (tps - 1u);
@@ -512,6 +514,11 @@ QRITA_DEV void make_pivots(uint32_t lo, uint32_t hi, int mode, int field, uint32
     }
 }
 
+// A wave compacts its set only when it holds at least this many candidates
+// (four per lane): below that an evaluation costs little more than the
+// compaction pass itself.
+constexpr uint32_t kCompactMin = 256;
+
 template <class T>
 QRITA_DEV T pick4(int j, T a, T b, T c, T d) {
     return j == 3 ? d : (j == 2 ? c : (j == 1 ? b : a));
@@ -611,7 +618,7 @@ QRITA_DEV CountOut search_count(C& c, uint32_t v_eq, uint32_t K, int64_t lo_in, 
             // in (t_js, t_js+1]
             const uint32_t bound = pick4(js, E.Gw[0], E.Gw[1], E.Gw[2], E.Gw[3]) -
                                    pick4(js, E.Gw[1], E.Gw[2], E.Gw[3], ws.above);
-            if (bound <= kcap && bound * 4u <= share * 3u) {
+            if (share >= kCompactMin && bound <= kcap && bound * 4u <= share * 3u) {
                 if (compact_wave<false>(c.src, ws, c.seg, kcap, lo, hi, 0.0f)) share = ws.n;
             }
         }
@@ -716,7 +723,7 @@ QRITA_DEV bool search_mass(C& c, const MassSet& ms, float m, int64_t lo_in, int6
         // while lo < vx, and until then the candidates at vx are kept
         const uint32_t bound = pick4(js, E.Gw[0], E.Gw[1], E.Gw[2], E.Gw[3]) -
                                    pick4(js, E.Gw[1], E.Gw[2], E.Gw[3], ws.above);
-        if (bound <= c.segcap && bound * 4u <= share * 3u) {
+        if (share >= kCompactMin && bound <= c.segcap && bound * 4u <= share * 3u) {
             if (compact_wave<true>(c.src, ws, c.seg, c.segcap, lo, hi, m)) share = ws.n;
         }
     }
@@ -789,20 +796,20 @@ QRITA_DEV uint32_t scan_counts(uint32_t* v, uint32_t n, Shared& sh, int& rb) {
     return big;
 }
 
-// Where a sort puts the word of rank r: index r of the index output
-// (r < lout); with `kept`, the position p of the word in the sort's position
-// array records its index when r < lmask (else ~0), for the mask afterwards;
-// without it, the mask byte is set directly.
+// Where a sort puts the word w of rank r: index r of the index output
+// (r < lout); the mask byte when r < lmask (scattered bytes, mrow); and, with
+// `last`, the word of rank lmask - 1 (the kept set's boundary word, for a
+// bitmap mask afterwards).
 struct RankOut {
     int32_t* out;
     uint32_t lout;
-    uint8_t* mrow;    // scattered mask bytes (null: none)
-    uint32_t* kept;   // LDS, [cnt] (null: none)
+    uint8_t* mrow;   // scattered mask bytes (null: none)
     uint32_t lmask;
-    QRITA_DEV void put(uint32_t r, uint32_t idx, uint32_t p) const {
-        if (r < lout) out[r] = (int32_t)idx;
-        if (mrow && r < lmask) mrow[idx] = 1;
-        if (kept) kept[p] = r < lmask ? idx : 0xFFFFFFFFu;
+    uint64_t* last;  // LDS word (null: none)
+    QRITA_DEV void put(uint32_t r, uint64_t w) const {
+        if (r < lout) out[r] = (int32_t)cand_idx(w);
+        if (mrow && r < lmask) mrow[cand_idx(w)] = 1;
+        if (last && r + 1 == lmask) *last = w;
     }
 };
 
@@ -835,13 +842,13 @@ QRITA_DEV void rank_sort(uint64_t* a, uint32_t cnt, const RankOut& ro, uint32_t*
         if (above) atomicAdd(&acc[e], above);
     }
     lds_sync();
-    if (q == 0 && e < cnt) ro.put(acc[e], cand_idx(x), e);
+    if (q == 0 && e < cnt) ro.put(acc[e], x);
     lds_sync();
 }
 
-// Bitonic sort, descending, of the np (a power of two, <= the words' region)
-// words a[0 .. np) in LDS, one barrier per stage; then the rank of position g
-// is g. For sets the bucket sort cannot split.
+// Bitonic sort, descending, of the np (a power of two, at most twice the
+// set) words a[0 .. np) in LDS, one barrier per stage; then the rank of
+// position g is g. For sets the bucket sort cannot split.
 template <int NT>
 QRITA_DEV void bitonic_lds(uint64_t* a, uint32_t np, uint32_t cnt, const RankOut& ro) {
     const uint32_t t = threadIdx.x;
@@ -861,7 +868,7 @@ QRITA_DEV void bitonic_lds(uint64_t* a, uint32_t np, uint32_t cnt, const RankOut
             lds_sync();
         }
     }
-    for (uint32_t g = t; g < cnt; g += NT) ro.put(g, cand_idx(a[g]), g);
+    for (uint32_t g = t; g < cnt; g += NT) ro.put(g, a[g]);
     lds_sync();
 }
 
@@ -873,15 +880,15 @@ QRITA_DEV void bitonic_lds(uint64_t* a, uint32_t np, uint32_t cnt, const RankOut
 // (lmax - low), so tie groups spread too. First every code gets the same
 // number of bins; if a bin then holds more than kMaxBin words, each code
 // instead gets a run of bins in proportion to how many words it holds (code
-// starts in hc). The words' positions are scattered into bins (pos array,
-// LDS); a word's rank is its bin's start plus the number of larger words in
-// its bin, counted directly, so the result does not depend on the order of
-// the LDS atomics that fill the bins. Returns false, having written nothing,
-// when a bin still holds more than kMaxBin words.
+// starts in hc). The words' positions are scattered into bins (pos, LDS); a
+// word's rank is its bin's start plus the number of larger words in its bin,
+// counted directly, so the result does not depend on the order of the LDS
+// atomics that fill the bins. Returns false, having written nothing, when a
+// bin still holds more than kMaxBin words.
 constexpr uint32_t kMaxBin = 96;
 
 template <int NT, int NB>
-QRITA_DEV bool bucket_sort(const uint64_t* a, uint32_t cnt, const RankOut& ro, uint32_t* pos, uint32_t* bins,
+QRITA_DEV bool bucket_sort(const uint64_t* a, uint32_t cnt, const RankOut& ro, uint16_t* pos, uint32_t* bins,
                            uint32_t* hc, Shared& sh, int& rb) {
     const uint32_t t = threadIdx.x;
     const uint32_t key0 = uni(cand_key(a[0]));
@@ -964,7 +971,7 @@ QRITA_DEV bool bucket_sort(const uint64_t* a, uint32_t cnt, const RankOut& ro, u
         if (big > kMaxBin) return false;
     }
     // scatter the positions; afterwards bins[i] is the end of bin i
-    for (uint32_t i = t; i < cnt; i += NT) pos[atomicAdd(&bins[bin_of(a[i])], 1u)] = i;
+    for (uint32_t i = t; i < cnt; i += NT) pos[atomicAdd(&bins[bin_of(a[i])], 1u)] = (uint16_t)i;
     lds_sync();
     // ranks, by position in the binned order: the lanes of a wave mostly
     // share a bin, so their scans take the same number of steps
@@ -974,7 +981,7 @@ QRITA_DEV bool bucket_sort(const uint64_t* a, uint32_t cnt, const RankOut& ro, u
         const uint32_t s0 = bi ? bins[bi - 1] : 0u, e0 = bins[bi];
         uint32_t r = s0;
         for (uint32_t q = s0; q < e0; ++q) r += a[pos[q]] > w ? 1u : 0u;
-        ro.put(r, cand_idx(w), p);
+        ro.put(r, w);
     }
     lds_sync();
     return true;
@@ -982,12 +989,13 @@ QRITA_DEV bool bucket_sort(const uint64_t* a, uint32_t cnt, const RankOut& ro, u
 
 // Rank order of the cnt <= CSORT words at the start of the sort region: a
 // handful by ranking, more by the bucket sort, sets it cannot split by the
-// bitonic sort. RankOut::kept (when used) is the sort's position array.
+// bitonic sort. The words stay in the first region (the bitonic sort permutes
+// them).
 template <class T>
 QRITA_DEV void sort_words(uint32_t cnt, RankOut ro, Shared& sh, int& rb) {
     constexpr int NT = T::NT;
     uint64_t* a = (uint64_t*)(dyn_lds() + T::SA_OFF);
-    uint32_t* pos = (uint32_t*)(dyn_lds() + T::SB_OFF);
+    uint16_t* pos = (uint16_t*)(dyn_lds() + T::SB_OFF);
     uint32_t* bins = (uint32_t*)(dyn_lds() + T::BINS_OFF);
     uint32_t* hc = (uint32_t*)(dyn_lds() + T::HC_OFF);
     cnt = min(uni(cnt), (uint32_t)T::CSORT);  // more only for inputs outside the contract (NaN logits)
@@ -997,7 +1005,7 @@ QRITA_DEV void sort_words(uint32_t cnt, RankOut ro, Shared& sh, int& rb) {
         return;
     }
     if (bucket_sort<NT, T::NB>(a, cnt, ro, pos, bins, hc, sh, rb)) return;
-    const uint32_t np = next_pow2(cnt);
+    const uint32_t np = next_pow2(cnt);  // < 2 cnt: inside the fallback region
     for (uint32_t i = cnt + threadIdx.x; i < np; i += NT) a[i] = 0ull;
     lds_sync();
     bitonic_lds<NT>(a, np, cnt, ro);
@@ -1150,7 +1158,7 @@ QRITA_DEV void mask_from_boundary(const L& lsrc, uint64_t B, const RowOut& o) {
     constexpr int NT = T::NT;
     if (!o.mrow) return;
     if (o.bitmap) {
-        uint32_t* bm = (uint32_t*)(dyn_lds() + T::SA_OFF);
+        uint32_t* bm = (uint32_t*)(dyn_lds() + T::SB_OFF);
         lds_sync();
         clear_words(bm, (o.V + 31u) / 32u, NT);
         lds_sync();
@@ -1168,19 +1176,23 @@ QRITA_DEV void mask_from_boundary(const L& lsrc, uint64_t B, const RowOut& o) {
     }
 }
 
-// Mask from the kept indices the sort recorded in its position array.
+// Bitmap mask of the sorted words at or above the boundary word B (the words
+// are still in the first sort region; the bitmap follows it).
 template <class T>
-QRITA_DEV void mask_from_sorted(uint32_t cnt, const RowOut& o) {
+QRITA_DEV void mask_from_sorted(uint32_t cnt, uint64_t B, const RowOut& o) {
     constexpr int NT = T::NT;
     if (!o.mrow || !o.bitmap) return;
-    uint32_t* bm = (uint32_t*)(dyn_lds() + T::SA_OFF);
-    const uint32_t* kept = (const uint32_t*)(dyn_lds() + T::SR_OFF);
+    const uint64_t* a = (const uint64_t*)(dyn_lds() + T::SA_OFF);
+    uint32_t* bm = (uint32_t*)(dyn_lds() + T::SB_OFF);
     lds_sync();
     clear_words(bm, (o.V + 31u) / 32u, NT);
     lds_sync();
     for (uint32_t p = threadIdx.x; p < cnt; p += NT) {
-        const uint32_t i = kept[p];
-        if (i != 0xFFFFFFFFu) atomicOr(&bm[i >> 5], 1u << (i & 31u));
+        const uint64_t w = a[p];
+        if (w >= B) {
+            const uint32_t i = cand_idx(w);
+            atomicOr(&bm[i >> 5], 1u << (i & 31u));
+        }
     }
     lds_sync();
     write_mask_row<NT>(o.mrow, bm, o.V);
@@ -1218,10 +1230,14 @@ QRITA_DEV void emit_row(C& c, const L& lsrc, const RowOut& o, bool all, uint32_t
     if (Gi <= (uint32_t)T::CSORT && same) {
         // one sort over every candidate at or above the boundary value
         const uint32_t cnt = gather_words<NT>(lsrc, a, T::CSORT, (uint64_t)(Lout > 0 ? vo : vf) << 32, ~0ull, sh);
-        RankOut ro{o.idx, Lout, (mask && !o.bitmap) ? o.mrow : nullptr,
-                   (mask && o.bitmap) ? (uint32_t*)(dyn_lds() + T::SR_OFF) : nullptr, mask ? L_ : 0u};
+        RankOut ro{o.idx, Lout, (mask && !o.bitmap) ? o.mrow : nullptr, mask ? L_ : 0u,
+                   (mask && o.bitmap) ? (uint64_t*)&sh.u32[0] : nullptr};
         sort_words<T>(cnt, ro, sh, c.rb);
-        if (mask) mask_from_sorted<T>(min(cnt, (uint32_t)T::CSORT), o);
+        if (mask && o.bitmap) {
+            lds_sync();
+            const uint64_t B = uni(*(const uint64_t*)&sh.u32[0]);
+            mask_from_sorted<T>(min(cnt, (uint32_t)T::CSORT), B, o);
+        }
         return;
     }
     // the kept set's boundary word, for the mask
@@ -1232,7 +1248,7 @@ QRITA_DEV void emit_row(C& c, const L& lsrc, const RowOut& o, bool all, uint32_t
     if (Lout == 0) return;
     if (Gi <= (uint32_t)T::CSORT) {
         const uint32_t cnt = gather_words<NT>(lsrc, a, T::CSORT, (uint64_t)vo << 32, ~0ull, sh);
-        sort_words<T>(cnt, RankOut{o.idx, Lout, nullptr, nullptr, 0u}, sh, c.rb);
+        sort_words<T>(cnt, RankOut{o.idx, Lout, nullptr, 0u, nullptr}, sh, c.rb);
         return;
     }
     // windows of CSORT ranks, each bounded by its own boundary word
@@ -1246,7 +1262,7 @@ QRITA_DEV void emit_row(C& c, const L& lsrc, const RowOut& o, bool all, uint32_t
             Bn = tie_boundary<T>(lsrc, r.v, done + cnt - r.n_gt, r.N, o.V, c.mode, sh, c.rb, dg.iters);
         }
         const uint32_t got = gather_words<NT>(lsrc, a, T::CSORT, Bn, prev, sh);
-        sort_words<T>(got, RankOut{o.idx + done, cnt, nullptr, nullptr, 0u}, sh, c.rb);
+        sort_words<T>(got, RankOut{o.idx + done, cnt, nullptr, 0u, nullptr}, sh, c.rb);
         prev = Bn;
         done += cnt;
     }
@@ -1505,7 +1521,7 @@ __global__ __launch_bounds__(T::NT, T::WAVES_PER_SIMD) void tail_kernel(Params P
             const int64_t key_lo = (int64_t)f32_key(__float_as_uint(tc)) - 1;
             uint32_t* a = (uint32_t*)(dyn_lds() + T::A_OFF);
             // sub-list s is copied by a group of NT / next_pow2(S) threads to
-            // a[pre[s] ..]; eight loads per thread in flight
+            // a[pre[s] ..]; 32 loads per thread in flight
             {
                 const uint32_t s2 = next_pow2(S);
                 const uint32_t gshift = 31u - (uint32_t)__builtin_clz((uint32_t)NT / s2);
@@ -1513,18 +1529,20 @@ __global__ __launch_bounds__(T::NT, T::WAVES_PER_SIMD) void tail_kernel(Params P
                 const uint32_t s = threadIdx.x >> gshift, g = threadIdx.x & (tps - 1u);
                 const uint32_t cs = s < S ? sh.cnt[s] : 0u, ps = s < S ? sh.pre[s] : 0u;
                 const uint64_t* p = P.glist + row * (int64_t)P.list_stride + (int64_t)s * P.sub_cap;
-                constexpr int U = 8;
+                constexpr int U = 32;
+                // only the keys (the high words of the entries) are needed here
+                const uint32_t* pk = (const uint32_t*)p + 1;
                 for (uint32_t j0 = g; j0 < cs; j0 += tps * U) {
-                    uint64_t cv[U];
+                    uint32_t kv[U];
 #pragma unroll
                     for (int u = 0; u < U; ++u) {
                         const uint32_t j = j0 + (uint32_t)u * tps;
-                        cv[u] = j < cs ? p[j] : 0ull;
+                        kv[u] = j < cs ? pk[2 * (size_t)j] : 0u;
                     }
 #pragma unroll
                     for (int u = 0; u < U; ++u) {
                         const uint32_t j = j0 + (uint32_t)u * tps;
-                        if (j < cs) a[ps + j] = cand_key(cv[u]);
+                        if (j < cs) a[ps + j] = kv[u];
                     }
                 }
                 if (threadIdx.x < 4u && nlist + threadIdx.x < ((nlist + 3u) & ~3u)) a[nlist + threadIdx.x] = 0u;
