@@ -34,7 +34,8 @@ struct TailTier {
     static constexpr int WAVES_PER_SIMD = CFULL_ <= 12288 ? 2 : 1;  // rows resident per CU
     // LDS layout (bytes). Search phase: keys, then the wave segments. Emit
     // phase (after the search): the words to sort, the bucket sort's
-    // positions in bin order (16 bits each), bin counts and code starts. After
+    // positions in bin order and each word's bin (16 bits each), bin counts
+    // and code starts. After
     // the sort, everything past the words holds the mask bitmap; the bitonic
     // fallback sorts in everything from the words on.
     static constexpr size_t A_OFF = 0;
@@ -42,7 +43,8 @@ struct TailTier {
     static constexpr size_t SEARCH_END = W_OFF + (size_t)NW * SEG * 8;
     static constexpr size_t SA_OFF = 0;
     static constexpr size_t SB_OFF = SA_OFF + (size_t)(CSORT + 8) * 8;
-    static constexpr size_t BINS_OFF = SB_OFF + ((size_t)CSORT * 2 + 15) / 16 * 16;
+    static constexpr size_t BO_OFF = SB_OFF + ((size_t)CSORT * 2 + 15) / 16 * 16;
+    static constexpr size_t BINS_OFF = BO_OFF + ((size_t)CSORT * 2 + 15) / 16 * 16;
     static constexpr size_t HC_OFF = BINS_OFF + (size_t)(NB + 4) * 4;
     static constexpr size_t EMIT_END = HC_OFF + (size_t)(NB + 4) * 4;
     static constexpr size_t LDS = SEARCH_END > EMIT_END ? SEARCH_END : EMIT_END;
@@ -887,35 +889,20 @@ QRITA_DEV void bitonic_lds(uint64_t* a, uint32_t np, uint32_t cnt, const RankOut
 // bin still holds more than kMaxBin words.
 constexpr uint32_t kMaxBin = 96;
 
+// Extents of a set of words, gathered with it (block-uniform): key and
+// complemented-index ranges, and the number of low key bits all keys share.
+struct SortExt {
+    uint32_t kmn, kmx, lmn, lmx, tz;
+};
+
 template <int NT, int NB>
-QRITA_DEV bool bucket_sort(const uint64_t* a, uint32_t cnt, const RankOut& ro, uint16_t* pos, uint32_t* bins,
-                           uint32_t* hc, Shared& sh, int& rb) {
+QRITA_DEV bool bucket_sort(const uint64_t* a, uint32_t cnt, const SortExt& ex, const RankOut& ro, uint16_t* pos,
+                           uint16_t* binof, uint32_t* bins, uint32_t* hc, Shared& sh, int& rb) {
     const uint32_t t = threadIdx.x;
-    const uint32_t key0 = uni(cand_key(a[0]));
-    uint32_t kmn = 0xFFFFFFFFu, kmx = 0u, lmn = 0xFFFFFFFFu, lmx = 0u, tz = 32u;
-    for (uint32_t i = t; i < cnt; i += NT) {
-        const uint64_t w = a[i];
-        const uint32_t k = cand_key(w), l = cand_low(w);
-        kmn = k < kmn ? k : kmn;
-        kmx = k > kmx ? k : kmx;
-        lmn = l < lmn ? l : lmn;
-        lmx = l > lmx ? l : lmx;
-        const uint32_t d = k ^ key0;
-        const uint32_t z = d ? (uint32_t)__builtin_ctz(d) : 32u;
-        tz = z < tz ? z : tz;
-    }
-    uint32_t ext[5] = {wave_min_u32(kmn), ~wave_max_u32(kmx), wave_min_u32(lmn), ~wave_max_u32(lmx),
-                       wave_min_u32(tz)};
-    // the bin counts are cleared before the combination's barrier, which
-    // orders them before the first count
+    const uint32_t kmn = ex.kmn, kmx = ex.kmx, lmn = ex.lmn, lmx = ex.lmx;
     const uint32_t nb = min((uint32_t)NB, 2u * next_pow2(cnt));
     for (uint32_t i = t; i <= nb; i += NT) bins[i] = 0u;
-    comb_record<NT, 0, 0, 5>(nullptr, nullptr, ext, sh, rb);
-    kmn = uni(ext[0]);
-    kmx = ~uni(ext[1]);
-    lmn = uni(ext[2]);
-    lmx = ~uni(ext[3]);
-    const uint32_t kz = min(uni(ext[4]), 31u);
+    const uint32_t kz = min(ex.tz, 31u);
     const uint32_t nbits = 31u - (uint32_t)__builtin_clz(nb);
     const uint32_t fine_max = (kmx - kmn) >> kz;
     const uint32_t cbits = bits_for((uint64_t)fine_max);
@@ -935,24 +922,22 @@ QRITA_DEV bool bucket_sort(const uint64_t* a, uint32_t cnt, const RankOut& ro, u
     // every code the same run of bins: code bits, then the top sub bits
     const uint32_t lkeep = nbits - (cbits - kdrop);
     const uint32_t sshift = sbits > lkeep ? sbits - lkeep : 0u;
-    bool prop = false;
-    const float ratio = (float)nb / (float)cnt;
-    auto first = [&](uint32_t cc) {
-        if (cc >= ncodes) return nb;
-        const uint32_t f = (uint32_t)((float)hc[cc] * ratio);
-        return f < nb - 1u ? f : nb - 1u;
+    auto bin_eq = [&](uint64_t w) {
+        const uint32_t sc = lkeep ? (uint32_t)(sub_of(w) >> sshift) : 0u;
+        return (code_of(w) << lkeep) | sc;
     };
-    auto bin_of = [&](uint64_t w) {
-        if (!prop) {
-            const uint32_t sc = lkeep ? (uint32_t)(sub_of(w) >> sshift) : 0u;
-            return (code_of(w) << lkeep) | sc;
+    lds_sync();
+    for (uint32_t i = t; i < cnt; i += 2 * NT) {
+        const uint32_t i1 = i + NT;
+        const uint32_t b0 = bin_eq(a[i]);
+        const uint32_t b1 = i1 < cnt ? bin_eq(a[i1]) : 0u;
+        binof[i] = (uint16_t)b0;
+        atomicAdd(&bins[b0], 1u);
+        if (i1 < cnt) {
+            binof[i1] = (uint16_t)b1;
+            atomicAdd(&bins[b1], 1u);
         }
-        const uint32_t cc = code_of(w);
-        const uint32_t f0 = first(cc), nsub = first(cc + 1u) - f0;
-        const uint32_t off = sbits ? (uint32_t)((sub_of(w) * nsub) >> sbits) : 0u;
-        return f0 + off;
-    };
-    for (uint32_t i = t; i < cnt; i += NT) atomicAdd(&bins[bin_of(a[i])], 1u);
+    }
     lds_sync();
     uint32_t big = scan_counts<NT, NB>(bins, nb, sh, rb);
     if (big > kMaxBin) {
@@ -962,25 +947,53 @@ QRITA_DEV bool bucket_sort(const uint64_t* a, uint32_t cnt, const RankOut& ro, u
         for (uint32_t i = t; i < cnt; i += NT) atomicAdd(&hc[code_of(a[i])], 1u);
         lds_sync();
         scan_counts<NT, NB>(hc, ncodes, sh, rb);
-        prop = true;
+        const float ratio = (float)nb / (float)cnt;
+        auto first = [&](uint32_t cc) {
+            if (cc >= ncodes) return nb;
+            const uint32_t f = (uint32_t)((float)hc[cc] * ratio);
+            return f < nb - 1u ? f : nb - 1u;
+        };
         for (uint32_t i = t; i <= nb; i += NT) bins[i] = 0u;
         lds_sync();
-        for (uint32_t i = t; i < cnt; i += NT) atomicAdd(&bins[bin_of(a[i])], 1u);
+        for (uint32_t i = t; i < cnt; i += NT) {
+            const uint64_t w = a[i];
+            const uint32_t cc = code_of(w);
+            const uint32_t f0 = first(cc), nsub = first(cc + 1u) - f0;
+            const uint32_t off = sbits ? (uint32_t)((sub_of(w) * nsub) >> sbits) : 0u;
+            binof[i] = (uint16_t)(f0 + off);
+            atomicAdd(&bins[f0 + off], 1u);
+        }
         lds_sync();
         big = scan_counts<NT, NB>(bins, nb, sh, rb);
         if (big > kMaxBin) return false;
     }
     // scatter the positions; afterwards bins[i] is the end of bin i
-    for (uint32_t i = t; i < cnt; i += NT) pos[atomicAdd(&bins[bin_of(a[i])], 1u)] = (uint16_t)i;
+    for (uint32_t i = t; i < cnt; i += 2 * NT) {
+        const uint32_t i1 = i + NT;
+        const uint32_t q0 = atomicAdd(&bins[binof[i]], 1u);
+        pos[q0] = (uint16_t)i;
+        if (i1 < cnt) {
+            const uint32_t q1 = atomicAdd(&bins[binof[i1]], 1u);
+            pos[q1] = (uint16_t)i1;
+        }
+    }
     lds_sync();
     // ranks, by position in the binned order: the lanes of a wave mostly
-    // share a bin, so their scans take the same number of steps
+    // share a bin, so their scans take the same number of steps; four bin
+    // mates per step (the word itself stands in past the bin's end)
     for (uint32_t p = t; p < cnt; p += NT) {
-        const uint64_t w = a[pos[p]];
-        const uint32_t bi = bin_of(w);
+        const uint32_t i = pos[p];
+        const uint64_t w = a[i];
+        const uint32_t bi = binof[i];
         const uint32_t s0 = bi ? bins[bi - 1] : 0u, e0 = bins[bi];
         uint32_t r = s0;
-        for (uint32_t q = s0; q < e0; ++q) r += a[pos[q]] > w ? 1u : 0u;
+        for (uint32_t q = s0; q < e0; q += 4) {
+            const uint32_t j0 = pos[q];
+            const uint32_t j1 = q + 1 < e0 ? pos[q + 1] : i;
+            const uint32_t j2 = q + 2 < e0 ? pos[q + 2] : i;
+            const uint32_t j3 = q + 3 < e0 ? pos[q + 3] : i;
+            r += (a[j0] > w ? 1u : 0u) + (a[j1] > w ? 1u : 0u) + (a[j2] > w ? 1u : 0u) + (a[j3] > w ? 1u : 0u);
+        }
         ro.put(r, w);
     }
     lds_sync();
@@ -992,10 +1005,11 @@ QRITA_DEV bool bucket_sort(const uint64_t* a, uint32_t cnt, const RankOut& ro, u
 // bitonic sort. The words stay in the first region (the bitonic sort permutes
 // them).
 template <class T>
-QRITA_DEV void sort_words(uint32_t cnt, RankOut ro, Shared& sh, int& rb) {
+QRITA_DEV void sort_words(uint32_t cnt, const SortExt& ex, RankOut ro, Shared& sh, int& rb) {
     constexpr int NT = T::NT;
     uint64_t* a = (uint64_t*)(dyn_lds() + T::SA_OFF);
     uint16_t* pos = (uint16_t*)(dyn_lds() + T::SB_OFF);
+    uint16_t* binof = (uint16_t*)(dyn_lds() + T::BO_OFF);
     uint32_t* bins = (uint32_t*)(dyn_lds() + T::BINS_OFF);
     uint32_t* hc = (uint32_t*)(dyn_lds() + T::HC_OFF);
     cnt = min(uni(cnt), (uint32_t)T::CSORT);  // more only for inputs outside the contract (NaN logits)
@@ -1004,7 +1018,7 @@ QRITA_DEV void sort_words(uint32_t cnt, RankOut ro, Shared& sh, int& rb) {
         rank_sort<NT>(a, cnt, ro, bins);
         return;
     }
-    if (bucket_sort<NT, T::NB>(a, cnt, ro, pos, bins, hc, sh, rb)) return;
+    if (bucket_sort<NT, T::NB>(a, cnt, ex, ro, pos, binof, bins, hc, sh, rb)) return;
     const uint32_t np = next_pow2(cnt);  // < 2 cnt: inside the fallback region
     for (uint32_t i = cnt + threadIdx.x; i < np; i += NT) a[i] = 0ull;
     lds_sync();
@@ -1016,14 +1030,18 @@ QRITA_DEV void sort_words(uint32_t cnt, RankOut ro, Shared& sh, int& rb) {
 // ---------------------------------------------------------------------------
 
 // Words c with lo_w <= c < hi_w from the source (with indices) into
-// a[0 .. ), reserved per wave in LDS; returns the count (uniform). At most
-// cap are written.
+// a[0 .. ), reserved per wave in LDS; returns the count (uniform; at most
+// cap are written) and the set's extents for the sort. The key of lo_w must
+// be one of the set's keys (the reference for the shared low bits).
 template <int NT, class L>
-QRITA_DEV uint32_t gather_words(const L& lsrc, uint64_t* a, uint32_t cap, uint64_t lo_w, uint64_t hi_w, Shared& sh) {
+QRITA_DEV uint32_t gather_words(const L& lsrc, uint64_t* a, uint32_t cap, uint64_t lo_w, uint64_t hi_w, SortExt& ex,
+                                Shared& sh, int& rb) {
     block_sync<NT>();
     if (threadIdx.x == 0) sh.gather_n = 0;
     lds_sync();
     const uint32_t lane = tid_here() & (kWave - 1);
+    const uint32_t key0 = cand_key(lo_w);
+    uint32_t kmn = 0xFFFFFFFFu, kmx = 0u, lmn = 0xFFFFFFFFu, lmx = 0u, tz = 32u;
     lsrc.visit([&](uint32_t key, uint32_t low) {
         const uint64_t w = ((uint64_t)key << 32) | low;
         const bool take = key != 0 && w >= lo_w && w < hi_w;
@@ -1033,9 +1051,20 @@ QRITA_DEV uint32_t gather_words(const L& lsrc, uint64_t* a, uint32_t cap, uint64
             if (lane == 0) r0 = atomicAdd(&sh.gather_n, (uint32_t)__popcll(b));
             const uint32_t pos = readlane(r0, 0) + lanes_below(b);
             if (take && pos < cap) a[pos] = w;
+            if (take) {
+                kmn = key < kmn ? key : kmn;
+                kmx = key > kmx ? key : kmx;
+                lmn = low < lmn ? low : lmn;
+                lmx = low > lmx ? low : lmx;
+                const uint32_t d = key ^ key0;
+                const uint32_t z = d ? (uint32_t)__builtin_ctz(d) : 32u;
+                tz = z < tz ? z : tz;
+            }
         }
     });
-    lds_sync();
+    uint32_t e[5] = {wave_min_u32(kmn), ~wave_max_u32(kmx), wave_min_u32(lmn), ~wave_max_u32(lmx), wave_min_u32(tz)};
+    comb_record<NT, 0, 0, 5>(nullptr, nullptr, e, sh, rb);  // its barrier also completes the gather
+    ex = SortExt{e[0], ~e[1], e[2], ~e[3], e[4]};
     return uni(sh.gather_n);
 }
 
@@ -1229,10 +1258,12 @@ QRITA_DEV void emit_row(C& c, const L& lsrc, const RowOut& o, bool all, uint32_t
     const bool same = Lout == 0 || (!all && Lout == L_);  // the index boundary is the kept set's boundary
     if (Gi <= (uint32_t)T::CSORT && same) {
         // one sort over every candidate at or above the boundary value
-        const uint32_t cnt = gather_words<NT>(lsrc, a, T::CSORT, (uint64_t)(Lout > 0 ? vo : vf) << 32, ~0ull, sh);
+        SortExt ex;
+        const uint32_t cnt =
+            gather_words<NT>(lsrc, a, T::CSORT, (uint64_t)(Lout > 0 ? vo : vf) << 32, ~0ull, ex, sh, c.rb);
         RankOut ro{o.idx, Lout, (mask && !o.bitmap) ? o.mrow : nullptr, mask ? L_ : 0u,
                    (mask && o.bitmap) ? (uint64_t*)&sh.u32[0] : nullptr};
-        sort_words<T>(cnt, ro, sh, c.rb);
+        sort_words<T>(cnt, ex, ro, sh, c.rb);
         if (mask && o.bitmap) {
             lds_sync();
             const uint64_t B = uni(*(const uint64_t*)&sh.u32[0]);
@@ -1247,8 +1278,9 @@ QRITA_DEV void emit_row(C& c, const L& lsrc, const RowOut& o, bool all, uint32_t
     }
     if (Lout == 0) return;
     if (Gi <= (uint32_t)T::CSORT) {
-        const uint32_t cnt = gather_words<NT>(lsrc, a, T::CSORT, (uint64_t)vo << 32, ~0ull, sh);
-        sort_words<T>(cnt, RankOut{o.idx, Lout, nullptr, 0u, nullptr}, sh, c.rb);
+        SortExt ex;
+        const uint32_t cnt = gather_words<NT>(lsrc, a, T::CSORT, (uint64_t)vo << 32, ~0ull, ex, sh, c.rb);
+        sort_words<T>(cnt, ex, RankOut{o.idx, Lout, nullptr, 0u, nullptr}, sh, c.rb);
         return;
     }
     // windows of CSORT ranks, each bounded by its own boundary word
@@ -1261,8 +1293,9 @@ QRITA_DEV void emit_row(C& c, const L& lsrc, const RowOut& o, bool all, uint32_t
             const CountOut r = search_count<NT, 0>(c, 0u, done + cnt, (int64_t)vo - 1, ngo + No, (int64_t)kmax, 0u);
             Bn = tie_boundary<T>(lsrc, r.v, done + cnt - r.n_gt, r.N, o.V, c.mode, sh, c.rb, dg.iters);
         }
-        const uint32_t got = gather_words<NT>(lsrc, a, T::CSORT, Bn, prev, sh);
-        sort_words<T>(got, RankOut{o.idx + done, cnt, nullptr, 0u, nullptr}, sh, c.rb);
+        SortExt ex;
+        const uint32_t got = gather_words<NT>(lsrc, a, T::CSORT, Bn, prev, ex, sh, c.rb);
+        sort_words<T>(got, ex, RankOut{o.idx + done, cnt, nullptr, 0u, nullptr}, sh, c.rb);
         prev = Bn;
         done += cnt;
     }
