@@ -59,7 +59,8 @@ typedef enum {
     QRITA_EINVAL = 1,      /* bad argument: nothing launched, nothing written */
     QRITA_EWORKSPACE = 2,  /* workspace NULL or smaller than qrita_workspace_bytes() */
     QRITA_ELAUNCH = 3,     /* the HIP runtime reported an error at launch */
-    QRITA_EUNSUPPORTED = 4 /* the current device cannot run this library */
+    QRITA_EUNSUPPORTED = 4, /* the current device cannot run this library */
+    QRITA_ESCRATCH = 5     /* qrita_select_noalloc: the shape needs more than its static scratch */
 } qrita_status_t;
 
 /*
@@ -164,6 +165,27 @@ int qrita_select_ex(const void* logits, int64_t batch, int64_t vocab, int dtype,
                     uint8_t* out_mask, int32_t* out_idx, int32_t* out_count, int64_t idx_cap,
                     void* workspace, size_t workspace_bytes, void* stream,
                     const qrita_options* opt);
+
+/*
+ * qrita_select for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same selection and outputs as qrita_select, with the workspace taken
+ * from a static device array of the library (QRITA_NOALLOC_SCRATCH_BYTES,
+ * one per GPU, held until the process ends) instead of a caller's buffer.
+ * Shapes whose qrita_workspace_bytes exceeds that size return
+ * QRITA_ESCRATCH before anything is launched. The call allocates nothing
+ * (no hipMalloc, no allocating library routine); its first call on a device
+ * looks up the array's device address once. All calls on one GPU share the
+ * array: calls that overlap in time on one GPU (other streams, other host
+ * threads) race and must be serialised by the caller. The array's contents
+ * left by one call never affect the next.
+ * Returns the codes of qrita_select, or QRITA_ESCRATCH.
+ */
+#define QRITA_NOALLOC_SCRATCH_BYTES (32 << 20)
+int qrita_select_noalloc(const void* logits, int64_t batch, int64_t vocab, int dtype,
+                         const int32_t* k, const float* p,
+                         uint8_t* out_mask, int32_t* out_idx, int32_t* out_count, int64_t idx_cap,
+                         void* stream);
 
 /* Static description of a status code. */
 const char* qrita_strerror(int status);

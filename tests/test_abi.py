@@ -22,7 +22,7 @@ def _declared_functions():
 
 def test_header_declares_the_api():
     names = _declared_functions()
-    assert names == ["qrita_select", "qrita_select_ex", "qrita_strerror",
+    assert names == ["qrita_select", "qrita_select_ex", "qrita_select_noalloc", "qrita_strerror",
                      "qrita_workspace_bytes"]
 
 
@@ -114,3 +114,14 @@ def test_product_path_has_no_cpu_fallback():
                     for m in mods:
                         assert not m.startswith("oracle"), (fn, m)
                         assert not m.startswith("workloads"), (fn, m)
+
+
+def test_noalloc_rejects_oversize_and_bad_arguments_before_launch():
+    lib = q.lib()
+    # 300 x 262144 needs more than the static scratch: refused before any HIP call
+    assert lib.qrita_select_noalloc(FAKE, 300, 262144, 1, None, None, None, None, FAKE + 4096, 0, None) == \
+        q.QRITA_ESCRATCH
+    assert lib.qrita_select_noalloc(None, 4, 100, 0, None, None, None, None, FAKE, 0, None) == q.QRITA_EINVAL
+    assert lib.qrita_select_noalloc(FAKE, 4, 100, 9, None, None, None, None, FAKE, 0, None) == q.QRITA_EINVAL
+    assert lib.qrita_select_noalloc(FAKE, 0, 100, 0, None, None, None, None, FAKE, 0, None) == q.QRITA_OK
+    assert "static scratch" in q.qrita_strerror(q.QRITA_ESCRATCH)

@@ -25,6 +25,8 @@ QRITA_EINVAL = 1
 QRITA_EWORKSPACE = 2
 QRITA_ELAUNCH = 3
 QRITA_EUNSUPPORTED = 4
+QRITA_ESCRATCH = 5
+NOALLOC_SCRATCH_BYTES = 32 << 20
 DIAG_FIELDS = 8
 DIAG_NAMES = ("t", "tc", "n_t", "n_cand", "path", "hit", "iters", "predicted")
 
@@ -93,6 +95,8 @@ def lib() -> ctypes.CDLL:
             L.qrita_select.argtypes = sel
             L.qrita_select_ex.restype = ctypes.c_int
             L.qrita_select_ex.argtypes = sel + [ctypes.POINTER(_Options)]
+            L.qrita_select_noalloc.restype = ctypes.c_int
+            L.qrita_select_noalloc.argtypes = [vp, i64, i64, ctypes.c_int, vp, vp, vp, vp, vp, i64, vp]
             L.qrita_strerror.restype = ctypes.c_char_p
             L.qrita_strerror.argtypes = [ctypes.c_int]
             _lib = L
@@ -151,6 +155,18 @@ def qrita_select_ex(logits, k, p, out_mask, out_idx, out_count, idx_cap: int, wo
         st = lib().qrita_select_ex(*args, ctypes.byref(opt))
     if st != QRITA_OK:
         raise QritaError(st, "qrita_select")
+
+
+def qrita_select_noalloc(logits, k, p, out_mask, out_idx, out_count, idx_cap: int, stream=None) -> None:
+    """Call ``qrita_select_noalloc`` (the library's static scratch as workspace)."""
+    if logits.dim() != 2 or not logits.is_contiguous():
+        raise ValueError("logits must be a contiguous [batch, vocab] tensor")
+    B, V = logits.shape
+    st = lib().qrita_select_noalloc(logits.data_ptr(), B, V, dtype_code(logits), _ptr(k), _ptr(p),
+                                    _ptr(out_mask), _ptr(out_idx), _ptr(out_count), int(idx_cap),
+                                    _stream_ptr(stream))
+    if st != QRITA_OK:
+        raise QritaError(st, "qrita_select_noalloc")
 
 
 _ws_cache = {}

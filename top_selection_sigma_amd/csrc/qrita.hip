@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <atomic>
 #include <cstring>
+#include <mutex>
 
 #include "launch.hpp"
 #include "qrita.h"
@@ -179,9 +180,54 @@ int select_impl(const void* logits, int64_t batch, int64_t vocab, int dtype, con
     return err == hipSuccess ? QRITA_OK : QRITA_ELAUNCH;
 }
 
+// Static device scratch for qrita_select_noalloc: the workspace of callers
+// that cannot allocate. Every GPU the library runs on holds its own copy
+// until the process ends; its contents never matter to a call (every word a
+// call reads is written earlier in the same call).
+static __device__ __align__(256) unsigned char scratch[QRITA_NOALLOC_SCRATCH_BYTES];
+
+// The array's device address, looked up once per device with that device
+// current (in host code the array's name is only a host-side stand-in).
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+std::once_flag g_scratch_once[kMaxDevices];
+
+int scratch_for_current_device(void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return QRITA_EUNSUPPORTED;
+    std::call_once(g_scratch_once[dev], [dev] {
+        void* ptr = nullptr;
+        g_scratch_err[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? ptr : nullptr;
+    });
+    if (g_scratch_err[dev] != hipSuccess || !g_scratch_ptr[dev]) return QRITA_ELAUNCH;
+    *out = g_scratch_ptr[dev];
+    return QRITA_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int qrita_select_noalloc(const void* logits, int64_t batch, int64_t vocab, int dtype, const int32_t* k,
+                         const float* p, uint8_t* out_mask, int32_t* out_idx, int32_t* out_count,
+                         int64_t idx_cap, void* stream) {
+    // shape and argument checks first (nothing touches the GPU before them)
+    if (!logits || batch < 0 || vocab <= 0 || vocab > INT32_MAX || idx_cap < 0 || idx_cap > INT32_MAX)
+        return QRITA_EINVAL;
+    if (dtype != QRITA_F32 && dtype != QRITA_BF16) return QRITA_EINVAL;
+    if (batch == 0) return QRITA_OK;
+    if (qrita_workspace_bytes(batch, vocab, dtype, idx_cap) > (size_t)QRITA_NOALLOC_SCRATCH_BYTES)
+        return QRITA_ESCRATCH;
+    if (!out_mask && !out_idx && !out_count) return QRITA_EINVAL;
+    if (out_idx && !out_count) return QRITA_EINVAL;
+    if (!device_supported()) return QRITA_EUNSUPPORTED;
+    void* ws = nullptr;
+    const int st = scratch_for_current_device(&ws);
+    if (st != QRITA_OK) return st;
+    return select_impl(logits, batch, vocab, dtype, k, p, out_mask, out_idx, out_count, idx_cap, ws,
+                       (size_t)QRITA_NOALLOC_SCRATCH_BYTES, stream, nullptr);
+}
 
 size_t qrita_workspace_bytes(int64_t batch, int64_t vocab, int dtype, int64_t idx_cap) {
     (void)idx_cap;
@@ -217,6 +263,7 @@ const char* qrita_strerror(int status) {
         case QRITA_EWORKSPACE: return "workspace missing, misaligned or too small";
         case QRITA_ELAUNCH: return "kernel launch failed";
         case QRITA_EUNSUPPORTED: return "unsupported device (the library is built for gfx950)";
+        case QRITA_ESCRATCH: return "problem larger than the static scratch of qrita_select_noalloc";
         default: return "unknown status";
     }
 }
