@@ -1,0 +1,214 @@
+"""GPU parity of every tail path and option, through the C ABI, against the oracle.
+
+Each test names the path it drives: the two tail tiers, the whole-row bitmap
+mask (with unaligned and odd-length rows) and the byte-scattered mask, the
+three pivot placements (key quartiles, value quartiles, one pivot), windowed
+index output for kept sets larger than one sort, workspaces left dirty by other
+calls or filled with garbage, and calls on two streams.
+"""
+import numpy as np
+import pytest
+
+import workloads as w
+from parity import check, oracle_for, run_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+KINDS = ["gauss", "gauss_outliers", "ties16", "uniform", "heavy", "equal", "twolevel", "smallint",
+         "neginf", "allneginf", "zeros", "ascending", "descending", "spike", "flat"]
+
+
+@pytest.mark.parametrize("tier", [1, 2])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_forced_tiers_all_kinds(tier, dtype):
+    """Light (1) and heavy (2) tail tiers on the same rows as the default tier."""
+    import top_selection_sigma_amd as q
+
+    for i, kind in enumerate(KINDS):
+        x = w.make_rows(6, 7001, dtype, kind, seed=900 + i)
+        _say(f"tier {tier} {kind} {dtype}")
+        g = run_gpu(x, 400, options=q.Options(tier=tier))
+        check(x, g, oracle_for(x, 400), 400, f"tier {tier} {kind} {dtype}")
+
+
+@pytest.mark.parametrize("V", [3001, 4099, 20000])
+@pytest.mark.parametrize("tier", [1, 2])
+def test_bitmap_mask_rows(V, tier):
+    """512 rows switch the mask to whole-row writes from an LDS bitmap; odd V makes
+    every other row start unaligned (head and tail bytes around 16-byte stores)."""
+    import top_selection_sigma_amd as q
+
+    x = w.make_rows(512, V, "bf16", "gauss_outliers", seed=V + tier)
+    _say(f"bitmap V={V} tier {tier}")
+    g = run_gpu(x, 64, options=q.Options(tier=tier))
+    check(x, g, oracle_for(x, 64), 64, f"bitmap V={V} tier {tier}")
+
+
+@pytest.mark.parametrize("kind", ["ties16", "smallint", "neginf", "equal"])
+def test_bitmap_and_scattered_masks_agree_with_oracle(kind):
+    """The same 512-row batch with the bitmap mask and with byte-scattered masks
+    (pass 1 zero-fills, the tail stores the kept bytes)."""
+    import top_selection_sigma_amd as q
+
+    x = w.make_rows(512, 2500, "f32", kind, seed=31)
+    ref = oracle_for(x, 100)
+    for mode in (0, 1):
+        _say(f"mask mode {mode} {kind}")
+        g = run_gpu(x, 100, options=q.Options(mask_mode=mode))
+        check(x, g, ref, 100, f"mask mode {mode} {kind}")
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
+@pytest.mark.parametrize("kind,dtype", [("ties16", "bf16"), ("gauss_outliers", "bf16"), ("uniform", "f32"),
+                                        ("heavy", "bf16"), ("smallint", "f32")])
+def test_pivot_modes_match_oracle(mode, kind, dtype):
+    """Key quartiles (0), value quartiles (1) and a single key midpoint (2, the
+    binary search) all reach the oracle's result."""
+    import top_selection_sigma_amd as q
+
+    x = w.make_rows(8, 30000, dtype, kind, seed=12 + mode)
+    g = run_gpu(x, 300, options=q.Options(pivot_mode=mode))
+    check(x, g, oracle_for(x, 300), 300, f"pivot mode {mode} {kind}")
+
+
+@pytest.mark.parametrize("mode", [0, 2])
+def test_pivot_modes_on_truncation_misses(mode):
+    """The fallback search over the full row with quaternary and binary pivots."""
+    import top_selection_sigma_amd as q
+
+    x = w.make_rows(4, 20000, "f32", "uniform", seed=44, k=3000, p=1.0)
+    g = run_gpu(x, 3000, options=q.Options(pivot_mode=mode, force_miss=True))
+    check(x, g, oracle_for(x, 3000), 3000, f"miss pivot mode {mode}")
+    assert np.all(g.diag[:, 4] >= 2)
+
+
+def test_nan_p_turns_top_p_off():
+    x = w.make_rows(8, 5000, "bf16", "gauss_outliers", seed=71)
+    x.p[:] = np.float32("nan")
+    x.k[:] = np.array([0, 1, 10, 100, 0, 4999, 5000, 37], np.int32)
+    g = run_gpu(x, 200)
+    ref = oracle_for(x, 200)
+    check(x, g, ref, 200, "nan p")
+    K = np.where((x.k <= 0) | (x.k >= 5000), 5000, x.k)
+    assert np.array_equal(g.count, K)
+
+
+def test_mask_only_and_idx_only():
+    x = w.make_rows(6, 3000, "bf16", "gauss", seed=17)
+    ref = oracle_for(x, 50)
+    g = run_gpu(x, 0, want_mask=True, want_idx=False)
+    check(x, g, ref, 0, "mask only")
+    g = run_gpu(x, 50, want_mask=False, want_idx=True)
+    check(x, g, ref, 50, "idx only")
+
+
+@pytest.mark.parametrize("tier", [1, 2])
+def test_windowed_index_output(tier):
+    """Kept sets larger than one sort (4096 light, 8704 heavy) with heavy ties at
+    the boundary: the indices come out in rank windows, each with its own tie
+    boundary."""
+    import top_selection_sigma_amd as q
+
+    x = w.make_rows(3, 40000, "f32", "smallint", seed=5, k=np.array([10000, 20000, 25000]), p=1.0)
+    cap = 22000
+    g = run_gpu(x, cap, options=q.Options(tier=tier))
+    check(x, g, oracle_for(x, cap), cap, f"windows tier {tier}")
+
+
+def test_workspace_left_dirty_by_a_smaller_batch():
+    """A call on 9 rows of 17 logits, then one on 17 rows of top-p-only rows on
+    the same workspace: nothing an earlier call wrote is read by a later one."""
+    import torch
+
+    import top_selection_sigma_amd as q
+
+    dev = torch.device("cuda", 0)
+    ws = torch.empty(q.qrita_workspace_bytes(17, 64, q.QRITA_F32, 17), dtype=torch.uint8, device=dev)
+    a = w.make_rows(9, 17, "f32", "gauss", seed=1, p=1.0)
+    a.k[1] = 1
+    b = w.make_rows(17, 64, "f32", "gauss_outliers", seed=2, k=0, p=0.9)
+    for x in (a, b):
+        logits = torch.from_numpy(x.logits).to(dev)
+        k = torch.from_numpy(x.k).to(dev)
+        p = torch.from_numpy(x.p).to(dev)
+        B, V = x.batch, x.vocab
+        mask = torch.empty((B, V), dtype=torch.uint8, device=dev)
+        idx = torch.empty((B, 17), dtype=torch.int32, device=dev)
+        cnt = torch.empty(B, dtype=torch.int32, device=dev)
+        diag = torch.zeros((B, q.DIAG_FIELDS), dtype=torch.int32, device=dev)
+        q.qrita_select_ex(logits, k, p, mask, idx, cnt, 17, ws, None, q.Options(diag=diag))
+        torch.cuda.synchronize()
+        from parity import GpuOut
+
+        g = GpuOut(mask.cpu().numpy(), idx.cpu().numpy(), cnt.cpu().numpy(), diag.cpu().numpy())
+        check(x, g, oracle_for(x, 17), 17, f"dirty workspace {B}x{V}")
+        assert np.all(g.diag[:, 4] <= 1)
+
+
+def test_workspace_filled_with_garbage():
+    """Every word a call reads from the workspace is written earlier in the call."""
+    import torch
+
+    import top_selection_sigma_amd as q
+
+    dev = torch.device("cuda", 0)
+    x = w.make_rows(40, 20000, "bf16", "ties16", seed=3)
+    for fill in (0x00, 0xFF, 0x5A):
+        ws = torch.full((q.qrita_workspace_bytes(40, 20000, q.QRITA_BF16, 100),), fill, dtype=torch.uint8,
+                        device=dev)
+        logits = torch.from_numpy(x.logits.view(np.int16)).to(dev).view(torch.bfloat16)
+        k = torch.from_numpy(x.k).to(dev)
+        p = torch.from_numpy(x.p).to(dev)
+        mask = torch.empty((40, 20000), dtype=torch.uint8, device=dev)
+        idx = torch.empty((40, 100), dtype=torch.int32, device=dev)
+        cnt = torch.empty(40, dtype=torch.int32, device=dev)
+        q.qrita_select(logits, k, p, mask, idx, cnt, 100, ws)
+        torch.cuda.synchronize()
+        from parity import GpuOut
+
+        g = GpuOut(mask.cpu().numpy(), idx.cpu().numpy(), cnt.cpu().numpy(), None)
+        check(x, g, oracle_for(x, 100), 100, f"garbage 0x{fill:02x}")
+
+
+def test_two_streams_ten_calls_each_are_identical():
+    """Two streams, each with its own workspace and outputs, ten calls each,
+    interleaved: every output is byte-identical to the others and to the oracle
+    (the selection is deterministic; the pages require it)."""
+    import torch
+
+    import top_selection_sigma_amd as q
+
+    dev = torch.device("cuda", 0)
+    x = w.make_rows(64, 50000, "bf16", "ties16", seed=19)
+    logits = torch.from_numpy(x.logits.view(np.int16)).to(dev).view(torch.bfloat16)
+    k = torch.from_numpy(x.k).to(dev)
+    p = torch.from_numpy(x.p).to(dev)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev)]
+    outs = []
+    for i in range(10):
+        for s in streams:
+            m, ix, c = q.select(logits, k, p, idx_cap=256, stream=s)
+            outs.append((m, ix, c))
+    torch.cuda.synchronize()
+    ref = oracle_for(x, 256)
+    first = None
+    from parity import GpuOut
+
+    for m, ix, c in outs:
+        g = GpuOut(m.cpu().numpy(), ix.cpu().numpy(), c.cpu().numpy(), None)
+        if first is None:
+            first = g
+            check(x, g, ref, 256, "two streams")
+        else:
+            assert np.array_equal(g.mask, first.mask)
+            assert np.array_equal(g.count, first.count)
+            for r in range(x.batch):
+                n = min(int(g.count[r]), 256)
+                assert np.array_equal(g.idx[r, :n], first.idx[r, :n])
+    assert len(q._ws_cache) >= 2
