@@ -2,16 +2,26 @@
 
 One step = one qrita_select call over one batch of a named synthetic workload
 (both kernels of the path: the streaming truncation pass and the per-row
-tail). The headline line is the 64 x 128256 bf16 workload; the other
-bandwidth workloads are reported in "per_config".
+tail). The headline is the largest workload, 1024 x 201088 float32 logits
+(U(-1,1), k = 4096); the other four named workloads are reported in
+"per_config" (the single 32000-logit row as a latency, with the oracle's
+seconds).
 
-Timing: W warmup steps, then K steps between two HIP events on the stream the
-library launches on, after a device synchronize. Inputs rotate over enough
-buffer sets to keep the footprint above 1 GiB so the 256 MiB Infinity Cache
-cannot serve them. A second loop with an event between the two kernels gives
-each kernel's average duration (the roofline numbers). The outputs of the
-last timed call are checked against the CPU oracle, which is then timed on a
-bounded sample of the same workload as the CPU baseline.
+Timing: W warm-up calls, then K calls between two HIP events on the stream the
+library launches on. Inputs rotate over enough buffer sets to keep the
+footprint above 1 GiB (at most 256 sets), so the 256 MiB Infinity Cache cannot
+serve them. A second loop records an event between the two kernels of every
+call (qrita_options.mid_event, recorded by the library on its stream) for each
+kernel's average duration: the roofline of the dominant kernel uses it. The
+outputs of every timed configuration, ablation legs included, are checked
+against the CPU oracle, which is then timed on the headline workload as the
+CPU baseline.
+
+Ablations (the pages' "Estudios de Ablación", reproduced on these shapes):
+truncation off (every row takes the full-row search), binary vs quaternary
+pivots on truncation hits and misses, duplicate handling (rows on a 1/16 grid
+vs the same distribution in distinct float32 values), and one fixed tier vs
+the tier table.
 """
 import argparse
 import hashlib
@@ -27,40 +37,58 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
-KERNEL_SOURCES = ("top_selection_sigma_amd/csrc/select_kernel.hpp", "top_selection_sigma_amd/csrc/device_common.hpp",
-                  "top_selection_sigma_amd/csrc/qrita.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pass1_traffic.json")
+METRIC = "rows/sec and effective HBM GB/s (% of peak) for exact top-k/top-p masks"
+HEADLINE = 3
+KERNEL_SOURCES = {
+    "pass1": ("top_selection_sigma_amd/csrc/select_kernel.hpp", "top_selection_sigma_amd/csrc/device_common.hpp",
+              "top_selection_sigma_amd/csrc/params.hpp", "top_selection_sigma_amd/csrc/pass1.hip"),
+    "tail": ("top_selection_sigma_amd/csrc/tail_kernel.hpp", "top_selection_sigma_amd/csrc/select_kernel.hpp",
+             "top_selection_sigma_amd/csrc/device_common.hpp", "top_selection_sigma_amd/csrc/params.hpp",
+             "top_selection_sigma_amd/csrc/tail_light.hip", "top_selection_sigma_amd/csrc/tail_heavy.hip"),
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+MAX_SETS = 256
 
 
-def kernel_source_digest():
-    """sha256 over the pass-1 kernel's sources (the tail lives in its own
-    file): counter readings taken on other sources do not describe this
-    build."""
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_digest(kernel):
+    """sha256 over a kernel's sources: counter readings taken on other sources
+    do not describe this build."""
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def measured_traffic(workload):
-    """HBM bytes per pass-1 launch from the rocprofv3 FETCH_SIZE/WRITE_SIZE
-    readings recorded in profiles/pass1_traffic.json (already scaled by the
-    copy-kernel factor), or None when absent or taken on other sources."""
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the rocprofv3 FETCH_SIZE/WRITE_SIZE
+    readings in profiles/hbm_traffic.json (already scaled by the copy-kernel
+    factors), or None when absent or taken on other sources."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    ent = rec.get("workloads", {}).get(workload)
-    if not ent or rec.get("kernel_sha256") != kernel_source_digest():
+    ent = rec.get("kernels", {}).get(kernel, {})
+    if ent.get("sha256") != source_digest(kernel):
         return None
-    return ent.get("hbm_bytes_per_launch")
-METRIC = "rows/sec and effective HBM GB/s (% of peak) for exact top-k/top-p masks"
+    w = ent.get("workloads", {}).get(workload)
+    return None if w is None else w.get("hbm_bytes_per_launch")
 
 
-def log(msg):
-    print(msg, file=sys.stderr, flush=True)
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def to_device(x, dev):
@@ -71,105 +99,97 @@ def to_device(x, dev):
     return torch.from_numpy(x.logits).to(dev)
 
 
-def bench_config(index, steps, warmup, rotate_bytes):
-    import torch
+class Runner:
+    """Device buffers of one workload (rotated copies of the inputs and outputs)."""
 
-    import top_selection_sigma_amd as q
-    import workloads as w
+    def __init__(self, x, rotate_bytes):
+        import torch
 
-    dev = torch.device("cuda", 0)
-    t0 = time.time()
-    x = w.make_config(index)
-    log(f"[bench] workload {index} {x.name}: generated in {time.time() - t0:.1f}s")
-    B, V = x.batch, x.vocab
-    es = 2 if x.dtype == "bf16" else 4
-    idx_cap = int(max(64, x.k.max()))
-    logits0 = to_device(x, dev)
-    k = torch.from_numpy(x.k).to(dev)
-    p = torch.from_numpy(x.p).to(dev)
-    set_bytes = B * V * (es + 1) + B * idx_cap * 4
-    nsets = max(2, math.ceil(rotate_bytes / set_bytes))
-    sets = []
-    for i in range(nsets):
-        lg = logits0 if i == 0 else logits0.clone()
-        sets.append((lg, torch.empty((B, V), dtype=torch.uint8, device=dev),
-                     torch.empty((B, idx_cap), dtype=torch.int32, device=dev),
-                     torch.empty(B, dtype=torch.int32, device=dev)))
-    ws = q.workspace_for(B, V, q.dtype_code(logits0), idx_cap, dev)
-    stream = torch.cuda.current_stream()
+        import top_selection_sigma_amd as q
 
-    def step(i, opts=None):
-        lg, m, ix, c = sets[i % nsets]
-        q.qrita_select_ex(lg, k, p, m, ix, c, idx_cap, ws, stream, opts)
+        self.q = q
+        self.x = x
+        self.dev = torch.device("cuda", 0)
+        B, V = x.batch, x.vocab
+        self.es = 2 if x.dtype == "bf16" else 4
+        self.idx_cap = int(max(64, x.k.max()))
+        logits0 = to_device(x, self.dev)
+        self.k = torch.from_numpy(x.k).to(self.dev)
+        self.p = torch.from_numpy(x.p).to(self.dev)
+        set_bytes = B * V * (self.es + 1) + B * self.idx_cap * 4
+        self.nsets = max(2, min(MAX_SETS, math.ceil(rotate_bytes / set_bytes)))
+        self.sets = []
+        for i in range(self.nsets):
+            lg = logits0 if i == 0 else logits0.clone()
+            self.sets.append((lg, torch.empty((B, V), dtype=torch.uint8, device=self.dev),
+                              torch.empty((B, self.idx_cap), dtype=torch.int32, device=self.dev),
+                              torch.empty(B, dtype=torch.int32, device=self.dev)))
+        self.code = q.dtype_code(logits0)
+        self.ws = q.workspace_for(B, V, self.code, self.idx_cap, self.dev)
+        self.stream = torch.cuda.current_stream()
+        self.last = 0
 
-    for i in range(warmup):
-        step(i)
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for i in range(steps):
-        step(warmup + i)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    total_ms = ev0.elapsed_time(ev1)
-    last = (warmup + steps - 1) % nsets
+    def step(self, i, opts=None):
+        lg, m, ix, c = self.sets[i % self.nsets]
+        self.q.qrita_select_ex(lg, self.k, self.p, m, ix, c, self.idx_cap, self.ws, self.stream, opts)
+        self.last = i % self.nsets
 
-    # per-kernel durations: an event between the two launches of every call
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    mids = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    for e in mids:
-        e.record(stream)  # create the underlying hipEvent before handing it over
-    torch.cuda.synchronize()
-    for i in range(steps):
-        starts[i].record(stream)
-        step(i, q.Options(mid_event=mids[i]))
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    pass1_ms = float(np.mean([s.elapsed_time(m) for s, m in zip(starts, mids)]))
-    tail_ms = float(np.mean([m.elapsed_time(e) for m, e in zip(mids, ends)]))
-    per_step = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+    def time(self, steps, warmup, opts=None):
+        """Mean ms per call, per-kernel means (ms) and p10/p50/p90 per call."""
+        import torch
 
-    # truncation outcome per row (one extra call with diagnostics)
-    diag = torch.zeros(B * q.DIAG_FIELDS, dtype=torch.int32, device=dev)
-    step(0, q.Options(diag=diag))
-    torch.cuda.synchronize()
-    dg = diag.cpu().numpy().reshape(B, q.DIAG_FIELDS)
-    path = dg[:, 4]
+        q = self.q
+        for i in range(warmup):
+            self.step(i, q.Options(**opts) if opts else None)
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(self.stream)
+        for i in range(steps):
+            self.step(warmup + i, q.Options(**opts) if opts else None)
+        ev1.record(self.stream)
+        torch.cuda.synchronize()
+        total_ms = ev0.elapsed_time(ev1) / steps
+        # per-kernel durations: the library records mid on its stream between the launches
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        mids = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        for e in mids:
+            e.record(self.stream)  # create the underlying hipEvent before handing it over
+        torch.cuda.synchronize()
+        for i in range(steps):
+            starts[i].record(self.stream)
+            o = dict(opts or {})
+            o["mid_event"] = mids[i]
+            self.step(i, q.Options(**o))
+            ends[i].record(self.stream)
+        torch.cuda.synchronize()
+        p1 = float(np.mean([s.elapsed_time(m) for s, m in zip(starts, mids)]))
+        tl = float(np.mean([m.elapsed_time(e) for m, e in zip(mids, ends)]))
+        per = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+        return dict(ms_per_step=total_ms, pass1_ms=p1, tail_ms=tl,
+                    step_ms_p10_p50_p90=[float(np.percentile(per, v)) for v in (10, 50, 90)])
 
-    res = dict(index=index, name=x.name, batch=B, vocab=V, dtype=x.dtype, steps=steps,
-               warmup=warmup, rotation_sets=nsets, ms_per_step=total_ms / steps,
-               pass1_ms=pass1_ms, tail_ms=tail_ms,
-               step_ms_p10_p50_p90=[float(np.percentile(per_step, q_)) for q_ in (10, 50, 90)],
-               rows_single_pass=int(np.sum(path <= 1)), rows_miss_predicted=int(np.sum(dg[:, 7] == 1)),
-               rows_recollected=int(np.sum(path == 2)), rows_full_row=int(np.sum(path == 3)),
-               gaussian_t_hit_rows=int(np.sum(dg[:, 5] == 1)),
-               workspace_bytes=int(q.qrita_workspace_bytes(B, V, q.dtype_code(logits0), idx_cap)),
-               sort_based_bytes=int(B * V * (es + 4) * 2))
-    lg, m, ix, c = sets[last]
-    count = c.cpu().numpy()
-    kept_idx = np.minimum(count, idx_cap).astype(np.int64).sum()
-    eff_bytes = B * V * es + B * V + 4 * kept_idx + 4 * B
-    sec = res["ms_per_step"] * 1e-3
-    res["rows_per_s"] = B / sec
-    res["effective_gbps"] = eff_bytes / sec / 1e9
-    res["pct_peak_hbm"] = 100.0 * res["effective_gbps"] / PEAK_HBM_GBS
-    res["pass1_alg_bytes"] = B * V * (es + 1)
-    res["pass1_gbps"] = res["pass1_alg_bytes"] / (pass1_ms * 1e-3) / 1e9
-    res["mean_count"] = float(count.mean())
-    res["_inputs"] = x
-    res["_gpu"] = (m.cpu().numpy(), ix.cpu().numpy(), count, idx_cap)
-    return res
+    def outputs(self):
+        lg, m, ix, c = self.sets[self.last]
+        return m.cpu().numpy(), ix.cpu().numpy(), c.cpu().numpy()
+
+    def diag(self, opts=None):
+        import torch
+
+        q = self.q
+        d = torch.zeros(self.x.batch * q.DIAG_FIELDS, dtype=torch.int32, device=self.dev)
+        o = dict(opts or {})
+        o["diag"] = d
+        self.step(0, q.Options(**o))
+        torch.cuda.synchronize()
+        return d.cpu().numpy().reshape(self.x.batch, q.DIAG_FIELDS)
 
 
-def oracle_leg(res):
-    """CPU oracle on the same host arrays: checks the last timed call's outputs."""
+def parity(x, ref, outs, idx_cap):
+    """Rows that differ from the oracle (band rows: a rank prefix of the right length)."""
     import oracle
 
-    x = res["_inputs"]
-    mask, idx, count, idx_cap = res["_gpu"]
-    t1 = time.time()
-    ref = oracle.select(x.logits, x.dtype, x.k, x.p, idx_cap)
+    mask, idx, count = outs
     band = ref.band_lo != ref.band_hi
     bad = np.zeros(x.batch, bool)
     bad |= ~band & (count != ref.count)
@@ -180,12 +200,144 @@ def oracle_leg(res):
             bad[b] = True
         if band[b] and not (ref.band_lo[b] <= count[b] <= ref.band_hi[b]):
             bad[b] = True
-    res["parity"] = dict(mismatch_rows=int(bad.sum()), band_rows=int(band.sum()),
-                         oracle_s=round(time.time() - t1, 2))
-    log(f"[bench] {x.name}: parity mismatches {int(bad.sum())}, band rows {int(band.sum())}")
+    brows = np.nonzero(band)[0]
+    if len(brows):
+        sub = x.take_rows(brows)
+        full = oracle.select(sub.logits, sub.dtype, sub.k, sub.p, int(max(ref.band_hi[brows].max(), 1)),
+                             want_mask=False)
+        for j, b in enumerate(brows):
+            c = int(count[b])
+            m = np.zeros(x.vocab, np.uint8)
+            m[full.idx[j, :c]] = 1
+            if not np.array_equal(mask[b], m) or not np.array_equal(idx[b, :min(c, idx_cap)],
+                                                                    full.idx[j, :min(c, idx_cap)]):
+                bad[b] = True
+    return dict(mismatch_rows=int(bad.sum()), band_rows=int(band.sum()))
 
 
-def cpu_baseline(x, idx_cap, target_s=10.0):
+def effective_bytes(x, count, idx_cap):
+    es = 2 if x.dtype == "bf16" else 4
+    kept = np.minimum(count, idx_cap).astype(np.int64).sum()
+    return int(x.batch * x.vocab * es + x.batch * x.vocab + 4 * kept + 4 * x.batch)
+
+
+def roofline_for(name, x, t, count, idx_cap, bitmap):
+    """The dominant kernel's roofline: its algorithmic bytes per launch over its
+    average duration. Pass 1 reads every logit once (and writes the mask bytes
+    unless the tail writes whole mask rows); the tail writes the indices, the
+    counts and, with whole-row masks, the mask."""
+    B, V = x.batch, x.vocab
+    es = 2 if x.dtype == "bf16" else 4
+    kept = int(np.minimum(count, idx_cap).astype(np.int64).sum())
+    p1_bytes = B * V * es + (0 if bitmap else B * V)
+    tail_bytes = 4 * kept + 4 * B + (B * V if bitmap else 0)
+    dom = "pass1" if t["pass1_ms"] >= t["tail_ms"] else "tail"
+    ms = t["pass1_ms"] if dom == "pass1" else t["tail_ms"]
+    alg = p1_bytes if dom == "pass1" else tail_bytes
+    ach = alg / (ms * 1e-3) / 1e9
+    return {"kernel": "pass1_kernel" if dom == "pass1" else "tail_kernel", "bound": "hbm",
+            "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
+            "traffic": measured_traffic(name, dom), "alg_bytes_per_launch": alg,
+            "pass1_us": round(t["pass1_ms"] * 1e3, 2), "tail_us": round(t["tail_ms"] * 1e3, 2),
+            "pass1_alg_bytes": p1_bytes, "tail_alg_bytes": tail_bytes}
+
+
+def bench_workload(index, steps, warmup, rotate_bytes, check, ablate):
+    import oracle
+    import workloads as w
+
+    t0 = time.time()
+    x = w.make_config(index)
+    log(f"[bench] workload {index} {x.name}: generated in {time.time() - t0:.1f}s")
+    r = Runner(x, rotate_bytes)
+    t = r.time(steps, warmup)
+    outs = r.outputs()
+    dg = r.diag()
+    res = dict(index=index, name=x.name, batch=x.batch, vocab=x.vocab, dtype=x.dtype,
+               rotation_sets=r.nsets, **{k: v for k, v in t.items()})
+    count = outs[2]
+    eff = effective_bytes(x, count, r.idx_cap)
+    sec = t["ms_per_step"] * 1e-3
+    res.update(rows_per_s=x.batch / sec, effective_gbps=eff / sec / 1e9,
+               pct_peak_hbm=100.0 * eff / sec / 1e9 / PEAK_HBM_GBS, effective_bytes=eff,
+               mean_count=float(count.mean()))
+    bitmap = x.batch >= 512  # the tier table's whole-row mask rule (the rows here fit every bitmap)
+    res["roofline"] = roofline_for(x.name, x, t, count, r.idx_cap, bitmap)
+    path = dg[:, 4]
+    res["truncation"] = dict(rows=x.batch, single_pass=int(np.sum(path <= 1)),
+                             miss_predicted=int(np.sum(dg[:, 7] == 1)), recollected=int(np.sum(path == 2)),
+                             full_row=int(np.sum(path == 3)), gaussian_t_hit=int(np.sum(dg[:, 5] == 1)),
+                             mean_iterations=float(dg[:, 6].mean()))
+    es = 2 if x.dtype == "bf16" else 4
+    out_bytes = x.batch * x.vocab + x.batch * r.idx_cap * 4 + x.batch * 4
+    res["memory"] = dict(workspace_bytes=int(r.q.qrita_workspace_bytes(x.batch, x.vocab, r.code, r.idx_cap)),
+                         output_bytes=out_bytes,
+                         sort_based_bytes=int(2 * x.batch * x.vocab * (es + 4)) + out_bytes)
+    res["memory"]["ratio"] = round((res["memory"]["workspace_bytes"] + out_bytes) / res["memory"]["sort_based_bytes"],
+                                   4)
+    ref = None
+    if check:
+        t1 = time.time()
+        ref = oracle.select(x.logits, x.dtype, x.k, x.p, r.idx_cap)
+        res["oracle_s"] = round(time.time() - t1, 3)
+        res["parity"] = parity(x, ref, outs, r.idx_cap)
+        log(f"[bench] {x.name}: {t['ms_per_step'] * 1e3:.1f} us/call, parity mismatches "
+            f"{res['parity']['mismatch_rows']}, band rows {res['parity']['band_rows']}")
+    if ablate:
+        res["ablations"] = ablations(index, r, ref, steps, warmup, t)
+    return res, x, r
+
+
+def leg(r, ref, steps, warmup, opts):
+    t = r.time(max(5, steps // 2), max(2, warmup // 2), opts)
+    out = dict(us_per_call=round(t["ms_per_step"] * 1e3, 2), pass1_us=round(t["pass1_ms"] * 1e3, 2),
+               tail_us=round(t["tail_ms"] * 1e3, 2))
+    if ref is not None:
+        out["parity"] = parity(r.x, ref, r.outputs(), r.idx_cap)["mismatch_rows"]
+    return out
+
+
+def ablations(index, r, ref, steps, warmup, base):
+    """The ablation legs on this workload (each parity-checked against the oracle)."""
+    a = {"default_us": round(base["ms_per_step"] * 1e3, 2)}
+    if index in (1, 2, 4):
+        # truncation off: no survivors in pass 1, every row searches its full row
+        a["truncation_off"] = leg(r, ref, steps, warmup, dict(force_miss=True))
+    if index in (1, 2, 3, 4):
+        # one pivot per step (binary) instead of three, same duplicate tracking
+        a["binary_pivots"] = leg(r, ref, steps, warmup, dict(pivot_mode=2))
+    if index in (1, 2):
+        a["binary_pivots_on_misses"] = leg(r, ref, steps, warmup, dict(pivot_mode=2, force_miss=True))
+        a["quaternary_pivots_on_misses"] = a.get("truncation_off")
+    if index in (1, 2, 3, 4):
+        a["light_tier_only"] = leg(r, ref, steps, warmup, dict(tier=1))
+        a["heavy_tier_only"] = leg(r, ref, steps, warmup, dict(tier=2))
+        a["one_slice_per_row"] = leg(r, ref, steps, warmup, dict(slices=1))
+    return a
+
+
+def duplicate_ablation(steps, warmup, rotate_bytes, check):
+    """Duplicate handling: the 256 x 151936 shape (k = 50, p = 0.95) in float32,
+    rows on the 1/16 grid (heavy ties, including at the k boundary) vs the same
+    normal distribution unquantised (distinct values)."""
+    import oracle
+    import workloads as w
+
+    out = {}
+    for kind in ("ties16", "gauss2"):
+        x = w.make_rows(256, 151936, "f32", kind, seed=1002, k=50, p=0.95)
+        r = Runner(x, rotate_bytes)
+        t = r.time(steps, warmup)
+        ent = dict(us_per_call=round(t["ms_per_step"] * 1e3, 2), pass1_us=round(t["pass1_ms"] * 1e3, 2),
+                   tail_us=round(t["tail_ms"] * 1e3, 2))
+        if check:
+            ref = oracle.select(x.logits, x.dtype, x.k, x.p, r.idx_cap)
+            ent["parity"] = parity(x, ref, r.outputs(), r.idx_cap)["mismatch_rows"]
+        out["tied_rows" if kind == "ties16" else "distinct_rows"] = ent
+    return out
+
+
+def cpu_baseline(x, idx_cap, target_s):
     """The oracle, as it stands, on all host cores over whole batches of the
     headline workload until about target_s seconds of work."""
     import oracle
@@ -201,19 +353,20 @@ def cpu_baseline(x, idx_cap, target_s=10.0):
         el = time.perf_counter() - t0
         if el >= target_s or reps >= 1000:
             break
-    return dict(value=rows / el, unit="rows/s", cores=threads, kind="oracle",
-                sample=f"{reps} passes over the full {x.batch}-row batch ({el:.1f}s wall)")
+    return dict(value=round(rows / el, 2), unit="rows/s", cores=threads, kind="oracle",
+                sample=f"{reps} passes over the full {x.batch}-row batch ({el:.1f}s wall)", cpu_model=cpu_model())
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=1)
-    ap.add_argument("--others", default="2,3,4", help="extra workloads for per_config ('' = none)")
+    ap.add_argument("--config", type=int, default=HEADLINE)
+    ap.add_argument("--others", default="0,1,2,4", help="extra workloads for per_config ('' = none)")
     ap.add_argument("--rotate-gib", type=float, default=1.0)
     ap.add_argument("--no-check", action="store_true")
+    ap.add_argument("--no-ablation", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -227,27 +380,25 @@ def main():
     q.lib()
     torch.cuda.init()
     rot = int(args.rotate_gib * (1 << 30))
-    head = bench_config(args.config, args.steps, args.warmup, rot)
-    others = []
+    check = not args.no_check
+    ablate = not args.no_ablation
+    head, hx, hr = bench_workload(args.config, args.steps, args.warmup, rot, check, ablate)
+    del hr
+    per = {}
     for s in [t for t in args.others.split(",") if t.strip()]:
         i = int(s)
-        if i != args.config:
-            others.append(bench_config(i, args.steps, args.warmup, rot))
-    # oracle leg: parity of every timed workload, then the CPU baseline
-    per = {}
-    for r in [head] + others:
-        if not args.no_check:
-            oracle_leg(r)
-    for r in others:
-        r.pop("_inputs")
-        r.pop("_gpu")
-        per[r["name"]] = {kk: (round(v, 4) if isinstance(v, float) else v) for kk, v in r.items()}
-    x = head.pop("_inputs")
-    head.pop("_gpu")
-    cpu = None
-    if args.cpu_seconds > 0:
-        cpu = cpu_baseline(x, int(max(64, x.k.max())), args.cpu_seconds)
-    dev_name = torch.cuda.get_device_name(0)
+        if i == args.config:
+            continue
+        res, x, r = bench_workload(i, args.steps, args.warmup, rot, check, ablate)
+        del r
+        if i == 0:
+            # the single-row case is a latency, reported with the oracle's seconds
+            res["latency_us"] = round(res["ms_per_step"] * 1e3, 2)
+        per[res["name"]] = res
+        torch.cuda.empty_cache()
+    dup = duplicate_ablation(max(5, args.steps // 2), max(2, args.warmup // 2), rot, check) if ablate else None
+    cpu = cpu_baseline(hx, int(max(64, hx.k.max())), args.cpu_seconds) if args.cpu_seconds > 0 else None
+    props = torch.cuda.get_device_properties(0)
     line = {
         "metric": METRIC,
         "value": round(head["rows_per_s"], 1),
@@ -259,34 +410,26 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": head["dtype"],
+        "dtype": "f32" if head["dtype"] == "f32" else head["dtype"],
         "data": "synthetic",
         "config": {"workload": head["name"], "batch": head["batch"], "vocab": head["vocab"],
-                   "logits": head["dtype"], "k": "per-row U{1..1024}", "p": "per-row U[0.5,1)",
+                   "logits": head["dtype"], "k": 4096, "p": "1.0 (top-p off)",
                    "outputs": "uint8 mask + int32 indices + counts"},
         "effective_gbps": round(head["effective_gbps"], 1),
         "pct_peak_hbm": round(head["pct_peak_hbm"], 2),
-        "roofline": {
-            "kernel": "pass1_kernel (sample stats, single-pass truncation, mask fill)",
-            "bound": "hbm",
-            "achieved": round(head["pass1_gbps"], 1),
-            "peak": PEAK_HBM_GBS,
-            "unit": "GB/s",
-            "frac": round(head["pass1_gbps"] / PEAK_HBM_GBS, 4),
-            "traffic": measured_traffic(head["name"]),
-            "pass1_us": round(head["pass1_ms"] * 1e3, 3),
-            "tail_us": round(head["tail_ms"] * 1e3, 3),
-            "alg_bytes_per_launch": head["pass1_alg_bytes"],
-        },
+        "roofline": head["roofline"],
         "cpu_baseline": cpu,
         "parity": head.get("parity"),
+        "oracle_s": head.get("oracle_s"),
         "step_ms_p10_p50_p90": [round(v, 5) for v in head["step_ms_p10_p50_p90"]],
-        "truncation": {"rows": head["batch"], "single_pass": head["rows_single_pass"],
-                       "miss_predicted": head["rows_miss_predicted"], "recollected": head["rows_recollected"],
-                       "full_row": head["rows_full_row"], "gaussian_t_hit": head["gaussian_t_hit_rows"]},
-        "memory": {"workspace_bytes": head["workspace_bytes"], "sort_based_bytes": head["sort_based_bytes"]},
-        "per_config": per,
-        "device": dev_name,
+        "truncation": head["truncation"],
+        "memory": head["memory"],
+        "ablations": head.get("ablations"),
+        "duplicate_handling_ablation": dup,
+        "per_config": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                       for k, v in per.items()},
+        "device": {"name": props.name, "arch": getattr(props, "gcnArchName", None),
+                   "compute_units": props.multi_processor_count},
     }
     print(json.dumps(line), flush=True)
 

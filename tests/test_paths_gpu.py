@@ -120,6 +120,22 @@ def test_windowed_index_output(tier):
     check(x, g, oracle_for(x, cap), cap, f"windows tier {tier}")
 
 
+@pytest.mark.parametrize("tier,k", [(1, 8192), (2, 10000)])
+def test_windowed_index_output_from_lds_candidates(tier, k):
+    """Windows when the row's candidates sit in LDS (heavy-tailed rows whose
+    single pass keeps 9-20 K candidates, at most the tier's LDS capacity) and
+    the kept set with its boundary duplicates exceeds one sort: the windows'
+    gathers and sorts reuse that LDS, so their boundary searches must not read
+    it."""
+    import top_selection_sigma_amd as q
+
+    x = w.make_rows(4, 262144, "bf16", "heavy", seed=6, k=k, p=1.0)
+    g = run_gpu(x, k, options=q.Options(tier=tier))
+    check(x, g, oracle_for(x, k), k, f"lds windows tier {tier}")
+    _say(f"paths {g.diag[:, 4].tolist()} candidates {g.diag[:, 3].tolist()}")
+    assert np.sum(g.diag[:, 4] == 0) >= 3  # most rows on the LDS path
+
+
 def test_workspace_left_dirty_by_a_smaller_batch():
     """A call on 9 rows of 17 logits, then one on 17 rows of top-p-only rows on
     the same workspace: nothing an earlier call wrote is read by a later one."""

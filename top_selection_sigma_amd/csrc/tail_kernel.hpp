@@ -1283,14 +1283,22 @@ QRITA_DEV void emit_row(C& c, const L& lsrc, const RowOut& o, bool all, uint32_t
         sort_words<T>(cnt, ex, RankOut{o.idx, Lout, nullptr, 0u, nullptr}, sh, c.rb);
         return;
     }
-    // windows of CSORT ranks, each bounded by its own boundary word
+    // windows of CSORT ranks, each bounded by its own boundary word. The
+    // gathers and sorts reuse the LDS that may hold the search source's
+    // keys, so each window's boundary is searched over the candidate list in
+    // memory (lsrc), which nothing overwrites.
     const uint64_t Bo = tie_boundary<T>(lsrc, vo, needo, No, o.V, c.mode, sh, c.rb, dg.iters);
+    Ctx<T, L> cl{lsrc, c.seg, c.segcap, c.mode, c.sh, c.rb, 0};
     uint64_t prev = ~0ull;
     for (uint32_t done = 0; done < Lout;) {
         const uint32_t cnt = min((uint32_t)T::CSORT, Lout - done);
         uint64_t Bn = Bo;
         if (done + cnt < Lout) {
-            const CountOut r = search_count<NT, 0>(c, 0u, done + cnt, (int64_t)vo - 1, ngo + No, (int64_t)kmax, 0u);
+            cl.rb = c.rb;
+            const CountOut r = search_count<NT, 0>(cl, 0u, done + cnt, (int64_t)vo - 1, ngo + No, (int64_t)kmax, 0u);
+            c.rb = cl.rb;
+            dg.iters += cl.iters;
+            cl.iters = 0;
             Bn = tie_boundary<T>(lsrc, r.v, done + cnt - r.n_gt, r.N, o.V, c.mode, sh, c.rb, dg.iters);
         }
         SortExt ex;

@@ -214,6 +214,10 @@ def _kind_fn(kind: str) -> Callable:
     def uniform(rng, V):
         return _row_c3(rng, V)
 
+    def gauss2(rng, V):
+        # the 1/16-grid rows' distribution before quantisation (distinct in float32)
+        return rng.normal(0.0, 2.0, V)
+
     def heavy(rng, V):
         return _row_c4(rng, V)
 
@@ -258,14 +262,14 @@ def _kind_fn(kind: str) -> Callable:
     def flat(rng, V):
         return rng.normal(0.0, 0.05, V)
 
-    table = dict(gauss=gauss, gauss_outliers=gauss_outliers, ties16=ties16, uniform=uniform,
+    table = dict(gauss=gauss, gauss_outliers=gauss_outliers, ties16=ties16, uniform=uniform, gauss2=gauss2,
                  heavy=heavy, equal=equal, twolevel=twolevel, smallint=smallint, neginf=neginf,
                  allneginf=allneginf, zeros=zeros, ascending=ascending, descending=descending,
                  spike=spike, flat=flat)
     return table[kind]
 
 
-ROW_KINDS = ("gauss", "gauss_outliers", "ties16", "uniform", "heavy", "equal", "twolevel",
+ROW_KINDS = ("gauss", "gauss_outliers", "ties16", "uniform", "gauss2", "heavy", "equal", "twolevel",
              "smallint", "neginf", "allneginf", "zeros", "ascending", "descending", "spike",
              "flat")
 
