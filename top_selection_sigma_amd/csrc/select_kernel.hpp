@@ -763,52 +763,105 @@ __global__ __launch_bounds__(THREADS, 4) void pass1_kernel(Params P) {
 // fallback after a miss). Returns the number of candidates (capped at the
 // list capacity); *overflow is set when the list was too small, *kmax_out is
 // the largest key and *rest_out the fixed-point mass (relative to tr) of the
-// logits below tr.
+// logits below tr. Survivors are staged in LDS (stage, stage_cap entries)
+// and written to the list in bursts between batches of loads: stores mixed
+// into the streaming loads would make every batch wait for them.
 template <int THREADS, bool BF16>
-QRITA_DEV uint32_t collect_row(const Params& P, int64_t row, float tr, bool rest_on, Shared& sh, int& rb,
-                               uint64_t& rest_out, uint32_t& kmax_out, bool& overflow) {
+QRITA_DEV uint32_t collect_row(const Params& P, int64_t row, float tr, bool rest_on, uint64_t* stage,
+                               uint32_t stage_cap, Shared& sh, int& rb, uint64_t& rest_out, uint32_t& kmax_out,
+                               bool& overflow) {
     const int32_t V = P.vocab;
     const void* rowp = row_ptr<BF16>(P, row);
     uint64_t* lst = P.glist + row * (int64_t)P.list_stride;
+    const uint32_t lcap = (uint32_t)P.list_cap;
     __syncthreads();
-    if (threadIdx.x == 0) {
-        sh.gather_n = 0;
-        sh.flags = 0;
-    }
+    if (threadIdx.x == 0) sh.gather_n = 0;
     __syncthreads();
     const uint32_t lane = threadIdx.x & (kWave - 1);
     uint64_t rest = 0;
     uint32_t kmax = 0;
-    for (int64_t base = 0; base < V; base += THREADS) {
-        const int64_t e = base + threadIdx.x;
-        const float f = e < V ? load_value<BF16>(rowp, e) : 0.0f;
-        const bool s = e < V && f >= tr;
-        if (rest_on && e < V && !s) rest += fx_from_unit_f32(__expf(f - tr));
-        const uint64_t b = __ballot(s);
-        if (b) {
-            uint32_t g = 0;
-            if (lane == 0) g = atomicAdd(&sh.gather_n, (uint32_t)__popcll(b));
-            g = readlane(g, 0);
+    uint32_t flushed = 0;  // entries below this position are in the list already
+    // stage entries [flushed, flushed + stage_cap) go to stage[pos - flushed];
+    // two batches add at most 2 * THREADS * U, so with a flush once half the
+    // stage is used, later positions only arise when the stage is smaller
+    // than that (they are then written to the list directly)
+    constexpr int U = 16;
+    auto flush = [&](uint32_t upto) {
+        const uint32_t n = min(upto - flushed, stage_cap);
+        for (uint32_t i = threadIdx.x; i < n; i += THREADS)
+            if (flushed + i < lcap) lst[flushed + i] = stage[i];
+        flushed = upto;
+    };
+    // the index is clamped and the value masked afterwards, so the loads do
+    // not turn into branches that wait for each load in turn
+    auto load = [&](int64_t base, float (&fv)[U]) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t e = base + (int64_t)u * THREADS + threadIdx.x;
+            const float x = load_value<BF16>(rowp, e < V ? e : V - 1);
+            fv[u] = e < V ? x : 0.0f;
+        }
+    };
+    // one batch of U logits per thread: the wave's survivors are counted
+    // first and reserved with a single LDS atomic, then written to the stage
+    auto consume = [&](int64_t base, const float (&fv)[U]) {
+        uint32_t tot = 0;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t e = base + (int64_t)u * THREADS + threadIdx.x;
+            const bool s = e < V && fv[u] >= tr;
+            if (rest_on && e < V && !s) rest += fx_from_unit_f32(__expf(fv[u] - tr));
+            tot += (uint32_t)__popcll(__ballot(s));
+        }
+        if (tot == 0) return;
+        uint32_t g = 0;
+        if (lane == 0) g = atomicAdd(&sh.gather_n, tot);
+        uint32_t run = readlane(g, 0);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t e = base + (int64_t)u * THREADS + threadIdx.x;
+            const bool s = e < V && fv[u] >= tr;
+            const uint64_t b = __ballot(s);
             if (s) {
-                const uint32_t pos = g + lanes_below(b);
-                const uint32_t key = f32_key(__float_as_uint(f));
+                const uint32_t pos = run + lanes_below(b);
+                const uint32_t key = f32_key(__float_as_uint(fv[u]));
                 kmax = key > kmax ? key : kmax;
-                if (pos < (uint32_t)P.list_cap)
-                    lst[pos] = make_cand(key, (uint32_t)e);
-                else
-                    atomicOr(&sh.flags, 1u);
+                const uint64_t c = make_cand(key, (uint32_t)e);
+                if (pos - flushed < stage_cap)
+                    stage[pos - flushed] = c;
+                else if (pos < lcap)
+                    lst[pos] = c;
             }
+            run += (uint32_t)__popcll(b);
+        }
+    };
+    // two batches alternate: the next one's loads are in flight while the
+    // current one is consumed; the stage is flushed when half full
+    const int64_t step = (int64_t)THREADS * U;
+    float fa[U], fb[U];
+    load(0, fa);
+    for (int64_t base = 0; base < V; base += 2 * step) {
+        if (base + step < V) load(base + step, fb);
+        consume(base, fa);
+        if (base + 2 * step < V) load(base + 2 * step, fa);
+        if (base + step < V) consume(base + step, fb);
+        __syncthreads();
+        const uint32_t now = sh.gather_n;
+        if (now - flushed > stage_cap / 2) {
+            flush(now);
+            __syncthreads();  // the stage is read before later batches refill it
         }
     }
+    flush(sh.gather_n);
     uint32_t d0 = 0, d1 = 0;
     block_sum_min_max<THREADS>(d0, d1, kmax, rest, sh, rb);
     __syncthreads();
     rest_out = rest;
     kmax_out = kmax;
     const uint32_t cnt = sh.gather_n;
-    overflow = sh.flags != 0 || cnt > (uint32_t)P.list_cap;
+    overflow = cnt > lcap;
     __syncthreads();
-    return cnt < (uint32_t)P.list_cap ? cnt : (uint32_t)P.list_cap;
+    return cnt < lcap ? cnt : lcap;
 }
 
 }  // namespace qrita

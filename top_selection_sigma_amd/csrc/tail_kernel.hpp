@@ -183,13 +183,22 @@ struct SrcLds {
     QRITA_DEV void visit(F&& f) const {
         const uint32_t n4 = (n + 3u) / 4u;
         const uint32_t lane = tid_here() & (kWave - 1);
-        for (uint32_t v0 = wave_base_here(); v0 < n4; v0 += NT) {
-            const uint32_t v = v0 + lane;
-            const uint4 q = v < n4 ? ((const uint4*)a)[v] : make_uint4(0u, 0u, 0u, 0u);
+        const uint4* a4 = (const uint4*)a;
+        const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+        // two 16-byte reads per step, both issued before use (indices
+        // clamped, values masked: no branch waits for a read)
+        for (uint32_t v0 = wave_base_here(); v0 < n4; v0 += 2 * NT) {
+            const uint32_t v = v0 + lane, w = v + NT;
+            const uint4 qa = a4[v < n4 ? v : n4 - 1u], qb = a4[w < n4 ? w : n4 - 1u];
+            const uint4 q = v < n4 ? qa : z, r = w < n4 ? qb : z;
             f(q.x, 0u);
             f(q.y, 0u);
             f(q.z, 0u);
             f(q.w, 0u);
+            f(r.x, 0u);
+            f(r.y, 0u);
+            f(r.z, 0u);
+            f(r.w, 0u);
         }
     }
     // this wave's share of the candidates (for sizing decisions)
@@ -198,7 +207,7 @@ struct SrcLds {
 
 // The row's candidate lists in global memory: S sub-lists, sub-list s holding
 // cnt[s] (LDS) entries at base + s * stride. Sub-list s is read by a group of
-// NT >> gshift threads; sixteen loads per thread are in flight.
+// NT >> gshift threads; two batches of eight loads per thread alternate.
 template <int NT>
 struct SrcList {
     static constexpr bool kLows = true;
@@ -210,23 +219,37 @@ struct SrcList {
     uint32_t n;            // total
     template <class F>
     QRITA_DEV void visit(F&& f) const {
-        constexpr int U = 16;
+        constexpr int U = 8;  // entries per thread per batch; the next batch is in flight meanwhile
         const uint32_t t = tid_here();
         const uint32_t tps = 1u << gshift;
-        const uint32_t s = t >> gshift, g = t & (tps - 1u);
-        const uint32_t cs = s < S ? cnt[s] : 0u;
+        const uint32_t s0 = t >> gshift, g = t & (tps - 1u);
+        const uint32_t s = s0 < S ? s0 : 0u;  // groups past the last sub-list read sub-list 0, masked
+        const uint32_t cs = s0 < S ? cnt[s] : 0u;
         const uint64_t* p = base + (size_t)s * stride;
+        const uint32_t jmax = cs ? cs - 1u : 0u;
         // wave-uniform trip count: the longest group of this wave
         const uint32_t trips = wave_max_u32((cs + tps * U - 1u) / (tps * U));
-        for (uint32_t it = 0; it < trips; ++it) {
-            uint64_t c[U];
+        // indices clamped, values masked: the loads never become branches
+        // that wait for each load in turn
+        auto load = [&](uint32_t it, uint64_t (&c)[U]) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const uint32_t j = g + (it * U + (uint32_t)u) * tps;
-                c[u] = j < cs ? p[j] : 0ull;
+                const uint64_t x = p[j < cs ? j : jmax];
+                c[u] = j < cs ? x : 0ull;
             }
+        };
+        auto use = [&](const uint64_t (&c)[U]) {
 #pragma unroll
             for (int u = 0; u < U; ++u) f(cand_key(c[u]), cand_low(c[u]));
+        };
+        uint64_t ca[U], cb[U];
+        if (trips) load(0, ca);
+        for (uint32_t it = 0; it < trips; it += 2) {
+            if (it + 1 < trips) load(it + 1, cb);
+            use(ca);
+            if (it + 2 < trips) load(it + 2, ca);
+            if (it + 1 < trips) use(cb);
         }
     }
     QRITA_DEV uint32_t wave_share() const { return (n + (uint32_t)(NT / kWave) - 1u) / (uint32_t)(NT / kWave); }
@@ -242,20 +265,34 @@ struct SrcRow {
     uint32_t n;
     template <class F>
     QRITA_DEV void visit(F&& f) const {
-        constexpr int U = 8;
+        constexpr int U = 16;  // logits per thread per batch; the next batch is in flight meanwhile
         const uint32_t lane = tid_here() & (kWave - 1);
-        for (uint32_t i0 = wave_base_here(); i0 < V; i0 += NT * U) {
-            uint32_t b[U];
+        const uint32_t wb = wave_base_here();
+        // indices clamped, values masked (unconditional loads stay in flight together)
+        auto load = [&](uint32_t i0, uint32_t (&b)[U]) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const uint32_t i = i0 + (uint32_t)u * NT + lane;
-                b[u] = i < V ? (bf16 ? ((uint32_t)((const uint16_t*)row)[i] << 16) : ((const uint32_t*)row)[i]) : 0u;
+                const uint32_t ic = i < V ? i : V - 1u;
+                const uint32_t x = bf16 ? ((uint32_t)((const uint16_t*)row)[ic] << 16) : ((const uint32_t*)row)[ic];
+                b[u] = i < V ? x : 0u;
             }
+        };
+        auto use = [&](uint32_t i0, const uint32_t (&b)[U]) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const uint32_t i = i0 + (uint32_t)u * NT + lane;
                 f(i < V ? f32_key(b[u]) : 0u, ~i);
             }
+        };
+        const uint32_t step = NT * U;
+        uint32_t ba[U], bb[U];
+        if (wb < V) load(wb, ba);
+        for (uint32_t i0 = wb; i0 < V; i0 += 2 * step) {
+            if (i0 + step < V) load(i0 + step, bb);
+            use(i0, ba);
+            if (i0 + 2 * step < V) load(i0 + 2 * step, ba);
+            if (i0 + step < V) use(i0 + step, bb);
         }
     }
     QRITA_DEV uint32_t wave_share() const { return (n + (uint32_t)(NT / kWave) - 1u) / (uint32_t)(NT / kWave); }
@@ -286,7 +323,8 @@ QRITA_DEV void visit_set(const S& src, const WaveSet& ws, const uint32_t* seg, F
         const uint32_t nv = MASS ? (ws.n + 1u) / 2u : (ws.n + 3u) / 4u;
         for (uint32_t v0 = 0; v0 < nv; v0 += kWave) {
             const uint32_t v = v0 + lane;
-            const uint4 q = v < nv ? ((const uint4*)seg)[v] : make_uint4(0u, 0u, 0u, 0u);
+            const uint4 qr = ((const uint4*)seg)[v < nv ? v : nv - 1u];  // clamped: no branch
+            const uint4 q = v < nv ? qr : make_uint4(0u, 0u, 0u, 0u);
             if (MASS) {
                 f(q.x, 0u, __uint_as_float(q.y));
                 f(q.z, 0u, __uint_as_float(q.w));
@@ -1442,15 +1480,16 @@ QRITA_DEV SrcList<NT> list_source(const Params& P, int64_t row, uint32_t S, uint
     return SrcList<NT>{P.glist + row * (int64_t)P.list_stride, stride, S, gshift, cnt, n};
 }
 
-// The tail's slow paths, kept out of line: a candidate list too long for LDS
-// (searched in memory), and after a truncation miss the re-collection of the
-// row with thresholds lowered to sample order statistics and, as the last
-// resort, the search of the full row (§1).
+// The tail's slow paths: a candidate list too long for LDS (searched in
+// memory), and after a truncation miss the re-collection of the row with
+// thresholds lowered to sample order statistics and, as the last resort, the
+// search of the full row (§1). Inlined: as a separate function its LDS and
+// global pointers would arrive as generic ones, and flat memory operations
+// serialise the loops.
 template <class T>
-__device__ __attribute__((noinline)) TailOut tail_fallback(const Params P, int64_t row, RowMode md, float t, float tc,
-                                                           uint32_t nlist, uint32_t kmax, uint64_t rest,
-                                                           bool overflow, bool lds_tried, float lambda, uint32_t ns_h,
-                                                           int32_t n_t, Shared& sh, int rb) {
+QRITA_DEV TailOut tail_fallback(const Params& P, int64_t row, RowMode md, float t, float tc, uint32_t nlist,
+                                uint32_t kmax, uint64_t rest, bool overflow, bool lds_tried, float lambda,
+                                uint32_t ns_h, int32_t n_t, Shared& sh, int rb) {
     constexpr int NT = T::NT;
     const int32_t V = P.vocab;
     const void* rowp = P.bf16 ? (const void*)((const uint16_t*)P.logits + row * (int64_t)V)
@@ -1485,10 +1524,13 @@ __device__ __attribute__((noinline)) TailOut tail_fallback(const Params P, int64
             uint32_t kmax2 = 0;
             bool ovf = false;
             uint32_t cnt;
+            // the whole dynamic LDS stages the survivors (nothing in it is live here)
+            uint64_t* stage = (uint64_t*)dyn_lds();
+            const uint32_t scap = (uint32_t)(T::LDS / 8);
             if (P.bf16)
-                cnt = collect_row<NT, true>(P, row, tr, md.topp && !md.topk, sh, rb, rest2, kmax2, ovf);
+                cnt = collect_row<NT, true>(P, row, tr, md.topp && !md.topk, stage, scap, sh, rb, rest2, kmax2, ovf);
             else
-                cnt = collect_row<NT, false>(P, row, tr, md.topp && !md.topk, sh, rb, rest2, kmax2, ovf);
+                cnt = collect_row<NT, false>(P, row, tr, md.topp && !md.topk, stage, scap, sh, rb, rest2, kmax2, ovf);
             if (ovf) break;
             if (threadIdx.x == 0) sh.cnt[0] = cnt;
             lds_sync();
@@ -1577,8 +1619,9 @@ __global__ __launch_bounds__(T::NT, T::WAVES_PER_SIMD) void tail_kernel(Params P
                     uint32_t kv[U];
 #pragma unroll
                     for (int u = 0; u < U; ++u) {
+                        // clamped index: unconditional loads, all in flight together
                         const uint32_t j = j0 + (uint32_t)u * tps;
-                        kv[u] = j < cs ? pk[2 * (size_t)j] : 0u;
+                        kv[u] = pk[2 * (size_t)(j < cs ? j : cs - 1u)];
                     }
 #pragma unroll
                     for (int u = 0; u < U; ++u) {
