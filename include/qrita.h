@@ -187,6 +187,53 @@ int qrita_select_noalloc(const void* logits, int64_t batch, int64_t vocab, int d
                          uint8_t* out_mask, int32_t* out_idx, int32_t* out_count, int64_t idx_cap,
                          void* stream);
 
+/*
+ * Select, then draw one token per row from the kept set: the sampling step
+ * the candidate set exists for (the summary motivates returning the whole
+ * top-k / top-p set because an LLM sampler draws from it next, "Declaración
+ * del Problema"). The selection and its outputs are those of qrita_select_ex;
+ * in addition, per row b with kept set of L tokens in rank order r = 0..L-1:
+ *   p_r   = exp(z_r - m) / sum_{s<L} exp(z_s - m)   (m = row maximum),
+ *   c_r   = p_0 + ... + p_r,
+ *   u     = the row's uniform in [0, 1): the first 64-bit output of
+ *           Philox4x64-10 (Salmon et al., SC 2011) at counter
+ *           (b, offset, 0, 0) under key (seed, 0), top 53 bits times 2^-53
+ *           (qrita_uniform returns it on the host),
+ *   token = the index of the smallest rank r with c_r >= u (inverse CDF).
+ * An all -inf row draws rank 0. Masses are formed in the same fixed point as
+ * the top-p cut: when u lies within 1e-6 of some c_r, the drawn rank may
+ * differ from an exact float64 computation by the ranks inside that band.
+ * The draw is a function of (logits, k, p, seed, offset, b) only: the same
+ * call gives the same tokens on any stream, any batch position is
+ * independent of the others, and a new offset gives new draws.
+ *
+ * out_token  device int32 [batch]: the drawn vocabulary index. Required.
+ * out_prob   device float32 [batch][idx_cap] or NULL: p_r beside out_idx for
+ *            the ranks out_idx holds (requires out_idx).
+ * seed, offset  the Philox key word and counter word above.
+ * out_mask, out_idx, out_count, idx_cap, workspace, stream, opt: as for
+ *            qrita_select_ex; all three outputs may be NULL here.
+ * Returns the codes of qrita_select_ex.
+ */
+int qrita_sample(const void* logits, int64_t batch, int64_t vocab, int dtype,
+                 const int32_t* k, const float* p, uint64_t seed, uint64_t offset,
+                 int32_t* out_token, float* out_prob,
+                 uint8_t* out_mask, int32_t* out_idx, int32_t* out_count, int64_t idx_cap,
+                 void* workspace, size_t workspace_bytes, void* stream,
+                 const qrita_options* opt);
+
+/*
+ * Philox4x64-10 on the host (Salmon, Moraes, Dror, Shaw, "Parallel random
+ * numbers: as easy as 1, 2, 3", SC 2011): out = the ten-round bijection of
+ * the 256-bit counter under the 128-bit key. The same routine the device
+ * draw runs; exported so that callers and tests can reproduce the draws.
+ * Host pointers; no GPU involved.
+ */
+void qrita_philox4x64_10(const uint64_t counter[4], const uint64_t key[2], uint64_t out[4]);
+
+/* The uniform qrita_sample draws for row `row` under (seed, offset); host only. */
+double qrita_uniform(uint64_t seed, uint64_t offset, uint64_t row);
+
 /* Static description of a status code. */
 const char* qrita_strerror(int status);
 

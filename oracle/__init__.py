@@ -54,6 +54,9 @@ def _load():
             lib.oracle_select.argtypes = [vp, i64, i64, ctypes.c_int, vp, vp, vp, vp, i64, vp,
                                           vp, vp, ctypes.c_int, ctypes.POINTER(i64),
                                           ctypes.POINTER(i64)]
+            lib.oracle_sample.restype = ctypes.c_int
+            lib.oracle_sample.argtypes = [vp, i64, i64, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64,
+                                          ctypes.c_int, ctypes.POINTER(i64), ctypes.POINTER(i64)]
             lib.oracle_hardware_threads.restype = ctypes.c_int
             _lib = lib
         return _lib
@@ -117,3 +120,71 @@ def select(logits: np.ndarray, dtype: str, k: Optional[np.ndarray], p: Optional[
     if rc != 0:
         raise RuntimeError(f"oracle_select failed with status {rc}")
     return OracleResult(mask, idx, count, lo, hi)
+
+
+def uniforms(seed: int, offset: int, batch: int) -> np.ndarray:
+    """The draw's uniforms from NumPy's own Philox4x64-10 (the generator of
+    Salmon et al., SC 2011, as NumPy implements it): for row b, the first
+    64-bit output at counter (b, offset, 0, 0) under key (seed, 0), top 53
+    bits times 2^-53. NumPy advances its counter before each block of four
+    outputs, so the generator starts one counter value earlier."""
+    out = np.empty(batch, np.float64)
+    for b in range(batch):
+        ctr = ((int(b) | (int(offset) % 2**64) << 64) - 1) % 2**256
+        g = np.random.Philox(counter=ctr, key=int(seed) % 2**64)
+        x = int(g.random_raw())
+        out[b] = (x >> 11) * 2.0**-53
+    return out
+
+
+@dataclass
+class SampleResult:
+    token: np.ndarray     # int32 [B] drawn vocabulary index
+    rank: np.ndarray      # int32 [B] its rank in the kept set
+    rank_lo: np.ndarray   # int32 [B] draw rank at u - 1e-6
+    rank_hi: np.ndarray   # int32 [B] draw rank at u + 1e-6
+    count: np.ndarray     # int32 [B] kept count
+    idx: np.ndarray       # int32 [B, idx_cap] kept indices in rank order (-1 past the count)
+    prob: np.ndarray      # float32 [B, idx_cap] renormalised probabilities beside idx
+
+
+def sample(logits: np.ndarray, dtype: str, k: Optional[np.ndarray], p: Optional[np.ndarray],
+           u: np.ndarray, idx_cap: int, nthreads: int = 0) -> SampleResult:
+    """Select, then draw by inverse CDF over the kept set with the given uniforms."""
+    lib = _load()
+    if dtype == "f32":
+        x = np.ascontiguousarray(logits, dtype=np.float32)
+        dt = 0
+    elif dtype == "bf16":
+        x = np.ascontiguousarray(logits, dtype=np.uint16)
+        dt = 1
+    else:
+        raise ValueError(f"unknown dtype {dtype!r}")
+    B, V = x.shape
+    kk = None if k is None else np.ascontiguousarray(k, dtype=np.int32)
+    pp = None if p is None else np.ascontiguousarray(p, dtype=np.float32)
+    uu = np.ascontiguousarray(u, dtype=np.float64)
+    if uu.shape != (B,):
+        raise ValueError("u must have one uniform per row")
+    token = np.empty(B, np.int32)
+    lo = np.empty(B, np.int32)
+    hi = np.empty(B, np.int32)
+    count = np.empty(B, np.int32)
+    cap = max(int(idx_cap), 1)
+    idx = np.full((B, cap), -1, np.int32)
+    prob = np.zeros((B, cap), np.float32)
+    bad_r, bad_c = ctypes.c_int64(-1), ctypes.c_int64(-1)
+
+    def ptr(a):
+        return None if a is None else a.ctypes.data
+
+    rank = np.empty(B, np.int32)
+    rc = lib.oracle_sample(ptr(x), B, V, dt, ptr(kk), ptr(pp), ptr(uu), ptr(token), ptr(rank), ptr(lo), ptr(hi),
+                           ptr(count), ptr(idx), ptr(prob), cap, int(nthreads), ctypes.byref(bad_r),
+                           ctypes.byref(bad_c))
+    if rc == 2:
+        raise OracleInputError(f"NaN or +inf logit at row {bad_r.value}, column {bad_c.value}")
+    if rc != 0:
+        raise RuntimeError(f"oracle_sample failed with status {rc}")
+    return SampleResult(token, rank, lo, hi, count, idx[:, :idx_cap] if idx_cap > 0 else idx[:, :0],
+                        prob[:, :idx_cap] if idx_cap > 0 else prob[:, :0])

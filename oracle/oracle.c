@@ -36,6 +36,16 @@
  * Top-k before top-p, with top-p renormalised over the top-k set, is the
  * composition of the sort-based samplers Qrita replaces; the pages do not
  * spell it out.
+ *
+ * Sampling from the candidate set (oracle_sample; the step after the
+ * selection, for which the pages motivate returning the whole candidate set,
+ * "Declaración del Problema"): with the kept set of L tokens in rank order
+ * and e_r = exp(z_r - m) for r < L, p_r = e_r / sum_{s<L} e_s (float64,
+ * sequential sums), c_r = sum_{s<=r} p_s; for a uniform u in [0, 1) the
+ * drawn token is the one of smallest rank r with c_r >= u (rank L-1 if no r
+ * qualifies; rank 0 when every kept logit is -inf). Draws whose u lies
+ * within 1e-6 of some c_r are band draws: the ranks for u - 1e-6 and
+ * u + 1e-6 bound the answers a rounding-different computation may give.
  */
 #include <math.h>
 #include <pthread.h>
@@ -165,6 +175,163 @@ done:
     free(cum);
     free(e);
     return NULL;
+}
+
+int oracle_hardware_threads(void);
+
+typedef struct {
+    oracle_job base;
+    const double *u;
+    int32_t *token, *rank, *tok_lo, *tok_hi;
+    float *prob;  /* [batch][idx_cap] or NULL */
+} oracle_sample_job;
+
+/* smallest r < L with c[r] >= x, else L - 1 */
+static int64_t draw_rank(const double *c, int64_t L, double x) {
+    for (int64_t r = 0; r < L; ++r)
+        if (c[r] >= x) return r;
+    return L - 1;
+}
+
+static void *run_sample_rows(void *arg) {
+    oracle_sample_job *S = (oracle_sample_job *)arg;
+    oracle_job *J = &S->base;
+    const int64_t V = J->vocab;
+    oracle_item *items = (oracle_item *)malloc((size_t)V * sizeof(oracle_item));
+    double *e = (double *)malloc((size_t)V * sizeof(double));
+    double *c = (double *)malloc((size_t)V * sizeof(double));
+    if (!items || !e || !c) {
+        J->status = 3;
+        free(items); free(e); free(c);
+        return NULL;
+    }
+    for (int64_t b = J->row_begin; b < J->row_end; ++b) {
+        for (int64_t i = 0; i < V; ++i) {
+            double x = decode(J->logits, J->dtype, b * V + i);
+            if (isnan(x) || x == INFINITY) {
+                J->status = 2;
+                J->bad_row = b;
+                J->bad_col = i;
+                goto done;
+            }
+            items[i].v = x;
+            items[i].i = i;
+        }
+        qsort(items, (size_t)V, sizeof(oracle_item), cmp_desc);
+        /* the kept set, exactly as in run_rows */
+        int64_t kb = J->k ? (int64_t)J->k[b] : 0;
+        int64_t K = (kb <= 0 || kb >= V) ? V : kb;
+        int64_t L = K;
+        double p = J->p ? (double)J->p[b] : 1.0;
+        const double m = items[0].v;
+        if (p < 1.0) {
+            if (p <= 0.0 || m == -INFINITY) {
+                L = 1;
+            } else {
+                double Sk = 0.0;
+                for (int64_t r = 0; r < K; ++r) {
+                    e[r] = exp(items[r].v - m);
+                    Sk += e[r];
+                }
+                double cc = 0.0;
+                for (int64_t r = 0; r < K; ++r) {
+                    cc += e[r] / Sk;
+                    c[r] = cc;
+                }
+                L = prefix_cut(c, K, p);
+            }
+        }
+        /* renormalised over the kept set */
+        int64_t r0 = 0, rlo = 0, rhi = 0;
+        if (m != -INFINITY) {
+            double Sl = 0.0;
+            for (int64_t r = 0; r < L; ++r) {
+                e[r] = exp(items[r].v - m);
+                Sl += e[r];
+            }
+            double cc = 0.0;
+            for (int64_t r = 0; r < L; ++r) {
+                cc += e[r] / Sl;
+                c[r] = cc;
+            }
+            const double u = S->u[b];
+            r0 = draw_rank(c, L, u);
+            rlo = draw_rank(c, L, u - 1e-6);
+            rhi = draw_rank(c, L, u + 1e-6);
+            if (S->prob) {
+                const int64_t n = L < J->idx_cap ? L : J->idx_cap;
+                for (int64_t r = 0; r < n; ++r) S->prob[b * J->idx_cap + r] = (float)(e[r] / Sl);
+            }
+        } else if (S->prob) {
+            const int64_t n = L < J->idx_cap ? L : J->idx_cap;
+            for (int64_t r = 0; r < n; ++r) S->prob[b * J->idx_cap + r] = 0.0f;
+        }
+        S->token[b] = (int32_t)items[r0].i;
+        if (S->rank) S->rank[b] = (int32_t)r0;
+        if (S->tok_lo) S->tok_lo[b] = (int32_t)rlo;
+        if (S->tok_hi) S->tok_hi[b] = (int32_t)rhi;
+        if (J->count) J->count[b] = (int32_t)L;
+        if (J->idx) {
+            const int64_t n = L < J->idx_cap ? L : J->idx_cap;
+            for (int64_t r = 0; r < n; ++r) J->idx[b * J->idx_cap + r] = (int32_t)items[r].i;
+        }
+    }
+done:
+    free(items);
+    free(e);
+    free(c);
+    return NULL;
+}
+
+/*
+ * Draw one token per row from the kept set (see the header comment):
+ * u [batch] uniforms in [0, 1); token [batch] the drawn vocabulary index;
+ * rank [batch] its rank in the kept set (may be NULL);
+ * tok_lo / tok_hi [batch] the band of ranks (may be NULL); count [batch] the
+ * kept count; idx [batch][idx_cap] the kept indices in rank order and prob
+ * [batch][idx_cap] their renormalised probabilities (each may be NULL).
+ * Returns as oracle_select.
+ */
+int oracle_sample(const void *logits, int64_t batch, int64_t vocab, int dtype, const int32_t *k,
+                  const float *p, const double *u, int32_t *token, int32_t *rank, int32_t *tok_lo, int32_t *tok_hi,
+                  int32_t *count, int32_t *idx, float *prob, int64_t idx_cap, int nthreads,
+                  int64_t *bad_row, int64_t *bad_col) {
+    if (!logits || !u || !token || batch < 0 || vocab <= 0 || vocab > INT32_MAX ||
+        (dtype != 0 && dtype != 1) || idx_cap < 0)
+        return 1;
+    if (batch == 0) return 0;
+    if (nthreads <= 0) nthreads = oracle_hardware_threads();
+    if (nthreads > batch) nthreads = (int)batch;
+    oracle_sample_job *jobs = (oracle_sample_job *)calloc((size_t)nthreads, sizeof(oracle_sample_job));
+    pthread_t *th = (pthread_t *)calloc((size_t)nthreads, sizeof(pthread_t));
+    if (!jobs || !th) {
+        free(jobs); free(th);
+        return 3;
+    }
+    for (int t = 0; t < nthreads; ++t) {
+        oracle_job *J = &jobs[t].base;
+        J->logits = logits; J->batch = batch; J->vocab = vocab; J->dtype = dtype;
+        J->k = k; J->p = p; J->idx = idx; J->idx_cap = idx_cap; J->count = count;
+        J->row_begin = batch * t / nthreads;
+        J->row_end = batch * (t + 1) / nthreads;
+        J->bad_row = J->bad_col = -1;
+        jobs[t].u = u; jobs[t].token = token; jobs[t].rank = rank; jobs[t].tok_lo = tok_lo; jobs[t].tok_hi = tok_hi;
+        jobs[t].prob = prob;
+    }
+    for (int t = 1; t < nthreads; ++t) pthread_create(&th[t], NULL, run_sample_rows, &jobs[t]);
+    run_sample_rows(&jobs[0]);
+    for (int t = 1; t < nthreads; ++t) pthread_join(th[t], NULL);
+    int status = 0;
+    for (int t = 0; t < nthreads && status == 0; ++t) {
+        if (jobs[t].base.status) {
+            status = jobs[t].base.status;
+            if (bad_row) *bad_row = jobs[t].base.bad_row;
+            if (bad_col) *bad_col = jobs[t].base.bad_col;
+        }
+    }
+    free(jobs);
+    free(th);
+    return status;
 }
 
 int oracle_hardware_threads(void) {

@@ -15,15 +15,15 @@ HEADER = os.path.join(ROOT, "include", "qrita.h")
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(qrita_[a-z_]+)\s*\(",
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(qrita_[a-z0-9_]+)\s*\(",
                        text, flags=re.M)
     return sorted(set(names))
 
 
 def test_header_declares_the_api():
     names = _declared_functions()
-    assert names == ["qrita_select", "qrita_select_ex", "qrita_select_noalloc", "qrita_strerror",
-                     "qrita_workspace_bytes"]
+    assert names == ["qrita_philox4x64_10", "qrita_sample", "qrita_select", "qrita_select_ex",
+                     "qrita_select_noalloc", "qrita_strerror", "qrita_uniform", "qrita_workspace_bytes"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -125,3 +125,60 @@ def test_noalloc_rejects_oversize_and_bad_arguments_before_launch():
     assert lib.qrita_select_noalloc(FAKE, 4, 100, 9, None, None, None, None, FAKE, 0, None) == q.QRITA_EINVAL
     assert lib.qrita_select_noalloc(FAKE, 0, 100, 0, None, None, None, None, FAKE, 0, None) == q.QRITA_OK
     assert "static scratch" in q.qrita_strerror(q.QRITA_ESCRATCH)
+
+
+def _sample(token=FAKE + (2 << 20), prob=None, opt=None, **kw):
+    lib = q.lib()
+    a = dict(logits=FAKE, batch=4, vocab=100, dtype=0, k=FAKE + 4096, p=FAKE + 8192, mask=FAKE + 16384,
+             idx=FAKE + 65536, count=FAKE + 131072, idx_cap=8, ws=FAKE + (1 << 20), ws_bytes=None)
+    a.update(kw)
+    if a["ws_bytes"] is None:
+        a["ws_bytes"] = q.qrita_workspace_bytes(max(a["batch"], 0), max(a["vocab"], 1), 0, a["idx_cap"])
+    return lib.qrita_sample(a["logits"], a["batch"], a["vocab"], a["dtype"], a["k"], a["p"], 5, 6, token, prob,
+                            a["mask"], a["idx"], a["count"], a["idx_cap"], a["ws"], a["ws_bytes"], None,
+                            None if opt is None else ctypes.byref(opt))
+
+
+def test_sample_argument_errors_return_before_launch():
+    assert _sample(token=None) == q.QRITA_EINVAL                       # no token output
+    assert _sample(token=FAKE + 2) == q.QRITA_EINVAL                   # misaligned token output
+    assert _sample(prob=FAKE + (3 << 20), idx=None, count=None) == q.QRITA_EINVAL  # prob without idx
+    assert _sample(logits=None) == q.QRITA_EINVAL
+    assert _sample(ws=None) == q.QRITA_EWORKSPACE
+    assert _sample(opt=q._Options(0, 0.0, 7, 0, 0, 0, None, None, 0, 0)) == q.QRITA_EINVAL
+    assert _sample(batch=0) == q.QRITA_OK
+    # token alone is a valid output set (checked up to the workspace)
+    assert _sample(mask=None, idx=None, count=None, ws=None) == q.QRITA_EWORKSPACE
+
+
+def test_host_philox_matches_numpy():
+    """The library's Philox4x64-10 (the routine its device draw runs) against
+    NumPy's independent implementation of the same published generator, over
+    counters and keys with every word in use."""
+    import numpy as np
+
+    rng = np.random.default_rng(11)
+    for t in range(40):
+        ctr = [int(x) for x in rng.integers(0, 2**63, 4, dtype=np.int64)]
+        if t % 4 == 0:
+            ctr = [t, 0, 0, 0]
+        if t % 4 == 1:
+            ctr = [2**64 - 1, 2**64 - 1, t, 2**63]
+        key = [int(x) for x in rng.integers(0, 2**63, 2, dtype=np.int64)]
+        if t % 3 == 0:
+            key[1] = 0
+        c = sum(w << (64 * i) for i, w in enumerate(ctr))
+        g = np.random.Philox(counter=(c - 1) % 2**256, key=key[0] | key[1] << 64)
+        want = [int(x) for x in g.random_raw(4)]
+        assert list(q.qrita_philox4x64_10(ctr, key)) == want, t
+
+
+def test_host_uniform_matches_oracle_uniforms():
+    import numpy as np
+
+    import oracle
+
+    for seed, offset in [(0, 0), (1, 2), (2**64 - 1, 2**63 + 5), (987654321, 12)]:
+        u = oracle.uniforms(seed, offset, 9)
+        assert [q.qrita_uniform(seed, offset, b) for b in range(9)] == u.tolist()
+        assert np.all((u >= 0) & (u < 1))

@@ -97,6 +97,14 @@ def lib() -> ctypes.CDLL:
             L.qrita_select_ex.argtypes = sel + [ctypes.POINTER(_Options)]
             L.qrita_select_noalloc.restype = ctypes.c_int
             L.qrita_select_noalloc.argtypes = [vp, i64, i64, ctypes.c_int, vp, vp, vp, vp, vp, i64, vp]
+            u64 = ctypes.c_uint64
+            L.qrita_sample.restype = ctypes.c_int
+            L.qrita_sample.argtypes = [vp, i64, i64, ctypes.c_int, vp, vp, u64, u64, vp, vp, vp, vp, vp, i64,
+                                       vp, sz, vp, ctypes.POINTER(_Options)]
+            L.qrita_philox4x64_10.restype = None
+            L.qrita_philox4x64_10.argtypes = [ctypes.POINTER(u64), ctypes.POINTER(u64), ctypes.POINTER(u64)]
+            L.qrita_uniform.restype = ctypes.c_double
+            L.qrita_uniform.argtypes = [u64, u64, u64]
             L.qrita_strerror.restype = ctypes.c_char_p
             L.qrita_strerror.argtypes = [ctypes.c_int]
             _lib = L
@@ -169,6 +177,37 @@ def qrita_select_noalloc(logits, k, p, out_mask, out_idx, out_count, idx_cap: in
         raise QritaError(st, "qrita_select_noalloc")
 
 
+def qrita_sample(logits, k, p, seed: int, offset: int, out_token, out_prob, out_mask, out_idx, out_count,
+                 idx_cap: int, workspace, stream=None, options: Optional[Options] = None) -> None:
+    """Call ``qrita_sample``: the selection plus one draw per row from the kept set."""
+    if logits.dim() != 2 or not logits.is_contiguous():
+        raise ValueError("logits must be a contiguous [batch, vocab] tensor")
+    B, V = logits.shape
+    ws_bytes = workspace.numel() * workspace.element_size()
+    opt = None if options is None else ctypes.byref(options.to_c())
+    st = lib().qrita_sample(logits.data_ptr(), B, V, dtype_code(logits), _ptr(k), _ptr(p),
+                            int(seed) % 2**64, int(offset) % 2**64, _ptr(out_token), _ptr(out_prob),
+                            _ptr(out_mask), _ptr(out_idx), _ptr(out_count), int(idx_cap),
+                            workspace.data_ptr(), ws_bytes, _stream_ptr(stream), opt)
+    if st != QRITA_OK:
+        raise QritaError(st, "qrita_sample")
+
+
+def qrita_philox4x64_10(counter, key) -> Tuple[int, int, int, int]:
+    """Philox4x64-10 of a 4-word counter under a 2-word key (host, through the library)."""
+    u64 = ctypes.c_uint64
+    c = (u64 * 4)(*[int(x) % 2**64 for x in counter])
+    k = (u64 * 2)(*[int(x) % 2**64 for x in key])
+    o = (u64 * 4)()
+    lib().qrita_philox4x64_10(c, k, o)
+    return tuple(int(x) for x in o)
+
+
+def qrita_uniform(seed: int, offset: int, row: int) -> float:
+    """The uniform ``qrita_sample`` draws for ``row`` under (seed, offset)."""
+    return float(lib().qrita_uniform(int(seed) % 2**64, int(offset) % 2**64, int(row) % 2**64))
+
+
 _ws_cache = {}
 
 
@@ -221,3 +260,31 @@ def select(logits, k=None, p=None, want_mask: bool = True, idx_cap: Optional[int
     ws = workspace_for(B, V, dtype_code(logits), cap, dev, stream)
     qrita_select_ex(logits, k, p, mask, idx, count, cap, ws, stream, options)
     return mask, idx, count
+
+
+def sample(logits, k=None, p=None, seed: int = 0, offset: int = 0, idx_cap: Optional[int] = None,
+           want_mask: bool = False, options: Optional[Options] = None, stream=None) -> Tuple:
+    """Allocate outputs, select and draw one token per row.
+
+    Returns (token int32 [B], idx int32 [B, idx_cap] or None, prob float32
+    [B, idx_cap] or None, count int32 [B], mask uint8 [B, V] or None).
+    """
+    import torch
+
+    B, V = logits.shape
+    dev = logits.device
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    idx = prob = None
+    cap = 0
+    with torch.cuda.stream(stream):
+        token = torch.empty(B, dtype=torch.int32, device=dev)
+        mask = torch.empty((B, V), dtype=torch.uint8, device=dev) if want_mask else None
+        if idx_cap is not None and idx_cap > 0:
+            cap = int(idx_cap)
+            idx = torch.empty((B, cap), dtype=torch.int32, device=dev)
+            prob = torch.empty((B, cap), dtype=torch.float32, device=dev)
+        count = torch.empty(B, dtype=torch.int32, device=dev)
+    ws = workspace_for(B, V, dtype_code(logits), cap, dev, stream)
+    qrita_sample(logits, k, p, seed, offset, token, prob, mask, idx, count, cap, ws, stream, options)
+    return token, idx, prob, count, mask

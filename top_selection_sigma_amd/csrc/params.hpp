@@ -32,6 +32,10 @@ struct Params {
     int32_t pivot_mode;  // 0 key quartiles, 1 value quartiles, 2 one pivot at the key midpoint
     int32_t bitmap;      // 1: the tail writes whole mask rows; pass 1 leaves the mask alone
     int32_t bf16;
+    int32_t* out_token;  // sampling: [batch] drawn token, or null (no draw)
+    float* out_prob;     // sampling: [batch][idx_cap] probabilities beside out_idx, or null
+    uint64_t seed;       // sampling: Philox key
+    uint64_t offset;     // sampling: Philox counter word 1
 };
 
 // Records that pass 1 leaves for the tail. Every word is written by plain

@@ -9,6 +9,7 @@
 #include <mutex>
 
 #include "launch.hpp"
+#include "philox.hpp"
 #include "qrita.h"
 
 namespace {
@@ -117,16 +118,33 @@ bool device_supported() {
     return s == 1;
 }
 
+// The draw of a sampling call (null for a selection).
+struct Draw {
+    int32_t* token;
+    float* prob;
+    uint64_t seed, offset;
+};
+
+bool options_valid(const qrita_options* opt) {
+    return !opt || !(((uintptr_t)opt->diag & 3u) || opt->pivot_mode < 0 || opt->pivot_mode > 2 ||
+                     opt->slices < 0 || opt->lds_cap < 0 || opt->list_cap < 0 || opt->tier < 0 ||
+                     opt->tier > 2 || opt->mask_mode < 0 || opt->mask_mode > 1 ||
+                     !(opt->delta_scale == opt->delta_scale));
+}
+
 int select_impl(const void* logits, int64_t batch, int64_t vocab, int dtype, const int32_t* k,
                 const float* p, uint8_t* out_mask, int32_t* out_idx, int32_t* out_count,
                 int64_t idx_cap, void* workspace, size_t workspace_bytes, void* stream,
-                const qrita_options* opt) {
+                const qrita_options* opt, const Draw* draw = nullptr) {
     if (!logits || batch < 0 || vocab <= 0 || vocab > INT32_MAX || idx_cap < 0 ||
         idx_cap > INT32_MAX)
         return QRITA_EINVAL;
     if (dtype != QRITA_F32 && dtype != QRITA_BF16) return QRITA_EINVAL;
     if (out_idx && !out_count) return QRITA_EINVAL;
-    if (!out_mask && !out_idx && !out_count) return QRITA_EINVAL;
+    if (!out_mask && !out_idx && !out_count && !draw) return QRITA_EINVAL;
+    if (draw && (!draw->token || ((uintptr_t)draw->token & 3u) || ((uintptr_t)draw->prob & 3u) ||
+                 (draw->prob && !out_idx)))
+        return QRITA_EINVAL;
     if (((uintptr_t)logits & 15u) || ((uintptr_t)out_mask & 15u)) return QRITA_EINVAL;
     if (((uintptr_t)k & 3u) || ((uintptr_t)p & 3u) || ((uintptr_t)out_idx & 3u) ||
         ((uintptr_t)out_count & 3u))
@@ -168,6 +186,12 @@ int select_impl(const void* logits, int64_t batch, int64_t vocab, int dtype, con
     P.pivot_mode = opt ? opt->pivot_mode : 0;
     P.bitmap = t.bitmap ? 1 : 0;
     P.bf16 = bf16 ? 1 : 0;
+    if (draw) {
+        P.out_token = draw->token;
+        P.out_prob = draw->prob;
+        P.seed = draw->seed;
+        P.offset = draw->offset;
+    }
 
     hipStream_t s = (hipStream_t)stream;
     const unsigned groups = (unsigned)(((batch + 7) / 8) * 8 * (int64_t)t.slices);
@@ -247,13 +271,27 @@ int qrita_select_ex(const void* logits, int64_t batch, int64_t vocab, int dtype,
                     const float* p, uint8_t* out_mask, int32_t* out_idx, int32_t* out_count,
                     int64_t idx_cap, void* workspace, size_t workspace_bytes, void* stream,
                     const qrita_options* opt) {
-    if (opt && (((uintptr_t)opt->diag & 3u) || opt->pivot_mode < 0 || opt->pivot_mode > 2 ||
-                opt->slices < 0 || opt->lds_cap < 0 || opt->list_cap < 0 || opt->tier < 0 ||
-                opt->tier > 2 || opt->mask_mode < 0 || opt->mask_mode > 1 ||
-                !(opt->delta_scale == opt->delta_scale)))
-        return QRITA_EINVAL;
+    if (!options_valid(opt)) return QRITA_EINVAL;
     return select_impl(logits, batch, vocab, dtype, k, p, out_mask, out_idx, out_count, idx_cap,
                        workspace, workspace_bytes, stream, opt);
+}
+
+int qrita_sample(const void* logits, int64_t batch, int64_t vocab, int dtype, const int32_t* k,
+                 const float* p, uint64_t seed, uint64_t offset, int32_t* out_token, float* out_prob,
+                 uint8_t* out_mask, int32_t* out_idx, int32_t* out_count, int64_t idx_cap,
+                 void* workspace, size_t workspace_bytes, void* stream, const qrita_options* opt) {
+    if (!options_valid(opt)) return QRITA_EINVAL;
+    const Draw d{out_token, out_prob, seed, offset};
+    return select_impl(logits, batch, vocab, dtype, k, p, out_mask, out_idx, out_count, idx_cap,
+                       workspace, workspace_bytes, stream, opt, &d);
+}
+
+void qrita_philox4x64_10(const uint64_t counter[4], const uint64_t key[2], uint64_t out[4]) {
+    qrita::philox4x64_10(counter, key, out);
+}
+
+double qrita_uniform(uint64_t seed, uint64_t offset, uint64_t row) {
+    return qrita::row_uniform(seed, offset, row);
 }
 
 const char* qrita_strerror(int status) {

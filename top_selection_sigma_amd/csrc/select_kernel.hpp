@@ -30,6 +30,7 @@
 
 #include "device_common.hpp"
 #include "params.hpp"
+#include "philox.hpp"
 
 namespace qrita {
 
@@ -75,6 +76,9 @@ struct RowMode {
     float p;
     uint32_t K_t;  // ranks the candidate set must contain (0: mass-driven or none)
     bool need_cand;
+    bool sample_all;  // a draw over a row that keeps every token (needs its whole mass)
+    float p_table;    // the top-p the threshold table is read at
+    QRITA_DEV bool rest_on() const { return (topp && !topk) || sample_all; }
 };
 
 QRITA_DEV RowMode row_mode(const Params& P, int64_t row) {
@@ -101,6 +105,11 @@ QRITA_DEV RowMode row_mode(const Params& P, int64_t row) {
     else
         m.K_t = lcap < (uint32_t)V ? lcap : (uint32_t)V;
     m.need_cand = m.topk || m.topp || m.K_t > 0;
+    // a draw over a keep-all row: candidates as for top-p 0.999, the mass of
+    // the logits left out accumulated so that the draw can tell a miss
+    m.sample_all = P.out_token != nullptr && m.keep_all;
+    m.p_table = m.sample_all ? 0.999f : m.p;
+    if (m.sample_all) m.need_cand = true;
     return m;
 }
 
@@ -228,16 +237,15 @@ QRITA_DEV Thresh compute_threshold(const Params& P, const RowMode& md, const voi
     // the table entries depend on K, p and V only: read them while the sample
     // is in flight
     const float cap = qrita_lut_k[lut_k_index(1.0f / (float)V)];
-    float tab;
-    if (md.K_t > 0) {
-        tab = qrita_lut_k[lut_k_index((float)md.K_t / (float)V)];
-    } else {
-        const float s = 1.0f - md.p;
+    float tab = 0.0f, tabp = 0.0f;
+    if (md.K_t > 0) tab = qrita_lut_k[lut_k_index((float)md.K_t / (float)V)];
+    if (md.K_t == 0 || md.sample_all) {
+        const float s = 1.0f - md.p_table;
         const float f = floorf((log2f(s) - QRITA_LUT_P_MIN) * QRITA_LUT_P_STEPS);
         const int i = (int)fminf(fmaxf(f, 0.0f), (float)(QRITA_LUT_P_N - 1));
-        tab = qrita_lut_p[i];
+        tabp = qrita_lut_p[i];
     }
-    asm volatile("" ::"s"(cap), "s"(tab));
+    asm volatile("" ::"s"(cap), "s"(tab), "s"(tabp));
     // mean, variance and range of the finite sample values in one reduction
     // (moments about the row's first logit c0, fixed reduction order)
     c0 = __builtin_isfinite(c0) ? c0 : 0.0f;
@@ -287,12 +295,16 @@ QRITA_DEV Thresh compute_threshold(const Params& P, const RowMode& md, const voi
         t = -kInf;
     } else {
         float delta;
+        // top-p: softmax mass of N(mu, sigma^2) above t is
+        // 1 - Phi((t - mu)/sigma - sigma); keep at least p of it, less a margin.
+        const float delta_p = fminf(sigma + tabp - 0.5f, cap);
         if (md.K_t > 0) {
             delta = tab;
+            // a draw over a keep-all row with index output: both the ranks
+            // and the mass must be covered
+            if (md.sample_all) delta = fminf(delta, delta_p);
         } else {
-            // top-p: softmax mass of N(mu, sigma^2) above t is
-            // 1 - Phi((t - mu)/sigma - sigma); keep at least p of it, less a margin.
-            delta = fminf(sigma + tab - 0.5f, cap);
+            delta = delta_p;
         }
         t = mu + P.delta_scale * delta * sigma;
     }
@@ -702,7 +714,7 @@ __global__ __launch_bounds__(THREADS, 4) void pass1_kernel(Params P) {
     __syncthreads();
     // a3: the single streaming pass over the slice
     const uint8_t fill = md.keep_all ? 1 : 0;
-    const bool rest_on = md.topp && !md.topk;
+    const bool rest_on = md.rest_on();
     uint64_t rest = 0;
     Spill sp{0u, 0u};
     if (rest_on)

@@ -677,7 +677,7 @@ struct MassOut {
 // candidates of value vx are the lowest of the set, so the correction applies
 // exactly to thresholds below vx, which only the lower end can be.
 struct MassSet {
-    float p;        // target fraction
+    double p;       // target fraction
     double rest;    // mass outside the source (top-p-only rows), relative to m
     bool need_all;  // the source must hold mass p itself (else a miss)
     uint32_t vx, dN;
@@ -691,7 +691,7 @@ struct MassSet {
 // (need_all and the source holds less than T).
 template <int NT, class C>
 QRITA_DEV bool search_mass(C& c, const MassSet& ms, float m, int64_t lo_in, int64_t hi_in, MassOut& out,
-                           uint64_t& Tq) {
+                           uint64_t& Tq, double* Stot = nullptr) {
     uint32_t lo = lo_in > 0 ? (uint32_t)lo_in : 0u;
     uint32_t hi = (uint32_t)hi_in;
     const uint64_t ex = ms.dN ? (uint64_t)ms.dN * mass_fx(ms.vx, m) : 0ull;
@@ -727,7 +727,10 @@ QRITA_DEV bool search_mass(C& c, const MassSet& ms, float m, int64_t lo_in, int6
             E.M[0] -= ex;
         }
         if (guard == 0) {
-            Tq = (uint64_t)ceil((double)ms.p * ((double)E.M[0] + ms.rest));
+            const double tot = (double)E.M[0] + ms.rest;
+            if (Stot) *Stot = tot;
+            Tq = (uint64_t)ceil(ms.p * tot);
+            Tq = Tq ? Tq : 1u;  // at least one unit of mass: the first token with mass
             if (ms.need_all && E.M[0] < Tq) return false;
         }
         if (!conf) {
@@ -846,8 +849,14 @@ struct RankOut {
     uint8_t* mrow;   // scattered mask bytes (null: none)
     uint32_t lmask;
     uint64_t* last;  // LDS word (null: none)
+    float* prob;     // probabilities beside the indices (null: none)
+    float mref;      // the row maximum the masses are taken against
+    double inv_s;    // 1 / the kept set's fixed-point mass
     QRITA_DEV void put(uint32_t r, uint64_t w) const {
-        if (r < lout) out[r] = (int32_t)cand_idx(w);
+        if (r < lout) {
+            out[r] = (int32_t)cand_idx(w);
+            if (prob) prob[r] = (float)((double)mass_fx(cand_key(w), mref) * inv_s);
+        }
         if (mrow && r < lmask) mrow[cand_idx(w)] = 1;
         if (last && r + 1 == lmask) *last = w;
     }
@@ -1162,10 +1171,11 @@ struct TailDiag {
 // candidates' indices.
 template <class T, class L>
 QRITA_DEV uint64_t tie_boundary(const L& lsrc, uint32_t v, uint32_t need, uint32_t N, uint32_t V, int mode,
-                                Shared& sh, int& rb, int& iters) {
+                                Shared& sh, int& rb, int& iters, bool exact = false) {
     constexpr int NT = T::NT;
     uint64_t b = (uint64_t)v << 32;
-    if (need >= N) return b;
+    if (need >= N && !exact) return b;  // all duplicates: the bound needs no index
+    need = need < N ? need : N;
     if (N <= kTieDirect) {
         const uint32_t lane = tid_here() & (kWave - 1);
         block_sync<NT>();
@@ -1216,6 +1226,9 @@ struct RowOut {
     uint8_t* mrow;   // mask row or null (keep-all rows: filled elsewhere)
     bool bitmap;     // mask written whole from an LDS bitmap
     uint32_t V;
+    float* prob;     // probabilities beside idx, or null
+    float mref;
+    double inv_s;
 };
 
 // Mask of the kept set {c >= B} from a pass over the candidates: bitmap, or
@@ -1300,7 +1313,7 @@ QRITA_DEV void emit_row(C& c, const L& lsrc, const RowOut& o, bool all, uint32_t
         const uint32_t cnt =
             gather_words<NT>(lsrc, a, T::CSORT, (uint64_t)(Lout > 0 ? vo : vf) << 32, ~0ull, ex, sh, c.rb);
         RankOut ro{o.idx, Lout, (mask && !o.bitmap) ? o.mrow : nullptr, mask ? L_ : 0u,
-                   (mask && o.bitmap) ? (uint64_t*)&sh.u32[0] : nullptr};
+                   (mask && o.bitmap) ? (uint64_t*)&sh.u32[0] : nullptr, o.prob, o.mref, o.inv_s};
         sort_words<T>(cnt, ex, ro, sh, c.rb);
         if (mask && o.bitmap) {
             lds_sync();
@@ -1318,7 +1331,7 @@ QRITA_DEV void emit_row(C& c, const L& lsrc, const RowOut& o, bool all, uint32_t
     if (Gi <= (uint32_t)T::CSORT) {
         SortExt ex;
         const uint32_t cnt = gather_words<NT>(lsrc, a, T::CSORT, (uint64_t)vo << 32, ~0ull, ex, sh, c.rb);
-        sort_words<T>(cnt, ex, RankOut{o.idx, Lout, nullptr, 0u, nullptr}, sh, c.rb);
+        sort_words<T>(cnt, ex, RankOut{o.idx, Lout, nullptr, 0u, nullptr, o.prob, o.mref, o.inv_s}, sh, c.rb);
         return;
     }
     // windows of CSORT ranks, each bounded by its own boundary word. The
@@ -1341,7 +1354,9 @@ QRITA_DEV void emit_row(C& c, const L& lsrc, const RowOut& o, bool all, uint32_t
         }
         SortExt ex;
         const uint32_t got = gather_words<NT>(lsrc, a, T::CSORT, Bn, prev, ex, sh, c.rb);
-        sort_words<T>(got, ex, RankOut{o.idx + done, cnt, nullptr, 0u, nullptr}, sh, c.rb);
+        sort_words<T>(got, ex,
+                      RankOut{o.idx + done, cnt, nullptr, 0u, nullptr, o.prob ? o.prob + done : nullptr, o.mref, o.inv_s},
+                      sh, c.rb);
         prev = Bn;
         done += cnt;
     }
@@ -1375,7 +1390,7 @@ QRITA_DEV bool finish_row(const Params& P, int64_t row, const RowMode& md, const
     uint32_t K = md.K;
     // a4: truncation hit test
     if (md.K_t > 0 && n < md.K_t) return false;
-    if (topp && n == 0) return false;
+    if ((topp || md.sample_all) && n == 0) return false;
     const float m = key_value(kmax);
     if (topp && m == -__builtin_inff()) {  // all -inf: keep one token
         topp = false;
@@ -1433,10 +1448,54 @@ QRITA_DEV bool finish_row(const Params& P, int64_t row, const RowMode& md, const
         needf = need;
     }
     const uint32_t Lk = all ? V : ngt + needf;
+    // the draw from the kept set (sampling calls): with S the kept set's mass
+    // (plus, for a keep-all row, the mass left out of the candidates) and u the
+    // row's uniform, the drawn token has the smallest rank whose cumulative mass
+    // reaches u * S: the mass search over the kept set with that target gives
+    // its value and its position j among that value's duplicates
+    double s_kept = 0.0;
+    int32_t token = -1;
+    if (P.out_token) {
+        if (m == -__builtin_inff()) {
+            // no finite logit: rank 0, the lowest index of the maximum
+            const CountOut r0 = search_count<NT, 0>(c, 0u, 1u, key_lo, n, (int64_t)kmax, 0u);
+            token = (int32_t)cand_idx(tie_boundary<T>(lsrc, r0.v, 1u, r0.N, V, c.mode, sh, c.rb, dg.iters, true));
+        } else {
+            MassSet ms{row_uniform(P.seed, P.offset, (uint64_t)row), 0.0, all, 0u, 0u};
+            int64_t lo = key_lo;
+            if (all) {
+                if (rest_fx) ms.rest = (double)rest_fx * (double)mass_f32(f32_key(__float_as_uint(rest_ref)), m);
+            } else {
+                ms.vx = vf;
+                ms.dN = Nf - needf;
+                lo = (int64_t)vf - 1;
+            }
+            MassOut mo;
+            uint64_t Tq = 0;
+            if (!search_mass<NT>(c, ms, m, lo, (int64_t)kmax, mo, Tq, &s_kept)) {
+                rb = c.rb;
+                dg.iters += c.iters;
+                return false;  // a keep-all row whose candidates miss the draw
+            }
+            const uint64_t e = mass_fx(mo.v, m);
+            uint32_t j = mo.N;
+            if (e > 0) {
+                const uint64_t d = Tq - mo.M_gt;
+                uint64_t jj = d / e + (d % e ? 1u : 0u);
+                jj = jj > mo.N ? mo.N : (jj < 1 ? 1 : jj);
+                j = (uint32_t)jj;
+            }
+            const uint32_t Nv = (!all && mo.v == vf) ? Nf : mo.N;
+            token = (int32_t)cand_idx(tie_boundary<T>(lsrc, mo.v, j, Nv, V, c.mode, sh, c.rb, dg.iters, true));
+        }
+    }
     RowOut o{(P.out_idx && P.idx_cap > 0) ? P.out_idx + row * (int64_t)P.idx_cap : nullptr, (uint32_t)P.idx_cap,
-             (P.mask && !md.keep_all) ? P.mask + row * (int64_t)V : nullptr, P.bitmap != 0, V};
+             (P.mask && !md.keep_all) ? P.mask + row * (int64_t)V : nullptr, P.bitmap != 0, V,
+             (P.out_prob && P.idx_cap > 0) ? P.out_prob + row * (int64_t)P.idx_cap : nullptr, m,
+             s_kept > 0.0 ? 1.0 / s_kept : 0.0};
     emit_row<T>(c, lsrc, o, all, vf, ngt, needf, Nf, Lk, key_lo, n, kmax, dg);
     if (P.out_count && threadIdx.x == 0) P.out_count[row] = (int32_t)Lk;
+    if (P.out_token && threadIdx.x == 0) P.out_token[row] = token;
     rb = c.rb;
     dg.iters += c.iters;
     return true;
@@ -1528,9 +1587,9 @@ QRITA_DEV TailOut tail_fallback(const Params& P, int64_t row, RowMode md, float 
             uint64_t* stage = (uint64_t*)dyn_lds();
             const uint32_t scap = (uint32_t)(T::LDS / 8);
             if (P.bf16)
-                cnt = collect_row<NT, true>(P, row, tr, md.topp && !md.topk, stage, scap, sh, rb, rest2, kmax2, ovf);
+                cnt = collect_row<NT, true>(P, row, tr, md.rest_on(), stage, scap, sh, rb, rest2, kmax2, ovf);
             else
-                cnt = collect_row<NT, false>(P, row, tr, md.topp && !md.topk, stage, scap, sh, rb, rest2, kmax2, ovf);
+                cnt = collect_row<NT, false>(P, row, tr, md.rest_on(), stage, scap, sh, rb, rest2, kmax2, ovf);
             if (ovf) break;
             if (threadIdx.x == 0) sh.cnt[0] = cnt;
             lds_sync();
