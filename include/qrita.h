@@ -50,7 +50,8 @@ extern "C" {
 /* Element type of the logits. */
 typedef enum {
     QRITA_F32 = 0,  /* IEEE float32 */
-    QRITA_BF16 = 1  /* bfloat16 (upper half of a float32) */
+    QRITA_BF16 = 1, /* bfloat16 (upper half of a float32) */
+    QRITA_F16 = 2   /* IEEE binary16 */
 } qrita_dtype_t;
 
 /* Return codes. */
@@ -83,7 +84,8 @@ size_t qrita_workspace_bytes(int64_t batch, int64_t vocab, int dtype, int64_t id
  * logits     device, [batch][vocab] contiguous rows of `dtype`; 16-byte aligned.
  * batch      rows (>= 0; 0 is a no-op).
  * vocab      logits per row, 1 .. 2^31 - 1.
- * dtype      QRITA_F32 or QRITA_BF16.
+ * dtype      QRITA_F32, QRITA_BF16 or QRITA_F16 (16-bit types are widened to
+ *            float32 exactly; order and ties are those of the logits).
  * k          device int32 [batch], or NULL (top-k off for all rows).
  * p          device float32 [batch], or NULL (top-p off for all rows).
  * out_mask   device uint8 [batch][vocab]: 1 = kept, 0 = dropped; or NULL.
@@ -135,6 +137,14 @@ int qrita_select(const void* logits, int64_t batch, int64_t vocab, int dtype,
  *   mask_mode    0 automatic; 1: pass 1 zero-fills the mask and the tail
  *                stores the kept bytes one by one (instead of the tail
  *                writing whole rows from an LDS bitmap).
+ *   idx_order    0: out_idx in rank order; 1: out_idx holds the first
+ *                min(count, idx_cap) kept indices in ascending vocabulary
+ *                order (the kept set itself is unchanged), for consumers
+ *                that gather from the kept set (a restricted vocabulary
+ *                of top-K marginals, beam pruning). Needs vocab + 64 <=
+ *                622080 (the row's bitmap in LDS); larger vocabularies
+ *                return QRITA_EINVAL. With qrita_sample, out_prob follows
+ *                the same order.
  */
 typedef struct {
     int32_t force_miss;
@@ -147,6 +157,7 @@ typedef struct {
     void* mid_event;
     int32_t tier;
     int32_t mask_mode;
+    int32_t idx_order;
 } qrita_options;
 
 #define QRITA_DIAG_FIELDS 8

@@ -66,6 +66,21 @@ def hardware_threads() -> int:
     return int(_load().oracle_hardware_threads())
 
 
+def _host_logits(logits, dtype):
+    """Host array and dtype code: "f32" float32 values; "bf16" and "f16"
+    uint16 bit patterns (an f16 array of float16 values is taken as its bits)."""
+    if dtype == "f32":
+        return np.ascontiguousarray(logits, dtype=np.float32), 0
+    if dtype == "bf16":
+        return np.ascontiguousarray(logits, dtype=np.uint16), 1
+    if dtype == "f16":
+        a = np.asarray(logits)
+        if a.dtype == np.float16:
+            a = a.view(np.uint16)
+        return np.ascontiguousarray(a, dtype=np.uint16), 2
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
 class OracleInputError(ValueError):
     pass
 
@@ -91,14 +106,7 @@ def select(logits: np.ndarray, dtype: str, k: Optional[np.ndarray], p: Optional[
     k: int32 [B] or None (top-k off); p: float32 [B] or None (top-p off).
     """
     lib = _load()
-    if dtype == "f32":
-        x = np.ascontiguousarray(logits, dtype=np.float32)
-        dt = 0
-    elif dtype == "bf16":
-        x = np.ascontiguousarray(logits, dtype=np.uint16)
-        dt = 1
-    else:
-        raise ValueError(f"unknown dtype {dtype!r}")
+    x, dt = _host_logits(logits, dtype)
     B, V = x.shape
     kk = None if k is None else np.ascontiguousarray(k, dtype=np.int32)
     pp = None if p is None else np.ascontiguousarray(p, dtype=np.float32)
@@ -152,14 +160,7 @@ def sample(logits: np.ndarray, dtype: str, k: Optional[np.ndarray], p: Optional[
            u: np.ndarray, idx_cap: int, nthreads: int = 0) -> SampleResult:
     """Select, then draw by inverse CDF over the kept set with the given uniforms."""
     lib = _load()
-    if dtype == "f32":
-        x = np.ascontiguousarray(logits, dtype=np.float32)
-        dt = 0
-    elif dtype == "bf16":
-        x = np.ascontiguousarray(logits, dtype=np.uint16)
-        dt = 1
-    else:
-        raise ValueError(f"unknown dtype {dtype!r}")
+    x, dt = _host_logits(logits, dtype)
     B, V = x.shape
     kk = None if k is None else np.ascontiguousarray(k, dtype=np.int32)
     pp = None if p is None else np.ascontiguousarray(p, dtype=np.float32)

@@ -15,7 +15,9 @@
  * algorithms ("Resultados"). The oracle is therefore that sort-based
  * definition written out, not the pivot algorithm:
  *
- *   1. decode each logit exactly to double (bf16: bits << 16 as float);
+ *   1. decode each logit exactly to double (bf16: bits << 16 as float;
+ *      f16: IEEE binary16, sign * 2^(e-15) * (1 + f/1024), or
+ *      sign * 2^-14 * f/1024 for subnormals);
  *      NaN and +inf are rejected, -inf is an ordinary value;
  *   2. order the indices by value descending, equal values by ascending
  *      index (-0.0 and +0.0 are equal values);
@@ -69,9 +71,29 @@ static int cmp_desc(const void *pa, const void *pb) {
     return (a->i < b->i) ? -1 : (a->i > b->i);
 }
 
+/* IEEE binary16 bits to double, from the format's definition: 1 sign bit,
+ * 5 exponent bits (bias 15), 10 fraction bits; exponent 0 is subnormal,
+ * exponent 31 is inf (fraction 0) or NaN. */
+static double half_to_double(uint16_t h) {
+    const int sign = (h >> 15) & 1;
+    const int e = (h >> 10) & 31;
+    const int f = h & 1023;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -24);                 /* 2^-14 * f / 2^10 */
+    else if (e == 31)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp(1.0 + (double)f / 1024.0, e - 15);
+    return sign ? -v : v;
+}
+
 static double decode(const void *logits, int dtype, int64_t off) {
     if (dtype == 0) {
         return (double)((const float *)logits)[off];
+    }
+    if (dtype == 2) {
+        return half_to_double(((const uint16_t *)logits)[off]);
     }
     uint32_t u = ((uint32_t)((const uint16_t *)logits)[off]) << 16;
     float f;
@@ -297,7 +319,7 @@ int oracle_sample(const void *logits, int64_t batch, int64_t vocab, int dtype, c
                   int32_t *count, int32_t *idx, float *prob, int64_t idx_cap, int nthreads,
                   int64_t *bad_row, int64_t *bad_col) {
     if (!logits || !u || !token || batch < 0 || vocab <= 0 || vocab > INT32_MAX ||
-        (dtype != 0 && dtype != 1) || idx_cap < 0)
+        (dtype < 0 || dtype > 2) || idx_cap < 0)
         return 1;
     if (batch == 0) return 0;
     if (nthreads <= 0) nthreads = oracle_hardware_threads();
@@ -340,7 +362,8 @@ int oracle_hardware_threads(void) {
 }
 
 /*
- * Select over `batch` rows of `vocab` logits (dtype 0 = float32, 1 = bf16 bits).
+ * Select over `batch` rows of `vocab` logits (dtype 0 = float32, 1 = bf16 bits,
+ * 2 = IEEE binary16 bits).
  * k, p: per-row controls (either may be NULL: that control is off).
  * mask [batch][vocab] uint8, idx [batch][idx_cap] int32, count [batch],
  * band_lo / band_hi [batch]: outputs, each may be NULL.
@@ -352,7 +375,7 @@ int oracle_select(const void *logits, int64_t batch, int64_t vocab, int dtype,
                   const int32_t *k, const float *p, uint8_t *mask, int32_t *idx,
                   int64_t idx_cap, int32_t *count, int32_t *band_lo, int32_t *band_hi,
                   int nthreads, int64_t *bad_row, int64_t *bad_col) {
-    if (!logits || batch < 0 || vocab <= 0 || vocab > INT32_MAX || (dtype != 0 && dtype != 1) ||
+    if (!logits || batch < 0 || vocab <= 0 || vocab > INT32_MAX || (dtype < 0 || dtype > 2) ||
         idx_cap < 0)
         return 1;
     if (batch == 0) return 0;

@@ -75,7 +75,7 @@ def _call(logits=FAKE, batch=4, vocab=100, dtype=0, k=FAKE + 4096, p=FAKE + 8192
     (dict(vocab=0), q.QRITA_EINVAL),
     (dict(vocab=-5), q.QRITA_EINVAL),
     (dict(vocab=1 << 31), q.QRITA_EINVAL),
-    (dict(dtype=2), q.QRITA_EINVAL),
+    (dict(dtype=3), q.QRITA_EINVAL),
     (dict(idx_cap=-1), q.QRITA_EINVAL),
     (dict(count=None), q.QRITA_EINVAL),                    # idx without count
     (dict(mask=None, idx=None, count=None), q.QRITA_EINVAL),
@@ -91,13 +91,26 @@ def test_argument_errors_return_before_launch(kw, code):
 
 
 def test_options_are_validated():
-    bad = [q._Options(0, 0.0, 3, 0, 0, 0, None, None, 0, 0), q._Options(0, 0.0, 0, -1, 0, 0, None, None, 0, 0),
-           q._Options(0, float("nan"), 0, 0, 0, 0, None, None, 0, 0),
-           q._Options(0, 0.0, 0, 0, -3, 0, None, None, 0, 0),
-           q._Options(0, 0.0, 0, 0, 0, 0, None, None, 3, 0),
-           q._Options(0, 0.0, 0, 0, 0, 0, None, None, 0, 2)]
+    bad = [q._Options(0, 0.0, 3, 0, 0, 0, None, None, 0, 0, 0), q._Options(0, 0.0, 0, -1, 0, 0, None, None, 0, 0, 0),
+           q._Options(0, float("nan"), 0, 0, 0, 0, None, None, 0, 0, 0),
+           q._Options(0, 0.0, 0, 0, -3, 0, None, None, 0, 0, 0),
+           q._Options(0, 0.0, 0, 0, 0, 0, None, None, 3, 0, 0),
+           q._Options(0, 0.0, 0, 0, 0, 0, None, None, 0, 2, 0),
+           q._Options(0, 0.0, 0, 0, 0, 0, None, None, 0, 0, 2),
+           q._Options(0, 0.0, 0, 0, 0, 0, None, None, 0, 0, -1)]
     for o in bad:
         assert _call(opt=o) == q.QRITA_EINVAL
+
+
+def test_index_order_rejects_rows_beyond_the_lds_bitmap():
+    """Index-ordered output keeps the row's bitmap in LDS: at most 622016
+    logits (the heavy tier); longer rows are refused before any HIP call."""
+    o = q._Options(0, 0.0, 0, 0, 0, 0, None, None, 0, 0, 1)
+    assert _call(vocab=622017, opt=o) == q.QRITA_EINVAL
+    assert _call(vocab=1 << 24, opt=o) == q.QRITA_EINVAL
+    # the light tier forced on a row beyond its bitmap
+    o = q._Options(0, 0.0, 0, 0, 0, 0, None, None, 1, 0, 1)
+    assert _call(vocab=400000, opt=o) == q.QRITA_EINVAL
 
 
 def test_product_path_has_no_cpu_fallback():
@@ -145,7 +158,7 @@ def test_sample_argument_errors_return_before_launch():
     assert _sample(prob=FAKE + (3 << 20), idx=None, count=None) == q.QRITA_EINVAL  # prob without idx
     assert _sample(logits=None) == q.QRITA_EINVAL
     assert _sample(ws=None) == q.QRITA_EWORKSPACE
-    assert _sample(opt=q._Options(0, 0.0, 7, 0, 0, 0, None, None, 0, 0)) == q.QRITA_EINVAL
+    assert _sample(opt=q._Options(0, 0.0, 7, 0, 0, 0, None, None, 0, 0, 0)) == q.QRITA_EINVAL
     assert _sample(batch=0) == q.QRITA_OK
     # token alone is a valid output set (checked up to the workspace)
     assert _sample(mask=None, idx=None, count=None, ws=None) == q.QRITA_EWORKSPACE

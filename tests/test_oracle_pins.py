@@ -306,3 +306,76 @@ def test_threads_do_not_change_results():
     b = oracle.select(x.logits, "bf16", x.k, x.p, 100, nthreads=5)
     for f in ("mask", "idx", "count", "band_lo", "band_hi"):
         assert np.array_equal(getattr(a, f), getattr(b, f))
+
+
+# ---------------------------------------------------------------------------
+# IEEE binary16 logits: the oracle's own decode of the bit patterns against
+# NumPy's float16 -> float32 conversion (exact), over every finite pattern
+# ---------------------------------------------------------------------------
+
+def _all_finite_f16_bits():
+    b = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    v = b.view(np.float16)
+    keep = np.isfinite(v) | (v == -np.inf)
+    return b[keep]
+
+
+def test_f16_decode_matches_numpy_over_every_pattern():
+    """Every finite binary16 pattern (and -inf), shuffled into rows: the full
+    order, masks and top-p cuts from the f16 bits equal those from the same
+    values widened by NumPy and passed as float32."""
+    bits = _all_finite_f16_bits()
+    rng = np.random.default_rng(5)
+    bits = bits[rng.permutation(len(bits))]
+    V = 2048
+    n = (len(bits) // V) * V
+    X16 = bits[:n].reshape(-1, V)
+    X32 = X16.view(np.float16).astype(np.float32)
+    B = X16.shape[0]
+    k = rng.integers(0, V + 1, B).astype(np.int32)
+    p = np.where(rng.random(B) < 0.5, rng.uniform(0.01, 1.0, B), 1.0).astype(np.float32)
+    a = oracle.select(X16, "f16", k, p, V)
+    b = oracle.select(X32, "f32", k, p, V)
+    assert np.array_equal(a.count, b.count)
+    assert np.array_equal(a.mask, b.mask)
+    assert np.array_equal(a.idx, b.idx)
+    assert np.array_equal(a.band_lo, b.band_lo) and np.array_equal(a.band_hi, b.band_hi)
+    # and the full order is NumPy's stable descending sort of the float64 values
+    full = oracle.select(X16, "f16", None, None, V)
+    for r in range(0, B, 7):
+        want = np.argsort(-X16[r].view(np.float16).astype(np.float64), kind="stable")
+        assert np.array_equal(full.idx[r], want)
+
+
+def test_f16_rejects_nan_and_pos_inf():
+    x = np.zeros((2, 8), np.float16)
+    x[1, 3] = np.inf
+    with pytest.raises(oracle.OracleInputError, match="row 1, column 3"):
+        oracle.select(x, "f16", None, None, 4)
+    x[1, 3] = np.nan
+    with pytest.raises(oracle.OracleInputError):
+        oracle.select(x, "f16", None, None, 4)
+
+
+def test_f16_decoded_values_through_a_closed_form():
+    """Each finite binary16 value v with |v| <= 16 (subnormals included) in a
+    two-logit row [v, 0]: the kept set's renormalised probability of the
+    first logit is 1 / (1 + exp(-v)) for v >= 0 (v is rank 0) and
+    1 / (1 + exp(v)) for v < 0 (0 is rank 0), with v from NumPy's conversion.
+    A decode that is off in scale, bias or subnormal step moves the value."""
+    bits = _all_finite_f16_bits()
+    v = bits.view(np.float16).astype(np.float64)
+    sel = np.abs(v) <= 16.0
+    bits, v = bits[sel], v[sel]
+    X = np.zeros((len(bits), 2), np.uint16)
+    X[:, 0] = bits
+    X[:, 1] = np.float16(0.0).view(np.uint16)
+    u = np.zeros(len(bits))
+    r = oracle.sample(X, "f16", None, None, u, 2)
+    top = r.prob[:, 0].astype(np.float64)
+    want = np.where(v >= 0, 1.0 / (1.0 + np.exp(-v)), 1.0 / (1.0 + np.exp(v)))
+    np.testing.assert_allclose(top, want, rtol=2e-7, atol=0)
+    # subnormals are not flushed: the smallest one still moves the rank-0 logit
+    sub = (np.abs(v) > 0) & (np.abs(v) < 2.0**-14)
+    assert np.any(sub)
+    assert np.all(r.idx[sub & (v > 0), 0] == 0) and np.all(r.idx[sub & (v < 0), 0] == 1)

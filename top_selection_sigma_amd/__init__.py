@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libqrita.so")
 
 QRITA_F32 = 0
 QRITA_BF16 = 1
+QRITA_F16 = 2
 QRITA_OK = 0
 QRITA_EINVAL = 1
 QRITA_EWORKSPACE = 2
@@ -52,6 +53,7 @@ class _Options(ctypes.Structure):
         ("mid_event", ctypes.c_void_p),
         ("tier", ctypes.c_int32),
         ("mask_mode", ctypes.c_int32),
+        ("idx_order", ctypes.c_int32),
     ]
 
 
@@ -69,13 +71,14 @@ class Options:
     mid_event: object = None  # torch.cuda.Event (already recorded once) or None
     tier: int = 0             # 0 automatic, 1 light, 2 heavy
     mask_mode: int = 0        # 0 automatic, 1 mask bytes stored one by one
+    idx_order: int = 0        # 0 rank order, 1 ascending vocabulary index
 
     def to_c(self) -> _Options:
         return _Options(int(self.force_miss), float(self.delta_scale), int(self.pivot_mode),
                         int(self.slices), int(self.lds_cap), int(self.list_cap),
                         None if self.diag is None else self.diag.data_ptr(),
                         None if self.mid_event is None else self.mid_event.cuda_event,
-                        int(self.tier), int(self.mask_mode))
+                        int(self.tier), int(self.mask_mode), int(self.idx_order))
 
 
 def lib() -> ctypes.CDLL:
@@ -138,7 +141,9 @@ def dtype_code(t) -> int:
         return QRITA_F32
     if t.dtype == torch.bfloat16:
         return QRITA_BF16
-    raise TypeError(f"logits must be float32 or bfloat16, got {t.dtype}")
+    if t.dtype == torch.float16:
+        return QRITA_F16
+    raise TypeError(f"logits must be float32, bfloat16 or float16, got {t.dtype}")
 
 
 def qrita_select(logits, k, p, out_mask, out_idx, out_count, idx_cap: int, workspace,

@@ -9,6 +9,24 @@
 
 namespace qrita {
 
+// Logit element types (the dtype codes of the C ABI): 0 float32, 1 bfloat16,
+// 2 float16. Both 16-bit types widen to float32 exactly, and keys are taken
+// from the widened value, so ordering and equality are those of the logits.
+template <int DT>
+inline constexpr bool kW16 = DT != 0;  // 16-bit elements
+
+// The 16-bit element in the low / high half of a 32-bit word, widened.
+template <int DT>
+QRITA_DEV float lo16(uint32_t w) {
+    if constexpr (DT == 1) return __uint_as_float(w << 16);
+    else return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
+}
+template <int DT>
+QRITA_DEV float hi16(uint32_t w) {
+    if constexpr (DT == 1) return __uint_as_float(w & 0xFFFF0000u);
+    else return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+
 constexpr int kWave = 64;
 constexpr int kMaxWaves = 16;
 

@@ -9,7 +9,7 @@
 namespace qrita {
 
 // pass 1 over `groups` workgroups of 256 threads with `lds` bytes of dynamic LDS
-hipError_t launch_pass1(const Params& P, unsigned groups, size_t lds, bool bf16, hipStream_t stream);
+hipError_t launch_pass1(const Params& P, unsigned groups, size_t lds, hipStream_t stream);
 // the tail, one workgroup per row, light tier (two workgroups per CU)
 hipError_t launch_tail_light(const Params& P, hipStream_t stream);
 // the tail, heavy tier (one workgroup per CU, twice the capacities)

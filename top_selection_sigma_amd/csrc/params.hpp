@@ -31,7 +31,8 @@ struct Params {
     float delta_scale;
     int32_t pivot_mode;  // 0 key quartiles, 1 value quartiles, 2 one pivot at the key midpoint
     int32_t bitmap;      // 1: the tail writes whole mask rows; pass 1 leaves the mask alone
-    int32_t bf16;
+    int32_t dtype;  // 0 float32, 1 bfloat16, 2 float16
+    int32_t idx_order;  // out_idx in ascending vocabulary index instead of rank order
     int32_t* out_token;  // sampling: [batch] drawn token, or null (no draw)
     float* out_prob;     // sampling: [batch][idx_cap] probabilities beside out_idx, or null
     uint64_t seed;       // sampling: Philox key

@@ -50,6 +50,8 @@ struct Plan {
     bool bitmap;     // the tail writes whole mask rows
 };
 
+bool dtype_ok(int d) { return d == QRITA_F32 || d == QRITA_BF16 || d == QRITA_F16; }
+
 // The tier table (the summary's tiered block sizes, "Autotuning": large blocks
 // for full rows, small ones for truncated sets), a static function of the
 // call's shape (B rows, V logits of `esize` bytes, idx_cap for the expected
@@ -86,6 +88,8 @@ Plan choose_plan(int64_t B, int64_t V, int64_t esize, int64_t idx_cap, const qri
     if (o && o->lds_cap > 0) stage = std::max(64, std::min(stage, (int)o->lds_cap));
     t.stage_cap = stage;
     t.heavy = B < 256 || idx_cap > 4096;
+    // index-ordered output needs the row's bitmap in LDS
+    if (o && o->idx_order && V + 64 > (int64_t)qrita::tier_light().bitmap_bits) t.heavy = true;
     if (o && o->tier == 1) t.heavy = false;
     if (o && o->tier == 2) t.heavy = true;
     const qrita::TierInfo ti = t.heavy ? qrita::tier_heavy() : qrita::tier_light();
@@ -128,7 +132,8 @@ struct Draw {
 bool options_valid(const qrita_options* opt) {
     return !opt || !(((uintptr_t)opt->diag & 3u) || opt->pivot_mode < 0 || opt->pivot_mode > 2 ||
                      opt->slices < 0 || opt->lds_cap < 0 || opt->list_cap < 0 || opt->tier < 0 ||
-                     opt->tier > 2 || opt->mask_mode < 0 || opt->mask_mode > 1 ||
+                     opt->tier > 2 || opt->mask_mode < 0 || opt->mask_mode > 1 || opt->idx_order < 0 ||
+                     opt->idx_order > 1 ||
                      !(opt->delta_scale == opt->delta_scale));
 }
 
@@ -139,7 +144,7 @@ int select_impl(const void* logits, int64_t batch, int64_t vocab, int dtype, con
     if (!logits || batch < 0 || vocab <= 0 || vocab > INT32_MAX || idx_cap < 0 ||
         idx_cap > INT32_MAX)
         return QRITA_EINVAL;
-    if (dtype != QRITA_F32 && dtype != QRITA_BF16) return QRITA_EINVAL;
+    if (!dtype_ok(dtype)) return QRITA_EINVAL;
     if (out_idx && !out_count) return QRITA_EINVAL;
     if (!out_mask && !out_idx && !out_count && !draw) return QRITA_EINVAL;
     if (draw && (!draw->token || ((uintptr_t)draw->token & 3u) || ((uintptr_t)draw->prob & 3u) ||
@@ -154,10 +159,14 @@ int select_impl(const void* logits, int64_t batch, int64_t vocab, int dtype, con
     const size_t need = qrita_workspace_bytes(batch, vocab, dtype, idx_cap);
     if (!workspace || workspace_bytes < need) return QRITA_EWORKSPACE;
     if ((uintptr_t)workspace & 255u) return QRITA_EWORKSPACE;
+    const int64_t esize = dtype == QRITA_F32 ? 4 : 2;
+    const Plan t = choose_plan(batch, vocab, esize, out_idx ? idx_cap : 0, opt);
+    if (opt && opt->idx_order) {
+        const qrita::TierInfo ti = t.heavy ? qrita::tier_heavy() : qrita::tier_light();
+        if (vocab + 64 > (int64_t)ti.bitmap_bits) return QRITA_EINVAL;
+    }
     if (!device_supported()) return QRITA_EUNSUPPORTED;
 
-    const bool bf16 = dtype == QRITA_BF16;
-    const Plan t = choose_plan(batch, vocab, bf16 ? 2 : 4, out_idx ? idx_cap : 0, opt);
     const WsLayout w = ws_layout(batch, vocab);
     Params P;
     std::memset(&P, 0, sizeof P);
@@ -185,7 +194,8 @@ int select_impl(const void* logits, int64_t batch, int64_t vocab, int dtype, con
     P.delta_scale = (opt && opt->delta_scale != 0.0f) ? opt->delta_scale : 1.0f;
     P.pivot_mode = opt ? opt->pivot_mode : 0;
     P.bitmap = t.bitmap ? 1 : 0;
-    P.bf16 = bf16 ? 1 : 0;
+    P.dtype = dtype;
+    P.idx_order = (opt && opt->idx_order) ? 1 : 0;
     if (draw) {
         P.out_token = draw->token;
         P.out_prob = draw->prob;
@@ -196,7 +206,7 @@ int select_impl(const void* logits, int64_t batch, int64_t vocab, int dtype, con
     hipStream_t s = (hipStream_t)stream;
     const unsigned groups = (unsigned)(((batch + 7) / 8) * 8 * (int64_t)t.slices);
     const size_t lds = ((size_t)std::max(t.stage_cap, kSampleN) + (size_t)(kPass1Threads / 64) * kWaveSpill) * 8;
-    if (qrita::launch_pass1(P, groups, lds, bf16, s) != hipSuccess) return QRITA_ELAUNCH;
+    if (qrita::launch_pass1(P, groups, lds, s) != hipSuccess) return QRITA_ELAUNCH;
     if (opt && opt->mid_event) {
         if (hipEventRecord((hipEvent_t)opt->mid_event, s) != hipSuccess) return QRITA_ELAUNCH;
     }
@@ -239,7 +249,7 @@ int qrita_select_noalloc(const void* logits, int64_t batch, int64_t vocab, int d
     // shape and argument checks first (nothing touches the GPU before them)
     if (!logits || batch < 0 || vocab <= 0 || vocab > INT32_MAX || idx_cap < 0 || idx_cap > INT32_MAX)
         return QRITA_EINVAL;
-    if (dtype != QRITA_F32 && dtype != QRITA_BF16) return QRITA_EINVAL;
+    if (!dtype_ok(dtype)) return QRITA_EINVAL;
     if (batch == 0) return QRITA_OK;
     if (qrita_workspace_bytes(batch, vocab, dtype, idx_cap) > (size_t)QRITA_NOALLOC_SCRATCH_BYTES)
         return QRITA_ESCRATCH;
@@ -256,7 +266,7 @@ int qrita_select_noalloc(const void* logits, int64_t batch, int64_t vocab, int d
 size_t qrita_workspace_bytes(int64_t batch, int64_t vocab, int dtype, int64_t idx_cap) {
     (void)idx_cap;
     if (batch < 0 || vocab <= 0 || vocab > INT32_MAX) return 0;
-    if (dtype != QRITA_F32 && dtype != QRITA_BF16) return 0;
+    if (!dtype_ok(dtype)) return 0;
     return (size_t)ws_layout(batch, vocab).total;
 }
 

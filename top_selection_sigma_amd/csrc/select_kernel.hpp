@@ -102,8 +102,10 @@ QRITA_DEV RowMode row_mode(const Params& P, int64_t row) {
         m.K_t = m.K;
     else if (m.topp)
         m.K_t = 0;
-    else
+    else if (!P.idx_order)
         m.K_t = lcap < (uint32_t)V ? lcap : (uint32_t)V;
+    else
+        m.K_t = 0;  // keep-all rows in index order: indices 0, 1, ... need no candidates
     m.need_cand = m.topk || m.topp || m.K_t > 0;
     // a draw over a keep-all row: candidates as for top-p 0.999, the mass of
     // the logits left out accumulated so that the draw can tell a miss
@@ -114,19 +116,16 @@ QRITA_DEV RowMode row_mode(const Params& P, int64_t row) {
 }
 
 
-template <bool BF16>
+template <int DT>
 QRITA_DEV float load_value(const void* rowp, int64_t e) {
-    if (BF16) {
-        const uint32_t u = ((const uint16_t*)rowp)[e];
-        return __uint_as_float(u << 16);
-    }
-    return ((const float*)rowp)[e];
+    if constexpr (kW16<DT>) return lo16<DT>(((const uint16_t*)rowp)[e]);
+    else return ((const float*)rowp)[e];
 }
 
-template <bool BF16>
+template <int DT>
 QRITA_DEV const void* row_ptr(const Params& P, int64_t row) {
     const int64_t roff = row * (int64_t)P.vocab;
-    return BF16 ? (const void*)((const uint16_t*)P.logits + roff)
+    return kW16<DT> ? (const void*)((const uint16_t*)P.logits + roff)
                 : (const void*)((const float*)P.logits + roff);
 }
 
@@ -186,26 +185,26 @@ QRITA_DEV int lut_k_index(float ratio) {
 // evenly spaced offsets (the whole row when it has at most 2048 logits). A
 // thread's 8 logits are consecutive; away from the row's ends each run is
 // moved down to a 16-byte boundary and read with vector loads.
-template <bool BF16>
+template <int DT>
 QRITA_DEV void load_sample(const void* rowp, int32_t V, float x[8], bool in[8]) {
     const int tid = threadIdx.x;
     const bool whole = V <= kSampleN;
     int64_t pos0 =
         whole ? (int64_t)tid * 8
               : ((int64_t)(tid >> 5) * (int64_t)(V - kSampleChunk)) / (kSampleChunks - 1) + (int64_t)(tid & 31) * 8;
-    constexpr int64_t ES = BF16 ? 2 : 4;
-    const int64_t mis = (int64_t)(((uintptr_t)rowp / ES + (uint64_t)pos0) & (BF16 ? 7 : 3));
+    constexpr int64_t ES = kW16<DT> ? 2 : 4;
+    const int64_t mis = (int64_t)(((uintptr_t)rowp / ES + (uint64_t)pos0) & (kW16<DT> ? 7 : 3));
     if (!whole && tid < kSampleN / 8 && pos0 >= mis && pos0 - mis + 8 <= V) {
         pos0 -= mis;
 #pragma unroll
         for (int i = 0; i < 8; ++i) in[i] = true;
-        if (BF16) {
+        if (kW16<DT>) {
             const u32x4_t w = *(const u32x4_t*)((const uint16_t*)rowp + pos0);
             const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                x[2 * r] = __uint_as_float(ws[r] << 16);
-                x[2 * r + 1] = __uint_as_float(ws[r] & 0xFFFF0000u);
+                x[2 * r] = lo16<DT>(ws[r]);
+                x[2 * r + 1] = hi16<DT>(ws[r]);
             }
         } else {
             const f32x4_t a = *(const f32x4_t*)((const float*)rowp + pos0);
@@ -219,12 +218,12 @@ QRITA_DEV void load_sample(const void* rowp, int32_t V, float x[8], bool in[8]) 
     for (int i = 0; i < 8; ++i) {
         const int64_t e = pos0 + i;
         in[i] = tid < kSampleN / 8 && e < V;
-        x[i] = in[i] ? load_value<BF16>(rowp, e) : 0.0f;
+        x[i] = in[i] ? load_value<DT>(rowp, e) : 0.0f;
     }
 }
 
 
-template <int THREADS, bool BF16>
+template <int THREADS, int DT>
 QRITA_DEV Thresh compute_threshold(const Params& P, const RowMode& md, const void* rowp, const float (&x)[8],
                                    const bool (&in)[8], float c0, Shared& sh, int& rb) {
     constexpr int NW = THREADS / kWave;
@@ -414,7 +413,7 @@ QRITA_DEV void wave_spill_flush(const Params& P, uint64_t* sub, const uint64_t* 
 // key, for the list's max). For top-p-only rows (REST) the dropped logits'
 // masses exp(f - tc) are summed per lane in float over the 16 and added to
 // the fixed-point `rest` once, so the total does not depend on lane order.
-template <int THREADS, bool BF16, bool REST, int VE>
+template <int THREADS, int DT, bool REST, int VE>
 QRITA_DEV void consume16(const Params& P, uint64_t* sub, const float f[16], uint32_t valid, uint32_t idx0,
                          uint32_t vstride, float tc, Shared& sh, uint64_t& rest, Spill& sp) {
     const uint32_t lane = threadIdx.x & (kWave - 1);
@@ -497,35 +496,35 @@ QRITA_DEV void consume16(const Params& P, uint64_t* sub, const float f[16], uint
 // are read once), and unpacked to float only when consumed, so that several
 // tiles can be in flight per lane: kTileDepth tiles, 96 bytes of bf16 or
 // 128 bytes of f32 per lane, 96-128 KiB per CU at four workgroups.
-template <bool BF16>
+template <int DT>
 struct RawTile {
-    u32x4_t v[BF16 ? 2 : 4];
+    u32x4_t v[kW16<DT> ? 2 : 4];
 };
-template <bool BF16>
-constexpr int kTileDepth = BF16 ? 3 : 2;
+template <int DT>
+constexpr int kTileDepth = kW16<DT> ? 3 : 2;
 
-template <int THREADS, bool BF16>
-QRITA_DEV void load_raw(const void* rowp, int64_t tile, RawTile<BF16>& r) {
-    constexpr int VE = BF16 ? 8 : 4;
+template <int THREADS, int DT>
+QRITA_DEV void load_raw(const void* rowp, int64_t tile, RawTile<DT>& r) {
+    constexpr int VE = kW16<DT> ? 8 : 4;
     constexpr int NV = 16 / VE;
 #pragma unroll
     for (int q = 0; q < NV; ++q) {
         const int64_t e = tile + (int64_t)q * THREADS * VE + (int64_t)threadIdx.x * VE;
-        const u32x4_t* src = BF16 ? (const u32x4_t*)((const uint16_t*)rowp + e) : (const u32x4_t*)((const float*)rowp + e);
+        const u32x4_t* src = kW16<DT> ? (const u32x4_t*)((const uint16_t*)rowp + e) : (const u32x4_t*)((const float*)rowp + e);
         r.v[q] = __builtin_nontemporal_load(src);
     }
 }
 
-template <bool BF16>
-QRITA_DEV void unpack_tile(const RawTile<BF16>& r, float f[16]) {
-    if (BF16) {
+template <int DT>
+QRITA_DEV void unpack_tile(const RawTile<DT>& r, float f[16]) {
+    if (kW16<DT>) {
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
             const uint32_t ws[4] = {r.v[q].x, r.v[q].y, r.v[q].z, r.v[q].w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                f[q * 8 + 2 * i] = __uint_as_float(ws[i] << 16);
-                f[q * 8 + 2 * i + 1] = __uint_as_float(ws[i] & 0xFFFF0000u);
+                f[q * 8 + 2 * i] = lo16<DT>(ws[i]);
+                f[q * 8 + 2 * i + 1] = hi16<DT>(ws[i]);
             }
         }
     } else {
@@ -540,15 +539,15 @@ QRITA_DEV void unpack_tile(const RawTile<BF16>& r, float f[16]) {
 }
 
 // The mask bytes of one full tile (this lane's 16 entries).
-template <int THREADS, bool BF16>
+template <int THREADS, int DT>
 QRITA_DEV void fill_tile(uint8_t* mrow, int64_t tile, uint8_t fill) {
-    constexpr int VE = BF16 ? 8 : 4;
+    constexpr int VE = kW16<DT> ? 8 : 4;
     constexpr int NV = 16 / VE;
     const uint64_t fill8 = 0x0101010101010101ull * fill;
 #pragma unroll
     for (int q = 0; q < NV; ++q) {
         const int64_t e = tile + (int64_t)q * THREADS * VE + (int64_t)threadIdx.x * VE;
-        if (BF16)
+        if (kW16<DT>)
             __builtin_nontemporal_store(fill8, (uint64_t*)(mrow + e));
         else
             __builtin_nontemporal_store((uint32_t)fill8, (uint32_t*)(mrow + e));
@@ -564,12 +563,12 @@ QRITA_DEV int64_t aligned_start(int64_t roff, int64_t e0, int64_t e1) {
 
 // The streaming pass over [e0, e1); ring[j] holds the slice's full tile j
 // for j < kTileDepth (loaded before the threshold was known).
-template <int THREADS, bool BF16, bool REST>
+template <int THREADS, int DT, bool REST>
 QRITA_DEV void stream_slice(const Params& P, int64_t row, uint64_t* sub, int64_t e0, int64_t e1, float tc,
-                            uint8_t fill, RawTile<BF16> (&ring)[kTileDepth<BF16>], Shared& sh, uint64_t& rest,
+                            uint8_t fill, RawTile<DT> (&ring)[kTileDepth<DT>], Shared& sh, uint64_t& rest,
                             Spill& sp) {
     const int64_t roff = row * (int64_t)P.vocab;
-    const void* rowp = row_ptr<BF16>(P, row);
+    const void* rowp = row_ptr<DT>(P, row);
     // the mask slice is filled here only when the tail does not write whole rows
     uint8_t* mrow = (P.mask && !P.bitmap) ? P.mask + roff : nullptr;
     const int tid = threadIdx.x;
@@ -582,17 +581,17 @@ QRITA_DEV void stream_slice(const Params& P, int64_t row, uint64_t* sub, int64_t
         for (int j = 0; j < 16; ++j) f[j] = 0.0f;
         const int64_t e = e0 + tid;
         if (e < a) {
-            f[0] = load_value<BF16>(rowp, e);
+            f[0] = load_value<DT>(rowp, e);
             valid = 1;
             if (mrow) mrow[e] = fill;
         }
         if (tid < kWave)
-            consume16<THREADS, BF16, REST, 16>(P, sub, f, valid, (uint32_t)e, 0u, tc, sh, rest, sp);
+            consume16<THREADS, DT, REST, 16>(P, sub, f, valid, (uint32_t)e, 0u, tc, sh, rest, sp);
     }
-    constexpr int VE = BF16 ? 8 : 4;  // logits per 16-byte vector
+    constexpr int VE = kW16<DT> ? 8 : 4;  // logits per 16-byte vector
     constexpr int NV = 16 / VE;       // vectors per thread per tile
     constexpr int TB = THREADS * 16;  // logits per tile
-    constexpr int D = kTileDepth<BF16>;
+    constexpr int D = kTileDepth<DT>;
     // full tiles: tile i sits in ring[i % D]; once unpacked, its slot is
     // refilled with tile i + D
     const int64_t nfull = (e1 - a) / TB;
@@ -603,10 +602,10 @@ QRITA_DEV void stream_slice(const Params& P, int64_t row, uint64_t* sub, int64_t
             if (i < nfull) {
                 const int64_t tile = a + i * TB;
                 float f[16];
-                unpack_tile<BF16>(ring[j], f);
-                if (i + D < nfull) load_raw<THREADS, BF16>(rowp, tile + (int64_t)D * TB, ring[j]);
-                if (mrow) fill_tile<THREADS, BF16>(mrow, tile, fill);
-                consume16<THREADS, BF16, REST, VE>(P, sub, f, 0xFFFFu, (uint32_t)(tile + (int64_t)tid * VE),
+                unpack_tile<DT>(ring[j], f);
+                if (i + D < nfull) load_raw<THREADS, DT>(rowp, tile + (int64_t)D * TB, ring[j]);
+                if (mrow) fill_tile<THREADS, DT>(mrow, tile, fill);
+                consume16<THREADS, DT, REST, VE>(P, sub, f, 0xFFFFu, (uint32_t)(tile + (int64_t)tid * VE),
                                                    (uint32_t)(THREADS * VE), tc, sh, rest, sp);
             }
         }
@@ -622,18 +621,18 @@ QRITA_DEV void stream_slice(const Params& P, int64_t row, uint64_t* sub, int64_t
         for (int q = 0; q < NV; ++q) {
             const int64_t ev = tile + (int64_t)q * THREADS * VE + (int64_t)tid * VE;
             if (ev + VE <= e1) {
-                RawTile<BF16> r1;
-                const u32x4_t* src = BF16 ? (const u32x4_t*)((const uint16_t*)rowp + ev)
+                RawTile<DT> r1;
+                const u32x4_t* src = kW16<DT> ? (const u32x4_t*)((const uint16_t*)rowp + ev)
                                           : (const u32x4_t*)((const float*)rowp + ev);
                 r1.v[0] = __builtin_nontemporal_load(src);
                 const uint32_t ws[4] = {r1.v[0].x, r1.v[0].y, r1.v[0].z, r1.v[0].w};
 #pragma unroll
                 for (int r = 0; r < VE; ++r)
-                    f[q * VE + r] = BF16 ? __uint_as_float((r & 1) ? (ws[r / 2] & 0xFFFF0000u) : (ws[r / 2] << 16))
-                                         : __uint_as_float(ws[r]);
+                    f[q * VE + r] = kW16<DT> ? ((r & 1) ? hi16<DT>(ws[r / 2]) : lo16<DT>(ws[r / 2]))
+                                             : __uint_as_float(ws[r]);
                 valid |= ((1u << VE) - 1u) << (q * VE);
                 if (mrow) {
-                    if (BF16)
+                    if (kW16<DT>)
                         __builtin_nontemporal_store(fill8, (uint64_t*)(mrow + ev));
                     else
                         __builtin_nontemporal_store((uint32_t)fill8, (uint32_t*)(mrow + ev));
@@ -643,7 +642,7 @@ QRITA_DEV void stream_slice(const Params& P, int64_t row, uint64_t* sub, int64_t
                 for (int r = 0; r < VE; ++r) {
                     const int64_t er = ev + r;
                     if (er < e1) {
-                        f[q * VE + r] = load_value<BF16>(rowp, er);
+                        f[q * VE + r] = load_value<DT>(rowp, er);
                         valid |= 1u << (q * VE + r);
                         if (mrow) mrow[er] = fill;
                     } else {
@@ -652,7 +651,7 @@ QRITA_DEV void stream_slice(const Params& P, int64_t row, uint64_t* sub, int64_t
                 }
             }
         }
-        consume16<THREADS, BF16, REST, VE>(P, sub, f, valid, (uint32_t)(tile + (int64_t)tid * VE),
+        consume16<THREADS, DT, REST, VE>(P, sub, f, valid, (uint32_t)(tile + (int64_t)tid * VE),
                                            (uint32_t)(THREADS * VE), tc, sh, rest, sp);
     }
 }
@@ -662,7 +661,7 @@ QRITA_DEV void stream_slice(const Params& P, int64_t row, uint64_t* sub, int64_t
 // one L2, which also holds the row list when the row's tail (workgroup r of
 // the next launch, on the same XCD) reads it. A slice writes only its own
 // sub-list and record: no global atomics, no state carried between calls.
-template <int THREADS, bool BF16>
+template <int THREADS, int DT>
 __global__ __launch_bounds__(THREADS, 4) void pass1_kernel(Params P) {
     __shared__ Shared sh;
     int rb = 0;
@@ -673,7 +672,7 @@ __global__ __launch_bounds__(THREADS, 4) void pass1_kernel(Params P) {
     if (row >= P.batch) return;
     const int32_t V = P.vocab;
     const int64_t roff = row * (int64_t)V;
-    const void* rowp = row_ptr<BF16>(P, row);
+    const void* rowp = row_ptr<DT>(P, row);
     uint64_t* sub = sub_list(P, row, slice);
     const RowMode md = row_mode(P, row);
     if (threadIdx.x == 0) {
@@ -693,18 +692,18 @@ __global__ __launch_bounds__(THREADS, 4) void pass1_kernel(Params P) {
     bool ins[8];
     float c0 = 0.0f;
     if (md.need_cand) {
-        load_sample<BF16>(rowp, V, xs, ins);
-        c0 = load_value<BF16>(rowp, 0);
+        load_sample<DT>(rowp, V, xs, ins);
+        c0 = load_value<DT>(rowp, 0);
     }
-    RawTile<BF16> ring[kTileDepth<BF16>];
+    RawTile<DT> ring[kTileDepth<DT>];
     {
         const int64_t a = aligned_start(roff, e0, e1);
         const int64_t nfull = (e1 - a) / ((int64_t)THREADS * 16);
 #pragma unroll
-        for (int j = 0; j < kTileDepth<BF16>; ++j)
-            if (j < nfull) load_raw<THREADS, BF16>(rowp, a + (int64_t)j * THREADS * 16, ring[j]);
+        for (int j = 0; j < kTileDepth<DT>; ++j)
+            if (j < nfull) load_raw<THREADS, DT>(rowp, a + (int64_t)j * THREADS * 16, ring[j]);
     }
-    const Thresh th = compute_threshold<THREADS, BF16>(P, md, rowp, xs, ins, c0, sh, rb);
+    const Thresh th = compute_threshold<THREADS, DT>(P, md, rowp, xs, ins, c0, sh, rb);
     if (slice == 0 && threadIdx.x == 0) {
         uint32_t* rr = P.rowrec + row * R_WORDS;
         *(uint4*)rr = make_uint4(__float_as_uint(th.t), __float_as_uint(th.tc), th.predicted ? 1u : 0u,
@@ -718,9 +717,9 @@ __global__ __launch_bounds__(THREADS, 4) void pass1_kernel(Params P) {
     uint64_t rest = 0;
     Spill sp{0u, 0u};
     if (rest_on)
-        stream_slice<THREADS, BF16, true>(P, row, sub, e0, e1, th.tc, fill, ring, sh, rest, sp);
+        stream_slice<THREADS, DT, true>(P, row, sub, e0, e1, th.tc, fill, ring, sh, rest, sp);
     else
-        stream_slice<THREADS, BF16, false>(P, row, sub, e0, e1, th.tc, fill, ring, sh, rest, sp);
+        stream_slice<THREADS, DT, false>(P, row, sub, e0, e1, th.tc, fill, ring, sh, rest, sp);
     const uint32_t lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     if (lane == 0) sh.wspill[wave] = sp.n;
     __syncthreads();
@@ -778,12 +777,12 @@ __global__ __launch_bounds__(THREADS, 4) void pass1_kernel(Params P) {
 // logits below tr. Survivors are staged in LDS (stage, stage_cap entries)
 // and written to the list in bursts between batches of loads: stores mixed
 // into the streaming loads would make every batch wait for them.
-template <int THREADS, bool BF16>
+template <int THREADS, int DT>
 QRITA_DEV uint32_t collect_row(const Params& P, int64_t row, float tr, bool rest_on, uint64_t* stage,
                                uint32_t stage_cap, Shared& sh, int& rb, uint64_t& rest_out, uint32_t& kmax_out,
                                bool& overflow) {
     const int32_t V = P.vocab;
-    const void* rowp = row_ptr<BF16>(P, row);
+    const void* rowp = row_ptr<DT>(P, row);
     uint64_t* lst = P.glist + row * (int64_t)P.list_stride;
     const uint32_t lcap = (uint32_t)P.list_cap;
     __syncthreads();
@@ -810,7 +809,7 @@ QRITA_DEV uint32_t collect_row(const Params& P, int64_t row, float tr, bool rest
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t e = base + (int64_t)u * THREADS + threadIdx.x;
-            const float x = load_value<BF16>(rowp, e < V ? e : V - 1);
+            const float x = load_value<DT>(rowp, e < V ? e : V - 1);
             fv[u] = e < V ? x : 0.0f;
         }
     };

@@ -261,7 +261,7 @@ struct SrcRow {
     static constexpr bool kLows = true;
     const void* row;
     uint32_t V;
-    bool bf16;
+    int dtype;
     uint32_t n;
     template <class F>
     QRITA_DEV void visit(F&& f) const {
@@ -274,7 +274,13 @@ struct SrcRow {
             for (int u = 0; u < U; ++u) {
                 const uint32_t i = i0 + (uint32_t)u * NT + lane;
                 const uint32_t ic = i < V ? i : V - 1u;
-                const uint32_t x = bf16 ? ((uint32_t)((const uint16_t*)row)[ic] << 16) : ((const uint32_t*)row)[ic];
+                uint32_t x;
+                if (dtype == 0) {
+                    x = ((const uint32_t*)row)[ic];
+                } else {
+                    const uint32_t h = ((const uint16_t*)row)[ic];
+                    x = __float_as_uint(dtype == 1 ? lo16<1>(h) : lo16<2>(h));
+                }
                 b[u] = i < V ? x : 0u;
             }
         };
@@ -1229,6 +1235,8 @@ struct RowOut {
     float* prob;     // probabilities beside idx, or null
     float mref;
     double inv_s;
+    const void* rowp;  // the row's logits (index-ordered probabilities)
+    int dtype;
 };
 
 // Mask of the kept set {c >= B} from a pass over the candidates: bitmap, or
@@ -1276,6 +1284,88 @@ QRITA_DEV void mask_from_sorted(uint32_t cnt, uint64_t B, const RowOut& o) {
     }
     lds_sync();
     write_mask_row<NT>(o.mrow, bm, o.V);
+}
+
+// Probability of vocabulary entry i (index-ordered output reads its logit).
+QRITA_DEV float prob_at(const RowOut& o, uint32_t i) {
+    uint32_t x;
+    if (o.dtype == 0) {
+        x = ((const uint32_t*)o.rowp)[i];
+    } else {
+        const uint32_t h = ((const uint16_t*)o.rowp)[i];
+        x = __float_as_uint(o.dtype == 1 ? lo16<1>(h) : lo16<2>(h));
+    }
+    return (float)((double)mass_fx(f32_key(x), o.mref) * o.inv_s);
+}
+
+// The outputs of a row in ascending index order (the kept set as in
+// emit_row): the kept set {c >= B} becomes an LDS bitmap, which also gives
+// the mask; each thread then takes a run of bitmap words, and an exclusive
+// prefix of their bit counts over the block places its indices.
+template <class T, class C, class L>
+QRITA_DEV void emit_row_by_index(C& c, const L& lsrc, const RowOut& o, bool all, uint32_t vf, uint32_t needf,
+                                 uint32_t Nf, uint32_t L_, TailDiag& dg) {
+    constexpr int NT = T::NT;
+    Shared& sh = *c.sh;
+    const uint32_t V = o.V;
+    const uint32_t Lout = o.idx ? (L_ < o.idx_cap ? L_ : o.idx_cap) : 0u;
+    if (all) {  // every index is kept: 0, 1, ..., Lout - 1
+        for (uint32_t r = threadIdx.x; r < Lout; r += NT) {
+            o.idx[r] = (int32_t)r;
+            if (o.prob) o.prob[r] = prob_at(o, r);
+        }
+        return;
+    }
+    if (!o.mrow && Lout == 0) return;
+    const uint64_t B = tie_boundary<T>(lsrc, vf, needf, Nf, V, c.mode, sh, c.rb, dg.iters);
+    uint32_t* bm = (uint32_t*)(dyn_lds() + T::SB_OFF);
+    const uint32_t nw = (V + 31u) / 32u;
+    lds_sync();
+    clear_words(bm, nw + 1u, NT);  // one word past the row: write_mask_row reads it
+    lds_sync();
+    lsrc.visit([&](uint32_t key, uint32_t low) {
+        const uint64_t w = ((uint64_t)key << 32) | low;
+        if (key != 0 && w >= B) atomicOr(&bm[(~low) >> 5], 1u << ((~low) & 31u));
+    });
+    lds_sync();
+    if (o.mrow) {
+        if (o.bitmap) {
+            write_mask_row<NT>(o.mrow, bm, V);
+        } else {
+            for (uint32_t i = threadIdx.x; i < nw; i += NT) {
+                uint32_t bits = bm[i];
+                while (bits) {
+                    const uint32_t b = (uint32_t)__builtin_ctz(bits);
+                    bits &= bits - 1u;
+                    o.mrow[i * 32u + b] = 1;
+                }
+            }
+        }
+    }
+    if (Lout == 0) return;
+    const uint32_t per = (nw + NT - 1u) / NT;
+    const uint32_t w0 = threadIdx.x * per < nw ? threadIdx.x * per : nw;
+    const uint32_t w1 = w0 + per < nw ? w0 + per : nw;
+    uint32_t cnt = 0;
+    for (uint32_t i = w0; i < w1; ++i) cnt += (uint32_t)__builtin_popcount(bm[i]);
+    // exclusive prefix of cnt over the block: lanes, then waves
+    uint32_t x = cnt;
+    QRITA_WAVE_STEPS(op_add, 0u)
+    const uint32_t wave_tot = readlane(x, kWave - 1);
+    uint32_t total = 0;
+    const uint32_t before = wave_prefix<NT>(wave_tot, total, sh, c.rb);
+    uint32_t r = before + x - cnt;
+    for (uint32_t i = w0; i < w1 && r < Lout; ++i) {
+        uint32_t bits = bm[i];
+        while (bits && r < Lout) {
+            const uint32_t b = (uint32_t)__builtin_ctz(bits);
+            bits &= bits - 1u;
+            const uint32_t ix = i * 32u + b;
+            o.idx[r] = (int32_t)ix;
+            if (o.prob) o.prob[r] = prob_at(o, ix);
+            ++r;
+        }
+    }
 }
 
 // The outputs (a7) of a row whose kept set is {> vf} and the needf
@@ -1489,11 +1579,16 @@ QRITA_DEV bool finish_row(const Params& P, int64_t row, const RowMode& md, const
             token = (int32_t)cand_idx(tie_boundary<T>(lsrc, mo.v, j, Nv, V, c.mode, sh, c.rb, dg.iters, true));
         }
     }
+    const void* rowp = P.dtype != 0 ? (const void*)((const uint16_t*)P.logits + row * (int64_t)V)
+                                    : (const void*)((const float*)P.logits + row * (int64_t)V);
     RowOut o{(P.out_idx && P.idx_cap > 0) ? P.out_idx + row * (int64_t)P.idx_cap : nullptr, (uint32_t)P.idx_cap,
              (P.mask && !md.keep_all) ? P.mask + row * (int64_t)V : nullptr, P.bitmap != 0, V,
              (P.out_prob && P.idx_cap > 0) ? P.out_prob + row * (int64_t)P.idx_cap : nullptr, m,
-             s_kept > 0.0 ? 1.0 / s_kept : 0.0};
-    emit_row<T>(c, lsrc, o, all, vf, ngt, needf, Nf, Lk, key_lo, n, kmax, dg);
+             s_kept > 0.0 ? 1.0 / s_kept : 0.0, rowp, (int)P.dtype};
+    if (P.idx_order)
+        emit_row_by_index<T>(c, lsrc, o, all, vf, needf, Nf, Lk, dg);
+    else
+        emit_row<T>(c, lsrc, o, all, vf, ngt, needf, Nf, Lk, key_lo, n, kmax, dg);
     if (P.out_count && threadIdx.x == 0) P.out_count[row] = (int32_t)Lk;
     if (P.out_token && threadIdx.x == 0) P.out_token[row] = token;
     rb = c.rb;
@@ -1509,10 +1604,12 @@ QRITA_DEV float sample_rank_value(const Params& P, const void* rowp, uint32_t r,
     const int32_t V = P.vocab;
     float x[8];
     bool in[8];
-    if (P.bf16)
-        load_sample<true>(rowp, V, x, in);
+    if (P.dtype == 1)
+        load_sample<1>(rowp, V, x, in);
+    else if (P.dtype == 2)
+        load_sample<2>(rowp, V, x, in);
     else
-        load_sample<false>(rowp, V, x, in);
+        load_sample<0>(rowp, V, x, in);
     uint32_t* a = (uint32_t*)(dyn_lds() + T::A_OFF);
     lds_sync();
 #pragma unroll
@@ -1551,8 +1648,8 @@ QRITA_DEV TailOut tail_fallback(const Params& P, int64_t row, RowMode md, float 
                                 uint32_t ns_h, int32_t n_t, Shared& sh, int rb) {
     constexpr int NT = T::NT;
     const int32_t V = P.vocab;
-    const void* rowp = P.bf16 ? (const void*)((const uint16_t*)P.logits + row * (int64_t)V)
-                              : (const void*)((const float*)P.logits + row * (int64_t)V);
+    const void* rowp = P.dtype != 0 ? (const void*)((const uint16_t*)P.logits + row * (int64_t)V)
+                                    : (const void*)((const float*)P.logits + row * (int64_t)V);
     const float kInf = __builtin_inff();
     TailDiag dg{n_t, 0};
     int path = 1;
@@ -1586,10 +1683,12 @@ QRITA_DEV TailOut tail_fallback(const Params& P, int64_t row, RowMode md, float 
             // the whole dynamic LDS stages the survivors (nothing in it is live here)
             uint64_t* stage = (uint64_t*)dyn_lds();
             const uint32_t scap = (uint32_t)(T::LDS / 8);
-            if (P.bf16)
-                cnt = collect_row<NT, true>(P, row, tr, md.rest_on(), stage, scap, sh, rb, rest2, kmax2, ovf);
+            if (P.dtype == 1)
+                cnt = collect_row<NT, 1>(P, row, tr, md.rest_on(), stage, scap, sh, rb, rest2, kmax2, ovf);
+            else if (P.dtype == 2)
+                cnt = collect_row<NT, 2>(P, row, tr, md.rest_on(), stage, scap, sh, rb, rest2, kmax2, ovf);
             else
-                cnt = collect_row<NT, false>(P, row, tr, md.rest_on(), stage, scap, sh, rb, rest2, kmax2, ovf);
+                cnt = collect_row<NT, 0>(P, row, tr, md.rest_on(), stage, scap, sh, rb, rest2, kmax2, ovf);
             if (ovf) break;
             if (threadIdx.x == 0) sh.cnt[0] = cnt;
             lds_sync();
@@ -1602,7 +1701,7 @@ QRITA_DEV TailOut tail_fallback(const Params& P, int64_t row, RowMode md, float 
     if (!done) {
         path = 3;
         uint32_t kr = 0;
-        const SrcRow<NT> src{rowp, (uint32_t)V, P.bf16 != 0, (uint32_t)V};
+        const SrcRow<NT> src{rowp, (uint32_t)V, (int)P.dtype, (uint32_t)V};
         src.visit([&](uint32_t key, uint32_t) { kr = key > kr ? key : kr; });
         uint32_t mn[1] = {~wave_max_u32(kr)};
         comb_record<NT, 0, 0, 1>(nullptr, nullptr, mn, sh, rb);
@@ -1655,6 +1754,11 @@ __global__ __launch_bounds__(T::NT, T::WAVES_PER_SIMD) void tail_kernel(Params P
     uint8_t* mrow = P.mask ? P.mask + row * (int64_t)V : nullptr;
     if (!md.need_cand) {
         if (P.out_count && threadIdx.x == 0) P.out_count[row] = V;
+        if (P.idx_order && P.out_idx) {  // keep-all row in index order
+            const uint32_t lo = (uint32_t)P.idx_cap < (uint32_t)V ? (uint32_t)P.idx_cap : (uint32_t)V;
+            int32_t* orow = P.out_idx + row * (int64_t)P.idx_cap;
+            for (uint32_t r = threadIdx.x; r < lo; r += NT) orow[r] = (int32_t)r;
+        }
         done = true;
     } else {
         const bool in_lds = !overflow && nlist <= (uint32_t)P.tail_cap;

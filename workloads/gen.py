@@ -7,8 +7,13 @@ stated distribution with NumPy's PCG64, from a seed sequence rooted at
 ``1000 + config_index``, so any subset of rows can be regenerated alone.
 
 Values are drawn in float64, cast to float32 with round-to-nearest-even, and
-for bf16 workloads rounded float32 -> bf16 with round-to-nearest-even. The
+for bf16 workloads rounded float32 -> bf16 with round-to-nearest-even; f16
+workloads round float64 -> IEEE binary16 (NumPy's cast, nearest-even). The
 resulting bit patterns are the data for both the GPU path and the oracle.
+
+Two more named workloads (EXTRA) have the shapes of the same selection in
+other systems: top-512 marginals of a block drafter over a full vocabulary,
+and top-B pruning of a beam search over BW x K scored proposals.
 
 This module only draws numbers. It contains none of the selection method's
 arithmetic (no ordering, no thresholds, no softmax).
@@ -22,6 +27,7 @@ import numpy as np
 
 __all__ = [
     "CONFIGS",
+    "EXTRA",
     "Inputs",
     "f32_to_bf16_bits",
     "bf16_bits_to_f32",
@@ -34,8 +40,8 @@ __all__ = [
 class Inputs:
     """One batch of rows.
 
-    logits: [B, V] array. float32 values for dtype "f32"; uint16 bf16 bit
-            patterns for dtype "bf16". Rows are contiguous (C order).
+    logits: [B, V] array. float32 values for dtype "f32"; uint16 bit
+            patterns for dtypes "bf16" and "f16". Rows are contiguous (C order).
     k:      int32 [B] per-row top-k (<= 0 or >= V means top-k off).
     p:      float32 [B] per-row top-p (>= 1 or NaN means top-p off).
     """
@@ -55,9 +61,11 @@ class Inputs:
         return int(self.logits.shape[1])
 
     def values_f32(self) -> np.ndarray:
-        """The logits widened to float32 (exact for both dtypes)."""
+        """The logits widened to float32 (exact for every dtype)."""
         if self.dtype == "bf16":
             return bf16_bits_to_f32(self.logits)
+        if self.dtype == "f16":
+            return self.logits.view(np.float16).astype(np.float32)
         return self.logits
 
     def take_rows(self, rows: Sequence[int]) -> "Inputs":
@@ -84,10 +92,16 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
 
 
 def _cast(z64: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "f16":
+        return z64.astype(np.float16).view(np.uint16)
     z32 = z64.astype(np.float32)
     if dtype == "bf16":
         return f32_to_bf16_bits(z32)
     return z32
+
+
+def _store_dtype(dtype: str):
+    return np.uint16 if dtype in ("bf16", "f16") else np.float32
 
 
 def _row_rngs(seed_root: int, batch: int) -> list:
@@ -191,7 +205,67 @@ def make_config(index: int, rows: Optional[Sequence[int]] = None) -> Inputs:
     rngs = _row_rngs(seed_root, B)
     k, p = c["ctl"](_ctl_rng(seed_root), B)
     sel = np.arange(B) if rows is None else np.asarray(rows, dtype=np.int64)
-    out = np.empty((len(sel), V), dtype=np.uint16 if dt == "bf16" else np.float32)
+    out = np.empty((len(sel), V), dtype=_store_dtype(dt))
+    for j, r in enumerate(sel):
+        out[j] = _cast(c["row"](rngs[int(r)], V), dt)
+    return Inputs(c["name"], dt, out, k[sel].copy(), p[sel].copy())
+
+
+# ---------------------------------------------------------------------------
+# The second workload: the same selection at other systems' shapes
+# ---------------------------------------------------------------------------
+
+def _row_marginals(rng, V):
+    # a drafter's per-position logits: a broad N(0, sd 2.5) body with about
+    # 0.5 % plausible tokens lifted to N(9, sd 2.5)
+    z = rng.normal(0.0, 2.5, V)
+    n = int(round(0.005 * V))
+    z[rng.choice(V, n, replace=False)] = rng.normal(9.0, 2.5, n)
+    return z
+
+
+def _row_beam(rng, V, K=64):
+    # BW = V / K beams, each with K proposals in beam-major order: the score
+    # is the beam's cumulative log-probability plus the proposal's
+    # log-probability, both modelled as decreasing sums of exponential steps
+    # (about 30 % of the proposals fail validation and score -inf)
+    BW = V // K
+    beam = -np.cumsum(rng.exponential(0.15, BW))
+    lp = -np.cumsum(rng.exponential(0.4, (BW, K)), axis=1)
+    s = (beam[:, None] + lp).reshape(-1)
+    s[rng.random(V) < 0.3] = -np.inf
+    return s
+
+
+def _ctl_marginals(rng, B):
+    return np.full(B, 512, np.int32), np.full(B, 1.0, np.float32)
+
+
+def _ctl_beam(rng, B):
+    return np.full(B, 64, np.int32), np.full(B, 1.0, np.float32)
+
+
+EXTRA = [
+    dict(index=0, name="b2048_v151936_f16_marginals_top512", batch=2048, vocab=151936, dtype="f16",
+         row=_row_marginals, ctl=_ctl_marginals, idx_order=1,
+         text="2048 x 151936 f16 (128 sequences x 16 block positions of drafter logits: N(0, sd 2.5), "
+              "0.5 % at N(9, sd 2.5)); k=512, indices in ascending vocabulary order"),
+    dict(index=1, name="b4096_v4096_f32_beam_prune_top64", batch=4096, vocab=4096, dtype="f32",
+         row=_row_beam, ctl=_ctl_beam, idx_order=1,
+         text="4096 x 4096 fp32 (64 beams x 64 proposals: cumulative beam log-prob + sorted "
+              "proposal log-softmax, 30 % -inf); k=64, indices in ascending (beam-major) order"),
+]
+
+
+def make_extra(index: int, rows: Optional[Sequence[int]] = None) -> Inputs:
+    """Generate the second-workload shape ``index`` (all rows, or only ``rows``)."""
+    c = EXTRA[index]
+    B, V, dt = c["batch"], c["vocab"], c["dtype"]
+    seed_root = 2000 + index
+    rngs = _row_rngs(seed_root, B)
+    k, p = c["ctl"](_ctl_rng(seed_root), B)
+    sel = np.arange(B) if rows is None else np.asarray(rows, dtype=np.int64)
+    out = np.empty((len(sel), V), dtype=_store_dtype(dt))
     for j, r in enumerate(sel):
         out[j] = _cast(c["row"](rngs[int(r)], V), dt)
     return Inputs(c["name"], dt, out, k[sel].copy(), p[sel].copy())
@@ -262,16 +336,31 @@ def _kind_fn(kind: str) -> Callable:
     def flat(rng, V):
         return rng.normal(0.0, 0.05, V)
 
+    def marginals(rng, V):
+        return _row_marginals(rng, V)
+
+    def beam(rng, V):
+        return _row_beam(rng, V, K=64 if V % 64 == 0 else 1)
+
+    def f16_edges(rng, V):
+        # binary16 extremes: subnormals, the largest finite values, signed zeros
+        z = rng.normal(0.0, 1.0, V)
+        pick = rng.integers(0, 5, V)
+        z = np.where(pick == 0, rng.integers(-1023, 1024, V) * 2.0**-24, z)
+        z = np.where(pick == 1, np.where(rng.random(V) < 0.5, -0.0, 0.0), z)
+        z = np.where(pick == 2, rng.choice([65504.0, 65472.0, -65504.0], V), z)
+        return z
+
     table = dict(gauss=gauss, gauss_outliers=gauss_outliers, ties16=ties16, uniform=uniform, gauss2=gauss2,
                  heavy=heavy, equal=equal, twolevel=twolevel, smallint=smallint, neginf=neginf,
                  allneginf=allneginf, zeros=zeros, ascending=ascending, descending=descending,
-                 spike=spike, flat=flat)
+                 spike=spike, flat=flat, marginals=marginals, beam=beam, f16_edges=f16_edges)
     return table[kind]
 
 
 ROW_KINDS = ("gauss", "gauss_outliers", "ties16", "uniform", "gauss2", "heavy", "equal", "twolevel",
              "smallint", "neginf", "allneginf", "zeros", "ascending", "descending", "spike",
-             "flat")
+             "flat", "marginals", "beam", "f16_edges")
 
 
 def make_rows(batch: int, vocab: int, dtype: str, kind: str, seed: int,
@@ -283,7 +372,7 @@ def make_rows(batch: int, vocab: int, dtype: str, kind: str, seed: int,
     """
     fn = _kind_fn(kind)
     rngs = _row_rngs(seed, batch)
-    out = np.empty((batch, vocab), dtype=np.uint16 if dtype == "bf16" else np.float32)
+    out = np.empty((batch, vocab), dtype=_store_dtype(dtype))
     for r in range(batch):
         out[r] = _cast(fn(rngs[r], vocab), dtype)
     crng = _ctl_rng(seed)
