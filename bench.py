@@ -22,6 +22,10 @@ truncation off (every row takes the full-row search), binary vs quaternary
 pivots on truncation hits and misses, duplicate handling (rows on a 1/16 grid
 vs the same distribution in distinct float32 values), and one fixed tier vs
 the tier table.
+
+Also timed and parity-checked: the second workload's shapes (top-512 drafter
+marginals in float16, top-64 beam pruning, indices in ascending order) and the
+fused draw (qrita_sample: tokens and probabilities) on two named workloads.
 """
 import argparse
 import hashlib
@@ -91,18 +95,29 @@ def cpu_model():
     return None
 
 
+def esize(dtype):
+    return 4 if dtype == "f32" else 2
+
+
 def to_device(x, dev):
     import torch
 
     if x.dtype == "bf16":
         return torch.from_numpy(x.logits.view(np.int16)).to(dev).view(torch.bfloat16)
+    if x.dtype == "f16":
+        return torch.from_numpy(x.logits.view(np.int16)).to(dev).view(torch.float16)
     return torch.from_numpy(x.logits).to(dev)
 
 
 class Runner:
-    """Device buffers of one workload (rotated copies of the inputs and outputs)."""
+    """Device buffers of one workload (rotated copies of the inputs and outputs).
 
-    def __init__(self, x, rotate_bytes):
+    sample: each step is a qrita_sample call (token and probabilities as well,
+    seed fixed, offset = the step); base: options every step carries."""
+
+    SEED = 20260201
+
+    def __init__(self, x, rotate_bytes, want_mask=True, sample=False, base=None):
         import torch
 
         import top_selection_sigma_amd as q
@@ -110,29 +125,42 @@ class Runner:
         self.q = q
         self.x = x
         self.dev = torch.device("cuda", 0)
+        self.sample = sample
+        self.base = dict(base or {})
         B, V = x.batch, x.vocab
-        self.es = 2 if x.dtype == "bf16" else 4
+        self.es = esize(x.dtype)
         self.idx_cap = int(max(64, x.k.max()))
         logits0 = to_device(x, self.dev)
         self.k = torch.from_numpy(x.k).to(self.dev)
         self.p = torch.from_numpy(x.p).to(self.dev)
-        set_bytes = B * V * (self.es + 1) + B * self.idx_cap * 4
+        set_bytes = B * V * (self.es + (1 if want_mask else 0)) + B * self.idx_cap * 4
         self.nsets = max(2, min(MAX_SETS, math.ceil(rotate_bytes / set_bytes)))
         self.sets = []
         for i in range(self.nsets):
             lg = logits0 if i == 0 else logits0.clone()
-            self.sets.append((lg, torch.empty((B, V), dtype=torch.uint8, device=self.dev),
-                              torch.empty((B, self.idx_cap), dtype=torch.int32, device=self.dev),
-                              torch.empty(B, dtype=torch.int32, device=self.dev)))
+            m = torch.empty((B, V), dtype=torch.uint8, device=self.dev) if want_mask else None
+            tok = torch.empty(B, dtype=torch.int32, device=self.dev) if sample else None
+            prob = torch.empty((B, self.idx_cap), dtype=torch.float32, device=self.dev) if sample else None
+            self.sets.append((lg, m, torch.empty((B, self.idx_cap), dtype=torch.int32, device=self.dev),
+                              torch.empty(B, dtype=torch.int32, device=self.dev), tok, prob))
         self.code = q.dtype_code(logits0)
         self.ws = q.workspace_for(B, V, self.code, self.idx_cap, self.dev)
         self.stream = torch.cuda.current_stream()
         self.last = 0
 
     def step(self, i, opts=None):
-        lg, m, ix, c = self.sets[i % self.nsets]
-        self.q.qrita_select_ex(lg, self.k, self.p, m, ix, c, self.idx_cap, self.ws, self.stream, opts)
+        lg, m, ix, c, tok, prob = self.sets[i % self.nsets]
+        if self.base:
+            opts = opts or self.q.Options()
+            for k, v in self.base.items():
+                setattr(opts, k, v)
+        if self.sample:
+            self.q.qrita_sample(lg, self.k, self.p, self.SEED, i, tok, prob, m, ix, c, self.idx_cap, self.ws,
+                                self.stream, opts)
+        else:
+            self.q.qrita_select_ex(lg, self.k, self.p, m, ix, c, self.idx_cap, self.ws, self.stream, opts)
         self.last = i % self.nsets
+        self.last_offset = i
 
     def time(self, steps, warmup, opts=None):
         """Mean ms per call, per-kernel means (ms) and p10/p50/p90 per call."""
@@ -170,8 +198,13 @@ class Runner:
                     step_ms_p10_p50_p90=[float(np.percentile(per, v)) for v in (10, 50, 90)])
 
     def outputs(self):
-        lg, m, ix, c = self.sets[self.last]
-        return m.cpu().numpy(), ix.cpu().numpy(), c.cpu().numpy()
+        lg, m, ix, c, tok, prob = self.sets[self.last]
+        return None if m is None else m.cpu().numpy(), ix.cpu().numpy(), c.cpu().numpy()
+
+    def draws(self):
+        """(tokens, probabilities, offset) of the last step of a sampling runner."""
+        lg, m, ix, c, tok, prob = self.sets[self.last]
+        return tok.cpu().numpy(), prob.cpu().numpy(), self.last_offset
 
     def diag(self, opts=None):
         import torch
@@ -193,7 +226,8 @@ def parity(x, ref, outs, idx_cap):
     band = ref.band_lo != ref.band_hi
     bad = np.zeros(x.batch, bool)
     bad |= ~band & (count != ref.count)
-    bad |= ~band & np.any(mask != ref.mask, axis=1)
+    if mask is not None:
+        bad |= ~band & np.any(mask != ref.mask, axis=1)
     for b in range(x.batch):
         n = min(int(count[b]), idx_cap)
         if not band[b] and not np.array_equal(idx[b, :n], ref.idx[b, :n]):
@@ -209,16 +243,66 @@ def parity(x, ref, outs, idx_cap):
             c = int(count[b])
             m = np.zeros(x.vocab, np.uint8)
             m[full.idx[j, :c]] = 1
-            if not np.array_equal(mask[b], m) or not np.array_equal(idx[b, :min(c, idx_cap)],
-                                                                    full.idx[j, :min(c, idx_cap)]):
+            if (mask is not None and not np.array_equal(mask[b], m)) or \
+                    not np.array_equal(idx[b, :min(c, idx_cap)], full.idx[j, :min(c, idx_cap)]):
                 bad[b] = True
     return dict(mismatch_rows=int(bad.sum()), band_rows=int(band.sum()))
 
 
-def effective_bytes(x, count, idx_cap):
-    es = 2 if x.dtype == "bf16" else 4
+def parity_index_order(x, ref, outs, idx_cap):
+    """Rows whose index-ordered output differs from the oracle's kept set
+    (indices ascending; band rows: a rank prefix of a length in the band)."""
+    import oracle
+
+    _, idx, count = outs
+    band = ref.band_lo != ref.band_hi
+    bad = 0
+    brows = np.nonzero(band)[0]
+    full = None
+    if len(brows):
+        sub = x.take_rows(brows)
+        full = oracle.select(sub.logits, sub.dtype, sub.k, sub.p, int(max(ref.band_hi[brows].max(), 1)),
+                             want_mask=False)
+    j = 0
+    for b in range(x.batch):
+        c = int(count[b])
+        if band[b]:
+            ok = ref.band_lo[b] <= c <= ref.band_hi[b]
+            kept = np.sort(full.idx[j, :c])
+            j += 1
+        else:
+            ok = c == ref.count[b]
+            kept = np.nonzero(ref.mask[b])[0]
+        n = min(c, idx_cap)
+        if not ok or not np.array_equal(idx[b, :n], kept[:n]):
+            bad += 1
+    return dict(mismatch_rows=int(bad), band_rows=int(band.sum()))
+
+
+def parity_draws(x, ref, tokens, probs, idx_cap, offset):
+    """Drawn tokens and probabilities against the oracle's draw with NumPy's
+    Philox uniforms (band draws: the rank within the oracle's band)."""
+    import oracle
+
+    u = oracle.uniforms(Runner.SEED, offset, x.batch)
+    s = oracle.sample(x.logits, x.dtype, x.k, x.p, u, idx_cap)
+    band = ref.band_lo != ref.band_hi
+    exact = ~band & (s.rank_lo == s.rank_hi)
+    tok_bad = int(np.sum(exact & (tokens != s.token)))
+    prob_bad = 0
+    for b in np.nonzero(~band)[0]:
+        n = min(int(ref.count[b]), idx_cap)
+        want = s.prob[b, :n].astype(np.float64)
+        if np.any(np.abs(probs[b, :n].astype(np.float64) - want) > 1e-6 * want + 1e-12):
+            prob_bad += 1
+    return dict(token_mismatch_rows=tok_bad, prob_mismatch_rows=prob_bad,
+                band_draws=int(np.sum(~band & (s.rank_lo != s.rank_hi))), band_rows=int(band.sum()))
+
+
+def effective_bytes(x, count, idx_cap, mask=True):
+    es = esize(x.dtype)
     kept = np.minimum(count, idx_cap).astype(np.int64).sum()
-    return int(x.batch * x.vocab * es + x.batch * x.vocab + 4 * kept + 4 * x.batch)
+    return int(x.batch * x.vocab * es + (x.batch * x.vocab if mask else 0) + 4 * kept + 4 * x.batch)
 
 
 def roofline_for(name, x, t, count, idx_cap, bitmap):
@@ -227,9 +311,9 @@ def roofline_for(name, x, t, count, idx_cap, bitmap):
     unless the tail writes whole mask rows); the tail writes the indices, the
     counts and, with whole-row masks, the mask."""
     B, V = x.batch, x.vocab
-    es = 2 if x.dtype == "bf16" else 4
+    es = esize(x.dtype)
     kept = int(np.minimum(count, idx_cap).astype(np.int64).sum())
-    p1_bytes = B * V * es + (0 if bitmap else B * V)
+    p1_bytes = B * V * es + (0 if bitmap or bitmap is None else B * V)
     tail_bytes = 4 * kept + 4 * B + (B * V if bitmap else 0)
     dom = "pass1" if t["pass1_ms"] >= t["tail_ms"] else "tail"
     ms = t["pass1_ms"] if dom == "pass1" else t["tail_ms"]
@@ -264,11 +348,12 @@ def bench_workload(index, steps, warmup, rotate_bytes, check, ablate):
     bitmap = x.batch >= 512  # the tier table's whole-row mask rule (the rows here fit every bitmap)
     res["roofline"] = roofline_for(x.name, x, t, count, r.idx_cap, bitmap)
     path = dg[:, 4]
-    res["truncation"] = dict(rows=x.batch, single_pass=int(np.sum(path <= 1)),
+    res["truncation"] = dict(rows=x.batch, single_pass=int(np.sum(path <= 1)), lds_path=int(np.sum(path == 0)),
+                             list_path=int(np.sum(path == 1)),
                              miss_predicted=int(np.sum(dg[:, 7] == 1)), recollected=int(np.sum(path == 2)),
                              full_row=int(np.sum(path == 3)), gaussian_t_hit=int(np.sum(dg[:, 5] == 1)),
                              mean_iterations=float(dg[:, 6].mean()))
-    es = 2 if x.dtype == "bf16" else 4
+    es = esize(x.dtype)
     out_bytes = x.batch * x.vocab + x.batch * r.idx_cap * 4 + x.batch * 4
     res["memory"] = dict(workspace_bytes=int(r.q.qrita_workspace_bytes(x.batch, x.vocab, r.code, r.idx_cap)),
                          output_bytes=out_bytes,
@@ -337,6 +422,60 @@ def duplicate_ablation(steps, warmup, rotate_bytes, check):
     return out
 
 
+def second_workload(steps, warmup, rotate_bytes, check):
+    """The same selection at other systems' shapes: top-512 marginals of a
+    block drafter (2048 x 151936 f16) and top-64 pruning of 64 x 64 beam
+    proposals (4096 x 4096 f32); indices in ascending order, no mask."""
+    import oracle
+    import workloads as w
+
+    out = {}
+    for i, c in enumerate(w.EXTRA):
+        x = w.make_extra(i)
+        r = Runner(x, rotate_bytes, want_mask=False, base=dict(idx_order=1))
+        t = r.time(steps, warmup)
+        outs = r.outputs()
+        sec = t["ms_per_step"] * 1e-3
+        eff = effective_bytes(x, outs[2], r.idx_cap, mask=False)
+        ent = dict(batch=x.batch, vocab=x.vocab, dtype=x.dtype, k=int(x.k[0]), output="indices ascending",
+                   us_per_call=round(t["ms_per_step"] * 1e3, 2), pass1_us=round(t["pass1_ms"] * 1e3, 2),
+                   tail_us=round(t["tail_ms"] * 1e3, 2), rows_per_s=round(x.batch / sec, 1),
+                   effective_gbps=round(eff / sec / 1e9, 1), pct_peak_hbm=round(100 * eff / sec / 1e9 / PEAK_HBM_GBS, 2),
+                   roofline=roofline_for(x.name, x, t, outs[2], r.idx_cap, None))
+        if check:
+            t1 = time.time()
+            ref = oracle.select(x.logits, x.dtype, x.k, x.p, r.idx_cap)
+            ent["oracle_s"] = round(time.time() - t1, 3)
+            ent["parity"] = parity_index_order(x, ref, outs, r.idx_cap)
+        log(f"[bench] {x.name}: {ent['us_per_call']} us/call")
+        out[x.name] = ent
+        del r
+    return out
+
+
+def sampling(index, steps, warmup, rotate_bytes, check, select_us):
+    """qrita_sample (selection + one draw per row, probabilities beside the
+    indices) on a named workload, against qrita_select on the same outputs."""
+    import oracle
+    import workloads as w
+
+    x = w.make_config(index)
+    r = Runner(x, rotate_bytes, sample=True)
+    t = r.time(steps, warmup)
+    ent = dict(workload=x.name, us_per_call=round(t["ms_per_step"] * 1e3, 2),
+               select_us_per_call=round(select_us, 2), pass1_us=round(t["pass1_ms"] * 1e3, 2),
+               tail_us=round(t["tail_ms"] * 1e3, 2))
+    if check:
+        outs = r.outputs()
+        ref = oracle.select(x.logits, x.dtype, x.k, x.p, r.idx_cap)
+        ent["parity"] = parity(x, ref, outs, r.idx_cap)
+        tok, prob, off = r.draws()
+        ent["draw_parity"] = parity_draws(x, ref, tok, prob, r.idx_cap, off)
+    log(f"[bench] sampling {x.name}: {ent['us_per_call']} us/call")
+    del r
+    return ent
+
+
 def cpu_baseline(x, idx_cap, target_s):
     """The oracle, as it stands, on all host cores over whole batches of the
     headline workload until about target_s seconds of work."""
@@ -357,6 +496,12 @@ def cpu_baseline(x, idx_cap, target_s):
                 sample=f"{reps} passes over the full {x.batch}-row batch ({el:.1f}s wall)", cpu_model=cpu_model())
 
 
+def w_name(index):
+    import workloads as w
+
+    return w.CONFIGS[index]["name"]
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -368,6 +513,8 @@ def main():
     ap.add_argument("--no-check", action="store_true")
     ap.add_argument("--no-ablation", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-second", dest="second", action="store_false", help="skip the second workload")
+    ap.add_argument("--no-sampling", dest="sampling", action="store_false", help="skip the sampling legs")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -397,6 +544,13 @@ def main():
         per[res["name"]] = res
         torch.cuda.empty_cache()
     dup = duplicate_ablation(max(5, args.steps // 2), max(2, args.warmup // 2), rot, check) if ablate else None
+    second = second_workload(args.steps, args.warmup, rot, check) if args.second else None
+    samp = None
+    if args.sampling:
+        samp = {"headline": sampling(args.config, args.steps, args.warmup, rot, check, head["ms_per_step"] * 1e3)}
+        sel1 = per.get(w_name(1), {}).get("ms_per_step")
+        if sel1 is not None:
+            samp["b64_v128256"] = sampling(1, args.steps, args.warmup, rot, check, sel1 * 1e3)
     cpu = cpu_baseline(hx, int(max(64, hx.k.max())), args.cpu_seconds) if args.cpu_seconds > 0 else None
     props = torch.cuda.get_device_properties(0)
     line = {
@@ -426,6 +580,8 @@ def main():
         "memory": head["memory"],
         "ablations": head.get("ablations"),
         "duplicate_handling_ablation": dup,
+        "second_workload": second,
+        "sampling": samp,
         "per_config": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                        for k, v in per.items()},
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", None),
