@@ -52,6 +52,7 @@ KERNEL_SOURCES = {
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 MAX_SETS = 256
+CHUNKS = 0  # --chunks
 
 
 def log(msg):
@@ -150,6 +151,9 @@ class Runner:
 
     def step(self, i, opts=None):
         lg, m, ix, c, tok, prob = self.sets[i % self.nsets]
+        if CHUNKS and (opts is None or opts.chunks == 0):
+            opts = opts or self.q.Options()
+            opts.chunks = CHUNKS
         if self.base:
             opts = opts or self.q.Options()
             for k, v in self.base.items():
@@ -177,7 +181,11 @@ class Runner:
         ev1.record(self.stream)
         torch.cuda.synchronize()
         total_ms = ev0.elapsed_time(ev1) / steps
-        # per-kernel durations: the library records mid on its stream between the launches
+        # per-kernel durations: the library records mid on its stream between
+        # the launches; one launch of each kernel over the whole batch (no
+        # chunk overlap), so that each duration is one kernel's
+        opts = dict(opts or {})
+        opts["chunks"] = 1
         starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
         mids = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
         ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
@@ -385,15 +393,26 @@ def leg(r, ref, steps, warmup, opts):
 def ablations(index, r, ref, steps, warmup, base):
     """The ablation legs on this workload (each parity-checked against the oracle)."""
     a = {"default_us": round(base["ms_per_step"] * 1e3, 2)}
-    if index in (1, 2, 4):
+    if index in (0, 1, 2, 4):
         # truncation off: no survivors in pass 1, every row searches its full row
         a["truncation_off"] = leg(r, ref, steps, warmup, dict(force_miss=True))
+    if index in (0, 1, 2, 4):
+        # the pivot searches on every row, also where the candidate set is
+        # small enough to sort and scan
+        a["pivot_search_every_row"] = leg(r, ref, steps, warmup, dict(pivot_search_only=1))
     if index in (1, 2, 3, 4):
-        # one pivot per step (binary) instead of three, same duplicate tracking
-        a["binary_pivots"] = leg(r, ref, steps, warmup, dict(pivot_mode=2))
+        # one pivot per step (binary) instead of three, same duplicate
+        # tracking, with the searches on every row
+        a["binary_pivots"] = leg(r, ref, steps, warmup, dict(pivot_mode=2, pivot_search_only=1))
+        a["quaternary_pivots"] = leg(r, ref, steps, warmup, dict(pivot_search_only=1)) if index == 3 else \
+            a.get("pivot_search_every_row")
     if index in (1, 2):
         a["binary_pivots_on_misses"] = leg(r, ref, steps, warmup, dict(pivot_mode=2, force_miss=True))
         a["quaternary_pivots_on_misses"] = a.get("truncation_off")
+    if index in (2, 3, 4):
+        # four row chunks, each chunk's tail on a second stream beside the
+        # next chunk's streaming pass (slower than one chunk on these shapes)
+        a["four_chunks_overlapped"] = leg(r, ref, steps, warmup, dict(chunks=4))
     if index in (1, 2, 3, 4):
         a["light_tier_only"] = leg(r, ref, steps, warmup, dict(tier=1))
         a["heavy_tier_only"] = leg(r, ref, steps, warmup, dict(tier=2))
@@ -411,7 +430,7 @@ def duplicate_ablation(steps, warmup, rotate_bytes, check):
     out = {}
     for kind in ("ties16", "gauss2"):
         x = w.make_rows(256, 151936, "f32", kind, seed=1002, k=50, p=0.95)
-        r = Runner(x, rotate_bytes)
+        r = Runner(x, rotate_bytes, base=dict(pivot_search_only=1))  # the searches track the duplicates
         t = r.time(steps, warmup)
         ent = dict(us_per_call=round(t["ms_per_step"] * 1e3, 2), pass1_us=round(t["pass1_ms"] * 1e3, 2),
                    tail_us=round(t["tail_ms"] * 1e3, 2))
@@ -515,7 +534,10 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-second", dest="second", action="store_false", help="skip the second workload")
     ap.add_argument("--no-sampling", dest="sampling", action="store_false", help="skip the sampling legs")
+    ap.add_argument("--chunks", type=int, default=0, help="qrita_options.chunks for every call (0 = automatic)")
     args = ap.parse_args()
+    global CHUNKS
+    CHUNKS = args.chunks
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(--gpus must be 1)", file=sys.stderr)

@@ -142,9 +142,17 @@ int qrita_select(const void* logits, int64_t batch, int64_t vocab, int dtype,
  *                order (the kept set itself is unchanged), for consumers
  *                that gather from the kept set (a restricted vocabulary
  *                of top-K marginals, beam pruning). Needs vocab + 64 <=
- *                622080 (the row's bitmap in LDS); larger vocabularies
+ *                688256 (the row's bitmap in LDS); larger vocabularies
  *                return QRITA_EINVAL. With qrita_sample, out_prob follows
  *                the same order.
+ *   chunks       0 automatic (one chunk); n in 1..16: the batch is cut into
+ *                n row chunks and the per-row tail of chunk c runs on a
+ *                second stream of the library (one per device) while the
+ *                streaming pass reads chunk c + 1; the caller's stream waits
+ *                for the last tail before anything queued after the call.
+ *   pivot_search_only  0 automatic: rows whose candidate set has at most 2048
+ *                entries are sorted once and answered from the rank order;
+ *                1: every row takes the pivot searches (for the ablations).
  */
 typedef struct {
     int32_t force_miss;
@@ -158,6 +166,8 @@ typedef struct {
     int32_t tier;
     int32_t mask_mode;
     int32_t idx_order;
+    int32_t chunks;
+    int32_t pivot_search_only;
 } qrita_options;
 
 #define QRITA_DIAG_FIELDS 8

@@ -97,16 +97,19 @@ def test_options_are_validated():
            q._Options(0, 0.0, 0, 0, 0, 0, None, None, 3, 0, 0),
            q._Options(0, 0.0, 0, 0, 0, 0, None, None, 0, 2, 0),
            q._Options(0, 0.0, 0, 0, 0, 0, None, None, 0, 0, 2),
-           q._Options(0, 0.0, 0, 0, 0, 0, None, None, 0, 0, -1)]
+           q._Options(0, 0.0, 0, 0, 0, 0, None, None, 0, 0, -1),
+           q._Options(0, 0.0, 0, 0, 0, 0, None, None, 0, 0, 0, 17),
+           q._Options(0, 0.0, 0, 0, 0, 0, None, None, 0, 0, 0, -1),
+           q._Options(0, 0.0, 0, 0, 0, 0, None, None, 0, 0, 0, 0, 2)]
     for o in bad:
         assert _call(opt=o) == q.QRITA_EINVAL
 
 
 def test_index_order_rejects_rows_beyond_the_lds_bitmap():
-    """Index-ordered output keeps the row's bitmap in LDS: at most 622016
+    """Index-ordered output keeps the row's bitmap in LDS: at most 688192
     logits (the heavy tier); longer rows are refused before any HIP call."""
     o = q._Options(0, 0.0, 0, 0, 0, 0, None, None, 0, 0, 1)
-    assert _call(vocab=622017, opt=o) == q.QRITA_EINVAL
+    assert _call(vocab=688193, opt=o) == q.QRITA_EINVAL
     assert _call(vocab=1 << 24, opt=o) == q.QRITA_EINVAL
     # the light tier forced on a row beyond its bitmap
     o = q._Options(0, 0.0, 0, 0, 0, 0, None, None, 1, 0, 1)

@@ -23,17 +23,20 @@ KINDS = ["gauss", "gauss_outliers", "ties16", "uniform", "heavy", "equal", "twol
          "neginf", "allneginf", "zeros", "ascending", "descending", "spike", "flat"]
 
 
+@pytest.mark.parametrize("search", [0, 1])
 @pytest.mark.parametrize("tier", [1, 2])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_forced_tiers_all_kinds(tier, dtype):
-    """Light (1) and heavy (2) tail tiers on the same rows as the default tier."""
+def test_forced_tiers_all_kinds(tier, dtype, search):
+    """Light (1) and heavy (2) tail tiers on the same rows as the default tier,
+    with small candidate sets sorted and scanned (search 0) or searched with
+    pivots like every other row (search 1)."""
     import top_selection_sigma_amd as q
 
     for i, kind in enumerate(KINDS):
         x = w.make_rows(6, 7001, dtype, kind, seed=900 + i)
-        _say(f"tier {tier} {kind} {dtype}")
-        g = run_gpu(x, 400, options=q.Options(tier=tier))
-        check(x, g, oracle_for(x, 400), 400, f"tier {tier} {kind} {dtype}")
+        _say(f"tier {tier} {kind} {dtype} search {search}")
+        g = run_gpu(x, 400, options=q.Options(tier=tier, pivot_search_only=search))
+        check(x, g, oracle_for(x, 400), 400, f"tier {tier} {kind} {dtype} search {search}")
 
 
 @pytest.mark.parametrize("V", [3001, 4099, 20000])
@@ -44,9 +47,11 @@ def test_bitmap_mask_rows(V, tier):
     import top_selection_sigma_amd as q
 
     x = w.make_rows(512, V, "bf16", "gauss_outliers", seed=V + tier)
-    _say(f"bitmap V={V} tier {tier}")
-    g = run_gpu(x, 64, options=q.Options(tier=tier))
-    check(x, g, oracle_for(x, 64), 64, f"bitmap V={V} tier {tier}")
+    ref = oracle_for(x, 64)
+    for search in (0, 1):
+        _say(f"bitmap V={V} tier {tier} search {search}")
+        g = run_gpu(x, 64, options=q.Options(tier=tier, pivot_search_only=search))
+        check(x, g, ref, 64, f"bitmap V={V} tier {tier} search {search}")
 
 
 @pytest.mark.parametrize("kind", ["ties16", "smallint", "neginf", "equal"])
@@ -58,9 +63,10 @@ def test_bitmap_and_scattered_masks_agree_with_oracle(kind):
     x = w.make_rows(512, 2500, "f32", kind, seed=31)
     ref = oracle_for(x, 100)
     for mode in (0, 1):
-        _say(f"mask mode {mode} {kind}")
-        g = run_gpu(x, 100, options=q.Options(mask_mode=mode))
-        check(x, g, ref, 100, f"mask mode {mode} {kind}")
+        for search in (0, 1):
+            _say(f"mask mode {mode} {kind} search {search}")
+            g = run_gpu(x, 100, options=q.Options(mask_mode=mode, pivot_search_only=search))
+            check(x, g, ref, 100, f"mask mode {mode} {kind} search {search}")
 
 
 @pytest.mark.parametrize("mode", [0, 1, 2])
@@ -72,7 +78,7 @@ def test_pivot_modes_match_oracle(mode, kind, dtype):
     import top_selection_sigma_amd as q
 
     x = w.make_rows(8, 30000, dtype, kind, seed=12 + mode)
-    g = run_gpu(x, 300, options=q.Options(pivot_mode=mode))
+    g = run_gpu(x, 300, options=q.Options(pivot_mode=mode, pivot_search_only=1))
     check(x, g, oracle_for(x, 300), 300, f"pivot mode {mode} {kind}")
 
 
@@ -228,3 +234,52 @@ def test_two_streams_ten_calls_each_are_identical():
                 n = min(int(g.count[r]), 256)
                 assert np.array_equal(g.idx[r, :n], first.idx[r, :n])
     assert len(q._ws_cache) >= 2
+
+
+@pytest.mark.parametrize("chunks", [2, 3, 16])
+def test_chunked_tails_overlap_and_agree(chunks):
+    """Row chunks whose tails run on the library's second stream: the same
+    outputs as one chunk, draws included (the draw's counter is the batch row),
+    and parity with the oracle; diagnostics land on the right rows."""
+    import torch
+
+    import top_selection_sigma_amd as q
+
+    x = w.make_rows(300, 9000, "bf16", "gauss_outliers", seed=60)
+    g1 = run_gpu(x, 300, options=q.Options(chunks=1))
+    gc = run_gpu(x, 300, options=q.Options(chunks=chunks))
+    check(x, gc, oracle_for(x, 300), 300, f"chunks {chunks}")
+    assert np.array_equal(g1.mask, gc.mask) and np.array_equal(g1.count, gc.count)
+    assert np.array_equal(g1.diag[:, 3], gc.diag[:, 3])
+    from parity import device_logits
+
+    dev = torch.device("cuda", 0)
+    lg = device_logits(x, dev)
+    k = torch.from_numpy(x.k).to(dev)
+    p = torch.from_numpy(x.p).to(dev)
+    t1 = q.sample(lg, k, p, seed=3, offset=1, idx_cap=300, options=q.Options(chunks=1))
+    tc = q.sample(lg, k, p, seed=3, offset=1, idx_cap=300, options=q.Options(chunks=chunks))
+    torch.cuda.synchronize()
+    assert np.array_equal(t1[0].cpu().numpy(), tc[0].cpu().numpy())
+    n = np.minimum(t1[3].cpu().numpy(), 300)
+    pa, pb = t1[2].cpu().numpy(), tc[2].cpu().numpy()
+    for b in range(300):
+        assert np.array_equal(pa[b, :n[b]], pb[b, :n[b]])
+
+
+@pytest.mark.parametrize("n_kind", ["gauss", "ties16", "smallint", "twolevel", "neginf", "zeros"])
+def test_small_sets_sorted_and_searched_agree(n_kind):
+    """The sort-and-scan path and the pivot searches give identical outputs
+    (masks, indices, counts, diagnostics of the kept set) on rows whose
+    candidate sets straddle the 2048 limit."""
+    import top_selection_sigma_amd as q
+
+    x = w.make_rows(40, 60000, "f32", n_kind, seed=8)
+    x.k[:] = np.array([1, 5, 50, 500, 1500, 2047, 0, 0] * 5, np.int32)
+    x.p[:] = np.array([1.0, 0.9, 0.5, 1.0, 0.99, 1.0, 0.7, 0.999] * 5, np.float32)
+    ref = oracle_for(x, 2100)
+    a = run_gpu(x, 2100, options=q.Options(pivot_search_only=0))
+    b = run_gpu(x, 2100, options=q.Options(pivot_search_only=1))
+    check(x, a, ref, 2100, f"sorted {n_kind}")
+    check(x, b, ref, 2100, f"searched {n_kind}")
+    assert np.array_equal(a.count, b.count) and np.array_equal(a.mask, b.mask)

@@ -87,24 +87,30 @@ KINDS = ["gauss", "gauss_outliers", "ties16", "uniform", "heavy", "equal", "twol
          "allneginf", "zeros", "spike", "flat"]
 
 
+@pytest.mark.parametrize("search", [0, 1])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_sample_all_kinds_mixed_controls(dtype):
+def test_sample_all_kinds_mixed_controls(dtype, search):
+    import top_selection_sigma_amd as q
+
     for i, kind in enumerate(KINDS):
         x = w.make_rows(24, 6007, dtype, kind, seed=300 + i)
-        _say(f"sample {kind} {dtype}")
-        got = run_sample(x, 6007, seed=1000 + i, offset=i)
-        check_sample(x, 6007, 1000 + i, i, got, f"sample {kind} {dtype}")
+        _say(f"sample {kind} {dtype} search {search}")
+        got = run_sample(x, 6007, seed=1000 + i, offset=i, options=q.Options(pivot_search_only=search))
+        check_sample(x, 6007, 1000 + i, i, got, f"sample {kind} {dtype} search {search}")
 
 
+@pytest.mark.parametrize("search", [0, 1])
 @pytest.mark.parametrize("kind", ["gauss", "gauss_outliers", "heavy", "ties16"])
-def test_sample_keep_all_rows(kind):
+def test_sample_keep_all_rows(kind, search):
     """Rows with top-k and top-p off: the draw covers the whole row, so its
     candidates are collected for a mass of 0.999 and the logits left out are
     summed; draws past the candidates' mass take the slow path."""
+    import top_selection_sigma_amd as q
+
     x = w.make_rows(64, 32000, "bf16", kind, seed=77, k=0, p=1.0)
-    _say(f"keep-all {kind}")
-    got = run_sample(x, 64, seed=5, offset=9)
-    n = check_sample(x, 64, 5, 9, got, f"keep-all {kind}")
+    _say(f"keep-all {kind} search {search}")
+    got = run_sample(x, 64, seed=5, offset=9, options=q.Options(pivot_search_only=search))
+    n = check_sample(x, 64, 5, 9, got, f"keep-all {kind} search {search}")
     _say(f"band draws {n}")
 
 

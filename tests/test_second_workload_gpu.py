@@ -57,9 +57,10 @@ def test_index_order(tier, kind, dtype):
     x.k[:3] = 0
     x.p[:3] = 1.0  # keep-all rows: indices 0, 1, ...
     for cap in (64, 4096):
-        _say(f"index order {kind} {dtype} tier {tier} cap {cap}")
-        g = run_gpu(x, cap, options=q.Options(tier=tier, idx_order=1))
-        check_index_order(x, g, oracle_for(x, cap), cap, f"index order {kind} tier {tier} cap {cap}")
+        for search in (0, 1):
+            _say(f"index order {kind} {dtype} tier {tier} cap {cap} search {search}")
+            g = run_gpu(x, cap, options=q.Options(tier=tier, idx_order=1, pivot_search_only=search))
+            check_index_order(x, g, oracle_for(x, cap), cap, f"index order {kind} tier {tier} cap {cap} s {search}")
 
 
 @pytest.mark.parametrize("mask_mode", [0, 1])

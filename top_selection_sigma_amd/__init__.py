@@ -54,6 +54,8 @@ class _Options(ctypes.Structure):
         ("tier", ctypes.c_int32),
         ("mask_mode", ctypes.c_int32),
         ("idx_order", ctypes.c_int32),
+        ("chunks", ctypes.c_int32),
+        ("pivot_search_only", ctypes.c_int32),
     ]
 
 
@@ -72,13 +74,15 @@ class Options:
     tier: int = 0             # 0 automatic, 1 light, 2 heavy
     mask_mode: int = 0        # 0 automatic, 1 mask bytes stored one by one
     idx_order: int = 0        # 0 rank order, 1 ascending vocabulary index
+    chunks: int = 0           # 0 automatic, 1 no overlap, n row chunks overlapping tail and pass 1
+    pivot_search_only: int = 0  # 1: no sort-and-scan path for small candidate sets
 
     def to_c(self) -> _Options:
         return _Options(int(self.force_miss), float(self.delta_scale), int(self.pivot_mode),
                         int(self.slices), int(self.lds_cap), int(self.list_cap),
                         None if self.diag is None else self.diag.data_ptr(),
                         None if self.mid_event is None else self.mid_event.cuda_event,
-                        int(self.tier), int(self.mask_mode), int(self.idx_order))
+                        int(self.tier), int(self.mask_mode), int(self.idx_order), int(self.chunks), int(self.pivot_search_only))
 
 
 def lib() -> ctypes.CDLL:

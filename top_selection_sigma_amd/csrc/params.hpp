@@ -37,6 +37,8 @@ struct Params {
     float* out_prob;     // sampling: [batch][idx_cap] probabilities beside out_idx, or null
     uint64_t seed;       // sampling: Philox key
     uint64_t offset;     // sampling: Philox counter word 1
+    int64_t row0;
+    int32_t small_max;   // rows with at most this many candidates take the sort-and-scan path (0: none)        // batch row of this launch's row 0 (the draw's counter uses batch rows)
 };
 
 // Records that pass 1 leaves for the tail. Every word is written by plain

@@ -17,6 +17,8 @@ namespace {
 using qrita::Params;
 
 constexpr int64_t kListMax = 32768;   // per-row candidate list (entries of 8 bytes)
+constexpr int kMaxChunks = 16;        // row chunks of one call
+constexpr int kSmallSet = 2048;       // candidate sets sorted and scanned instead of searched
 constexpr int kPass1Threads = 256;
 constexpr int kSampleN = 2048;        // pass 1 sample (its LDS stage holds at least this many entries)
 constexpr int kStageCap = 2048;       // pass 1 LDS candidate stage
@@ -48,6 +50,7 @@ struct Plan {
     int list_cap;    // usable entries of a row list
     int sub_cap;     // list entries per slice
     bool bitmap;     // the tail writes whole mask rows
+    int chunks;      // row chunks whose tails overlap the next chunk's streaming pass
 };
 
 bool dtype_ok(int d) { return d == QRITA_F32 || d == QRITA_BF16 || d == QRITA_F16; }
@@ -101,6 +104,13 @@ Plan choose_plan(int64_t B, int64_t V, int64_t esize, int64_t idx_cap, const qri
     t.list_cap = (int)lc;
     t.sub_cap = (int)std::max<int64_t>(1, lc / S);
     t.bitmap = B >= 512 && (uint64_t)V <= (uint64_t)ti.bitmap_bits && !(o && o->mask_mode == 1);
+    // on request, the batch is cut into chunks of whole multiples of 8 rows
+    // (the XCD dealing of rows): the tail of chunk c runs on a second stream
+    // while the streaming pass reads chunk c + 1
+    int ch = 1;  // measured: overlapping on two streams was slower at every shape (ablation leg)
+    if (o && o->chunks > 0) ch = o->chunks;
+    ch = (int)std::min<int64_t>(ch, std::max<int64_t>(1, B / 8));
+    t.chunks = std::min(ch, kMaxChunks);
     return t;
 }
 
@@ -122,6 +132,31 @@ bool device_supported() {
     return s == 1;
 }
 
+// The second stream of chunked calls, per device: created once (default
+// priority, non-blocking), with a pool of ordering events. The launch
+// sequence of a chunked call holds the device's mutex, so concurrent calls
+// never interleave their uses of the events.
+struct SideStream {
+    std::mutex mu;
+    std::once_flag once;
+    hipStream_t stream = nullptr;
+    hipEvent_t ev[kMaxChunks + 1] = {};
+    bool ok = false;
+};
+SideStream g_side[kMaxDevices];
+
+SideStream* side_for(int dev) {
+    if (dev < 0 || dev >= kMaxDevices) return nullptr;
+    SideStream& sd = g_side[dev];
+    std::call_once(sd.once, [&sd] {
+        bool ok = hipStreamCreateWithFlags(&sd.stream, hipStreamNonBlocking) == hipSuccess;
+        for (int i = 0; ok && i <= kMaxChunks; ++i)
+            ok = hipEventCreateWithFlags(&sd.ev[i], hipEventDisableTiming) == hipSuccess;
+        sd.ok = ok;
+    });
+    return sd.ok ? &sd : nullptr;
+}
+
 // The draw of a sampling call (null for a selection).
 struct Draw {
     int32_t* token;
@@ -133,14 +168,36 @@ bool options_valid(const qrita_options* opt) {
     return !opt || !(((uintptr_t)opt->diag & 3u) || opt->pivot_mode < 0 || opt->pivot_mode > 2 ||
                      opt->slices < 0 || opt->lds_cap < 0 || opt->list_cap < 0 || opt->tier < 0 ||
                      opt->tier > 2 || opt->mask_mode < 0 || opt->mask_mode > 1 || opt->idx_order < 0 ||
-                     opt->idx_order > 1 ||
+                     opt->idx_order > 1 || opt->chunks < 0 || opt->chunks > kMaxChunks ||
+                     opt->pivot_search_only < 0 || opt->pivot_search_only > 1 ||
                      !(opt->delta_scale == opt->delta_scale));
+}
+
+// The params of rows [r0, r0 + n) of a call as a batch of its own.
+Params rows_of(const Params& P, int64_t r0, int64_t n) {
+    Params c = P;
+    const int64_t V = P.vocab, es = P.dtype == 0 ? 4 : 2;
+    c.logits = (const char*)P.logits + r0 * V * es;
+    if (P.mask) c.mask = P.mask + r0 * V;
+    if (P.out_idx) c.out_idx = P.out_idx + r0 * (int64_t)P.idx_cap;
+    if (P.out_count) c.out_count = P.out_count + r0;
+    if (P.k) c.k = P.k + r0;
+    if (P.p) c.p = P.p + r0;
+    if (P.diag) c.diag = P.diag + r0 * 8;
+    if (P.out_token) c.out_token = P.out_token + r0;
+    if (P.out_prob) c.out_prob = P.out_prob + r0 * (int64_t)P.idx_cap;
+    c.rowrec = P.rowrec + r0 * qrita::R_WORDS;
+    c.slrec = P.slrec + r0 * qrita::kMaxSlices * qrita::S_WORDS;
+    c.glist = P.glist + r0 * (int64_t)P.list_stride;
+    c.batch = n;
+    c.row0 = P.row0 + r0;
+    return c;
 }
 
 int select_impl(const void* logits, int64_t batch, int64_t vocab, int dtype, const int32_t* k,
                 const float* p, uint8_t* out_mask, int32_t* out_idx, int32_t* out_count,
                 int64_t idx_cap, void* workspace, size_t workspace_bytes, void* stream,
-                const qrita_options* opt, const Draw* draw = nullptr) {
+                const qrita_options* opt, const Draw* draw = nullptr, bool one_stream = false) {
     if (!logits || batch < 0 || vocab <= 0 || vocab > INT32_MAX || idx_cap < 0 ||
         idx_cap > INT32_MAX)
         return QRITA_EINVAL;
@@ -195,6 +252,11 @@ int select_impl(const void* logits, int64_t batch, int64_t vocab, int dtype, con
     P.pivot_mode = opt ? opt->pivot_mode : 0;
     P.bitmap = t.bitmap ? 1 : 0;
     P.dtype = dtype;
+    // rows with at most kSmallSet candidates are sorted outright and scanned
+    // (unless the options ask for the pivot searches on every row)
+    P.small_max = (opt && opt->pivot_search_only)
+                      ? 0
+                      : std::min(kSmallSet, (t.heavy ? qrita::tier_heavy().csort : qrita::tier_light().csort) / 2);
     P.idx_order = (opt && opt->idx_order) ? 1 : 0;
     if (draw) {
         P.out_token = draw->token;
@@ -204,14 +266,48 @@ int select_impl(const void* logits, int64_t batch, int64_t vocab, int dtype, con
     }
 
     hipStream_t s = (hipStream_t)stream;
-    const unsigned groups = (unsigned)(((batch + 7) / 8) * 8 * (int64_t)t.slices);
     const size_t lds = ((size_t)std::max(t.stage_cap, kSampleN) + (size_t)(kPass1Threads / 64) * kWaveSpill) * 8;
-    if (qrita::launch_pass1(P, groups, lds, s) != hipSuccess) return QRITA_ELAUNCH;
-    if (opt && opt->mid_event) {
+    auto pass1 = [&](const Params& Q, hipStream_t st) {
+        const unsigned groups = (unsigned)(((Q.batch + 7) / 8) * 8 * (int64_t)t.slices);
+        return qrita::launch_pass1(Q, groups, lds, st);
+    };
+    auto tail = [&](const Params& Q, hipStream_t st) {
+        return t.heavy ? qrita::launch_tail_heavy(Q, st) : qrita::launch_tail_light(Q, st);
+    };
+    SideStream* sd = nullptr;
+    if (t.chunks > 1 && !one_stream) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess) return QRITA_ELAUNCH;
+        sd = side_for(dev);  // no second stream: one chunk
+    }
+    if (!sd) {
+        if (pass1(P, s) != hipSuccess) return QRITA_ELAUNCH;
+        if (opt && opt->mid_event) {
+            if (hipEventRecord((hipEvent_t)opt->mid_event, s) != hipSuccess) return QRITA_ELAUNCH;
+        }
+        return tail(P, s) == hipSuccess ? QRITA_OK : QRITA_ELAUNCH;
+    }
+    // chunk c: pass 1 on the caller's stream, then its tail on the side
+    // stream once that pass is done, while pass 1 of chunk c + 1 runs; the
+    // caller's stream finally waits for the last tail
+    std::lock_guard<std::mutex> lock(sd->mu);
+    const int C = t.chunks;
+    const int64_t per = (batch + C - 1) / C;
+    const int64_t step = (per + 7) / 8 * 8;
+    int used = 0;
+    for (int64_t r0 = 0; r0 < batch; r0 += step, ++used) {
+        const Params Q = rows_of(P, r0, std::min(step, batch - r0));
+        if (pass1(Q, s) != hipSuccess) return QRITA_ELAUNCH;
+        if (hipEventRecord(sd->ev[used], s) != hipSuccess) return QRITA_ELAUNCH;
+        if (hipStreamWaitEvent(sd->stream, sd->ev[used], 0) != hipSuccess) return QRITA_ELAUNCH;
+        if (tail(Q, sd->stream) != hipSuccess) return QRITA_ELAUNCH;
+    }
+    if (opt && opt->mid_event) {  // after the last streaming pass
         if (hipEventRecord((hipEvent_t)opt->mid_event, s) != hipSuccess) return QRITA_ELAUNCH;
     }
-    const hipError_t err = t.heavy ? qrita::launch_tail_heavy(P, s) : qrita::launch_tail_light(P, s);
-    return err == hipSuccess ? QRITA_OK : QRITA_ELAUNCH;
+    if (hipEventRecord(sd->ev[kMaxChunks], sd->stream) != hipSuccess) return QRITA_ELAUNCH;
+    if (hipStreamWaitEvent(s, sd->ev[kMaxChunks], 0) != hipSuccess) return QRITA_ELAUNCH;
+    return QRITA_OK;
 }
 
 // Static device scratch for qrita_select_noalloc: the workspace of callers
@@ -260,7 +356,7 @@ int qrita_select_noalloc(const void* logits, int64_t batch, int64_t vocab, int d
     const int st = scratch_for_current_device(&ws);
     if (st != QRITA_OK) return st;
     return select_impl(logits, batch, vocab, dtype, k, p, out_mask, out_idx, out_count, idx_cap, ws,
-                       (size_t)QRITA_NOALLOC_SCRATCH_BYTES, stream, nullptr);
+                       (size_t)QRITA_NOALLOC_SCRATCH_BYTES, stream, nullptr, nullptr, true);
 }
 
 size_t qrita_workspace_bytes(int64_t batch, int64_t vocab, int dtype, int64_t idx_cap) {

@@ -33,23 +33,25 @@ struct TailTier {
     static constexpr int NB = NB_;         // bucket-sort bins
     static constexpr int WAVES_PER_SIMD = CFULL_ <= 12288 ? 2 : 1;  // rows resident per CU
     // LDS layout (bytes). Search phase: keys, then the wave segments. Emit
-    // phase (after the search): the words to sort, the bucket sort's
-    // positions in bin order and each word's bin (16 bits each), bin counts
-    // and code starts. After
-    // the sort, everything past the words holds the mask bitmap; the bitonic
-    // fallback sorts in everything from the words on.
+    // phase (after the search): the words to sort; then a region that holds
+    // either the words again in bin order (the bucket sort's usual case) or,
+    // when bins get sized in proportion to the codes, the positions in bin
+    // order, each word's bin (16 bits each) and the code starts; then the
+    // bin counts. After the sort, everything past the words holds the mask
+    // bitmap; the bitonic fallback sorts in everything from the words on.
     static constexpr size_t A_OFF = 0;
     static constexpr size_t W_OFF = A_OFF + (size_t)CFULL * 4;
     static constexpr size_t SEARCH_END = W_OFF + (size_t)NW * SEG * 8;
     static constexpr size_t SA_OFF = 0;
     static constexpr size_t SB_OFF = SA_OFF + (size_t)(CSORT + 8) * 8;
     static constexpr size_t BO_OFF = SB_OFF + ((size_t)CSORT * 2 + 15) / 16 * 16;
-    static constexpr size_t BINS_OFF = BO_OFF + ((size_t)CSORT * 2 + 15) / 16 * 16;
-    static constexpr size_t HC_OFF = BINS_OFF + (size_t)(NB + 4) * 4;
-    static constexpr size_t EMIT_END = HC_OFF + (size_t)(NB + 4) * 4;
+    static constexpr size_t HC_OFF = BO_OFF + ((size_t)CSORT * 2 + 15) / 16 * 16;
+    static constexpr size_t BINS_OFF = SB_OFF + (size_t)CSORT * 8;
+    static constexpr size_t EMIT_END = BINS_OFF + (size_t)(NB + 4) * 4;
     static constexpr size_t LDS = SEARCH_END > EMIT_END ? SEARCH_END : EMIT_END;
     static constexpr uint32_t BITMAP_BITS = (uint32_t)((LDS - SB_OFF) * 8);
     static_assert(CSORT <= 65536, "16-bit positions");
+    static_assert(HC_OFF + (size_t)(NB + 4) * 4 <= BINS_OFF, "positions, bins of words and code starts in the words' region");
     static_assert(LDS - SA_OFF >= (size_t)2 * CSORT * 8, "bitonic fallback region");
     static_assert(SEARCH_END % 16 == 0 && SB_OFF % 16 == 0 && BINS_OFF % 16 == 0, "alignment");
 };
@@ -858,7 +860,9 @@ struct RankOut {
     float* prob;     // probabilities beside the indices (null: none)
     float mref;      // the row maximum the masses are taken against
     double inv_s;    // 1 / the kept set's fixed-point mass
+    uint64_t* sorted;  // LDS: word of rank r to sorted[r] (null: none)
     QRITA_DEV void put(uint32_t r, uint64_t w) const {
+        if (sorted) sorted[r] = w;
         if (r < lout) {
             out[r] = (int32_t)cand_idx(w);
             if (prob) prob[r] = (float)((double)mass_fx(cand_key(w), mref) * inv_s);
@@ -935,11 +939,12 @@ QRITA_DEV void bitonic_lds(uint64_t* a, uint32_t np, uint32_t cnt, const RankOut
 // (lmax - low), so tie groups spread too. First every code gets the same
 // number of bins; if a bin then holds more than kMaxBin words, each code
 // instead gets a run of bins in proportion to how many words it holds (code
-// starts in hc). The words' positions are scattered into bins (pos, LDS); a
-// word's rank is its bin's start plus the number of larger words in its bin,
-// counted directly, so the result does not depend on the order of the LDS
-// atomics that fill the bins. Returns false, having written nothing, when a
-// bin still holds more than kMaxBin words.
+// starts in hc). The words (equal runs; bw) or their positions (proportional
+// runs; pos) are scattered into bins; a word's rank is its bin's start plus
+// the number of larger words in its bin, counted directly, so the result does
+// not depend on the order of the LDS atomics that fill the bins. Returns
+// false, having written nothing, when a bin still holds more than kMaxBin
+// words.
 constexpr uint32_t kMaxBin = 96;
 
 // Extents of a set of words, gathered with it (block-uniform): key and
@@ -949,8 +954,8 @@ struct SortExt {
 };
 
 template <int NT, int NB>
-QRITA_DEV bool bucket_sort(const uint64_t* a, uint32_t cnt, const SortExt& ex, const RankOut& ro, uint16_t* pos,
-                           uint16_t* binof, uint32_t* bins, uint32_t* hc, Shared& sh, int& rb) {
+QRITA_DEV bool bucket_sort(const uint64_t* a, uint32_t cnt, const SortExt& ex, const RankOut& ro, uint64_t* bw,
+                           uint16_t* pos, uint16_t* binof, uint32_t* bins, uint32_t* hc, Shared& sh, int& rb) {
     const uint32_t t = threadIdx.x;
     const uint32_t kmn = ex.kmn, kmx = ex.kmx, lmn = ex.lmn, lmx = ex.lmx;
     const uint32_t nb = min((uint32_t)NB, 2u * next_pow2(cnt));
@@ -984,16 +989,68 @@ QRITA_DEV bool bucket_sort(const uint64_t* a, uint32_t cnt, const SortExt& ex, c
         const uint32_t i1 = i + NT;
         const uint32_t b0 = bin_eq(a[i]);
         const uint32_t b1 = i1 < cnt ? bin_eq(a[i1]) : 0u;
-        binof[i] = (uint16_t)b0;
         atomicAdd(&bins[b0], 1u);
-        if (i1 < cnt) {
-            binof[i1] = (uint16_t)b1;
-            atomicAdd(&bins[b1], 1u);
-        }
+        if (i1 < cnt) atomicAdd(&bins[b1], 1u);
     }
     lds_sync();
     uint32_t big = scan_counts<NT, NB>(bins, nb, sh, rb);
-    if (big > kMaxBin) {
+    if (big <= kMaxBin) {
+        // the usual case: the words themselves go to their bins (bw), so
+        // that ranking reads each bin's words side by side; a word's bin is
+        // recomputed from the word
+        for (uint32_t i0 = t; i0 < cnt; i0 += 4 * NT) {
+            uint64_t w[4];
+            uint32_t q[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint32_t i = i0 + (uint32_t)u * NT;
+                w[u] = a[i < cnt ? i : i0];
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint32_t i = i0 + (uint32_t)u * NT;
+                q[u] = i < cnt ? atomicAdd(&bins[bin_eq(w[u])], 1u) : 0u;
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (i0 + (uint32_t)u * NT < cnt) bw[q[u]] = w[u];
+        }
+        lds_sync();
+        // afterwards bins[i] is the end of bin i: a word's rank is its bin's
+        // start plus the number of larger words in its bin
+        for (uint32_t p0 = t; p0 < cnt; p0 += 4 * NT) {
+            uint64_t w[4];
+            uint32_t s0[4], e0[4], r[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint32_t p = p0 + (uint32_t)u * NT;
+                w[u] = bw[p < cnt ? p : p0];
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint32_t bi = bin_eq(w[u]);
+                s0[u] = bi ? bins[bi - 1] : 0u;
+                e0[u] = bins[bi];
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                r[u] = s0[u];
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const uint32_t q = s0[u] + (uint32_t)m;
+                    const uint64_t y = bw[q < e0[u] ? q : s0[u]];
+                    r[u] += (q < e0[u] && y > w[u]) ? 1u : 0u;
+                }
+                for (uint32_t q = s0[u] + 4; q < e0[u]; ++q) r[u] += bw[q] > w[u] ? 1u : 0u;
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (p0 + (uint32_t)u * NT < cnt) ro.put(r[u], w[u]);
+        }
+        lds_sync();
+        return true;
+    }
+    {
         // runs of bins in proportion to the codes' sizes
         for (uint32_t i = t; i <= ncodes; i += NT) hc[i] = 0u;
         lds_sync();
@@ -1020,34 +1077,72 @@ QRITA_DEV bool bucket_sort(const uint64_t* a, uint32_t cnt, const SortExt& ex, c
         big = scan_counts<NT, NB>(bins, nb, sh, rb);
         if (big > kMaxBin) return false;
     }
-    // scatter the positions; afterwards bins[i] is the end of bin i
-    for (uint32_t i = t; i < cnt; i += 2 * NT) {
-        const uint32_t i1 = i + NT;
-        const uint32_t q0 = atomicAdd(&bins[binof[i]], 1u);
-        pos[q0] = (uint16_t)i;
-        if (i1 < cnt) {
-            const uint32_t q1 = atomicAdd(&bins[binof[i1]], 1u);
-            pos[q1] = (uint16_t)i1;
+    // scatter the positions, four words per thread and step so that their
+    // LDS round trips overlap; afterwards bins[i] is the end of bin i
+    for (uint32_t i0 = t; i0 < cnt; i0 += 4 * NT) {
+        uint32_t b[4], q[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const uint32_t i = i0 + (uint32_t)u * NT;
+            b[u] = binof[i < cnt ? i : i0];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const uint32_t i = i0 + (uint32_t)u * NT;
+            q[u] = i < cnt ? atomicAdd(&bins[b[u]], 1u) : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const uint32_t i = i0 + (uint32_t)u * NT;
+            if (i < cnt) pos[q[u]] = (uint16_t)i;
         }
     }
     lds_sync();
-    // ranks, by position in the binned order: the lanes of a wave mostly
-    // share a bin, so their scans take the same number of steps; four bin
-    // mates per step (the word itself stands in past the bin's end)
-    for (uint32_t p = t; p < cnt; p += NT) {
-        const uint32_t i = pos[p];
-        const uint64_t w = a[i];
-        const uint32_t bi = binof[i];
-        const uint32_t s0 = bi ? bins[bi - 1] : 0u, e0 = bins[bi];
-        uint32_t r = s0;
-        for (uint32_t q = s0; q < e0; q += 4) {
-            const uint32_t j0 = pos[q];
-            const uint32_t j1 = q + 1 < e0 ? pos[q + 1] : i;
-            const uint32_t j2 = q + 2 < e0 ? pos[q + 2] : i;
-            const uint32_t j3 = q + 3 < e0 ? pos[q + 3] : i;
-            r += (a[j0] > w ? 1u : 0u) + (a[j1] > w ? 1u : 0u) + (a[j2] > w ? 1u : 0u) + (a[j3] > w ? 1u : 0u);
+    // ranks, by position in the binned order: a word's rank is its bin's
+    // start plus the number of larger bin mates. Four positions per thread
+    // and step, each with its first four bin mates (the word itself stands in
+    // past the bin's end), so that the chains of LDS reads overlap; longer
+    // bins continue four mates at a time.
+    for (uint32_t p0 = t; p0 < cnt; p0 += 4 * NT) {
+        uint32_t i[4], s0[4], e0[4], r[4];
+        uint64_t w[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const uint32_t p = p0 + (uint32_t)u * NT;
+            i[u] = pos[p < cnt ? p : p0];
         }
-        ro.put(r, w);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            w[u] = a[i[u]];
+            const uint32_t bi = binof[i[u]];
+            s0[u] = bi ? bins[bi - 1] : 0u;
+            e0[u] = bins[bi];
+        }
+        uint32_t j[4][4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) j[u][m] = s0[u] + m < e0[u] ? pos[s0[u] + m] : i[u];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            r[u] = s0[u];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) r[u] += a[j[u][m]] > w[u] ? 1u : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            for (uint32_t q = s0[u] + 4; q < e0[u]; q += 4) {
+                const uint32_t j0 = pos[q];
+                const uint32_t j1 = q + 1 < e0[u] ? pos[q + 1] : i[u];
+                const uint32_t j2 = q + 2 < e0[u] ? pos[q + 2] : i[u];
+                const uint32_t j3 = q + 3 < e0[u] ? pos[q + 3] : i[u];
+                r[u] += (a[j0] > w[u] ? 1u : 0u) + (a[j1] > w[u] ? 1u : 0u) + (a[j2] > w[u] ? 1u : 0u) +
+                        (a[j3] > w[u] ? 1u : 0u);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (p0 + (uint32_t)u * NT < cnt) ro.put(r[u], w[u]);
     }
     lds_sync();
     return true;
@@ -1071,7 +1166,8 @@ QRITA_DEV void sort_words(uint32_t cnt, const SortExt& ex, RankOut ro, Shared& s
         rank_sort<NT>(a, cnt, ro, bins);
         return;
     }
-    if (bucket_sort<NT, T::NB>(a, cnt, ex, ro, pos, binof, bins, hc, sh, rb)) return;
+    uint64_t* bw = (uint64_t*)(dyn_lds() + T::SB_OFF);
+    if (bucket_sort<NT, T::NB>(a, cnt, ex, ro, bw, pos, binof, bins, hc, sh, rb)) return;
     const uint32_t np = next_pow2(cnt);  // < 2 cnt: inside the fallback region
     for (uint32_t i = cnt + threadIdx.x; i < np; i += NT) a[i] = 0ull;
     lds_sync();
@@ -1088,12 +1184,12 @@ QRITA_DEV void sort_words(uint32_t cnt, const SortExt& ex, RankOut ro, Shared& s
 // be one of the set's keys (the reference for the shared low bits).
 template <int NT, class L>
 QRITA_DEV uint32_t gather_words(const L& lsrc, uint64_t* a, uint32_t cap, uint64_t lo_w, uint64_t hi_w, SortExt& ex,
-                                Shared& sh, int& rb) {
+                                Shared& sh, int& rb, uint32_t key_ref = 0u) {
     block_sync<NT>();
     if (threadIdx.x == 0) sh.gather_n = 0;
     lds_sync();
     const uint32_t lane = tid_here() & (kWave - 1);
-    const uint32_t key0 = cand_key(lo_w);
+    const uint32_t key0 = key_ref ? key_ref : cand_key(lo_w);
     uint32_t kmn = 0xFFFFFFFFu, kmx = 0u, lmn = 0xFFFFFFFFu, lmx = 0u, tz = 32u;
     lsrc.visit([&](uint32_t key, uint32_t low) {
         const uint64_t w = ((uint64_t)key << 32) | low;
@@ -1286,6 +1382,9 @@ QRITA_DEV void mask_from_sorted(uint32_t cnt, uint64_t B, const RowOut& o) {
     write_mask_row<NT>(o.mrow, bm, o.V);
 }
 
+template <int NT>
+QRITA_DEV void bitmap_outputs(const uint32_t* bm, const RowOut& o, uint32_t Lout, Shared& sh, int& rb);
+
 // Probability of vocabulary entry i (index-ordered output reads its logit).
 QRITA_DEV float prob_at(const RowOut& o, uint32_t i) {
     uint32_t x;
@@ -1328,9 +1427,19 @@ QRITA_DEV void emit_row_by_index(C& c, const L& lsrc, const RowOut& o, bool all,
         if (key != 0 && w >= B) atomicOr(&bm[(~low) >> 5], 1u << ((~low) & 31u));
     });
     lds_sync();
+    bitmap_outputs<NT>(bm, o, Lout, sh, c.rb);
+}
+
+// The mask (whole row, or bytes into the zero-filled row) and the first Lout
+// kept indices in ascending order, from the kept set's bitmap bm in LDS:
+// each thread takes a run of bitmap words, and an exclusive prefix of their
+// bit counts over the block places its indices.
+template <int NT>
+QRITA_DEV void bitmap_outputs(const uint32_t* bm, const RowOut& o, uint32_t Lout, Shared& sh, int& rb) {
+    const uint32_t nw = (o.V + 31u) / 32u;
     if (o.mrow) {
         if (o.bitmap) {
-            write_mask_row<NT>(o.mrow, bm, V);
+            write_mask_row<NT>(o.mrow, bm, o.V);
         } else {
             for (uint32_t i = threadIdx.x; i < nw; i += NT) {
                 uint32_t bits = bm[i];
@@ -1353,7 +1462,7 @@ QRITA_DEV void emit_row_by_index(C& c, const L& lsrc, const RowOut& o, bool all,
     QRITA_WAVE_STEPS(op_add, 0u)
     const uint32_t wave_tot = readlane(x, kWave - 1);
     uint32_t total = 0;
-    const uint32_t before = wave_prefix<NT>(wave_tot, total, sh, c.rb);
+    const uint32_t before = wave_prefix<NT>(wave_tot, total, sh, rb);
     uint32_t r = before + x - cnt;
     for (uint32_t i = w0; i < w1 && r < Lout; ++i) {
         uint32_t bits = bm[i];
@@ -1551,7 +1660,7 @@ QRITA_DEV bool finish_row(const Params& P, int64_t row, const RowMode& md, const
             const CountOut r0 = search_count<NT, 0>(c, 0u, 1u, key_lo, n, (int64_t)kmax, 0u);
             token = (int32_t)cand_idx(tie_boundary<T>(lsrc, r0.v, 1u, r0.N, V, c.mode, sh, c.rb, dg.iters, true));
         } else {
-            MassSet ms{row_uniform(P.seed, P.offset, (uint64_t)row), 0.0, all, 0u, 0u};
+            MassSet ms{row_uniform(P.seed, P.offset, (uint64_t)(P.row0 + row)), 0.0, all, 0u, 0u};
             int64_t lo = key_lo;
             if (all) {
                 if (rest_fx) ms.rest = (double)rest_fx * (double)mass_f32(f32_key(__float_as_uint(rest_ref)), m);
@@ -1593,6 +1702,197 @@ QRITA_DEV bool finish_row(const Params& P, int64_t row, const RowMode& md, const
     if (P.out_token && threadIdx.x == 0) P.out_token[row] = token;
     rb = c.rb;
     dg.iters += c.iters;
+    return true;
+}
+
+// Exclusive prefix over the block of per-thread 64-bit values v (thread
+// order); total is the block's sum (uniform).
+template <int NT>
+QRITA_DEV uint64_t block_scan_u64(uint64_t v, uint64_t& total, Shared& sh, int& rb) {
+    constexpr int NW = NT / kWave;
+    const uint32_t lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    uint64_t x = v;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const uint32_t lo = (uint32_t)__shfl_up((int)(uint32_t)x, o, kWave);
+        const uint32_t hi = (uint32_t)__shfl_up((int)(uint32_t)(x >> 32), o, kWave);
+        if (lane >= (uint32_t)o) x += ((uint64_t)hi << 32) | lo;
+    }
+    const uint64_t wtot = ((uint64_t)readlane((uint32_t)(x >> 32), kWave - 1) << 32) | readlane((uint32_t)x, kWave - 1);
+    if (lane == 0) *(uint2*)&sh.slot[rb][wave][0] = make_uint2((uint32_t)wtot, (uint32_t)(wtot >> 32));
+    lds_sync();
+    uint64_t before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        const uint2 q = *(const uint2*)&sh.slot[rb][w][0];
+        const uint64_t t = ((uint64_t)q.y << 32) | q.x;
+        before += (uint32_t)w < wave ? t : 0ull;
+        all += t;
+    }
+    rb ^= 1;
+    total = uni(all);
+    return before + x - v;
+}
+
+// Smallest rank r < R whose running mass P_r (rank-order prefix of
+// mass_fx over s[0 .. R), starting from the thread's exclusive prefix) is at
+// least T, or R. Each thread walks its own run of ranks [r0, r1).
+template <int NT>
+QRITA_DEV uint32_t first_reaching(const uint64_t* s, uint32_t r0, uint32_t r1, uint64_t before, uint64_t T,
+                                  float m, uint32_t R, Shared& sh, int& rb) {
+    uint32_t hit = 0xFFFFFFFFu;
+    uint64_t run = before;
+    for (uint32_t r = r0; r < r1; ++r) {
+        run += mass_fx(cand_key(s[r]), m);
+        if (run >= T) {
+            hit = r;
+            break;
+        }
+    }
+    uint32_t mn[1] = {wave_min_u32(hit)};
+    comb_record<NT, 0, 0, 1>(nullptr, nullptr, mn, sh, rb);
+    return mn[0] < R ? mn[0] : R;
+}
+
+// Steps a4-a7 for a row with few candidates (n <= CSORT / 2, all in the list
+// lsrc): every candidate is gathered and sorted once, after which the rank
+// order answers top-k (the first K ranks), top-p (the first rank whose
+// running fixed-point mass reaches T = p * S) and the draw (the first rank
+// reaching u * S) directly. The quantities are those of finish_row's pivot
+// searches, rank for rank: the searches exist to avoid ordering a large
+// candidate set, and once the set is small enough to sort in one piece the
+// order needed for the index output answers them as well. Returns false on a
+// truncation miss (nothing written).
+template <class T, class L>
+QRITA_DEV bool finish_small(const Params& P, int64_t row, const RowMode& md, const L& lsrc, uint32_t n,
+                            uint32_t kmax, uint64_t rest_fx, float rest_ref, float t_gauss, Shared& sh, int& rb,
+                            TailDiag& dg) {
+    constexpr int NT = T::NT;
+    const uint32_t V = (uint32_t)P.vocab;
+    if (P.diag) {  // #{z >= Gaussian t} among the candidates, for diagnostics
+        const uint32_t key_t = f32_key(__float_as_uint(t_gauss));
+        uint32_t cc = 0;
+        lsrc.visit([&](uint32_t key, uint32_t) { cc += key >= key_t ? 1u : 0u; });
+        dg.n_t = (int32_t)comb_sum32<NT>(cc, sh, rb);
+    }
+    bool topk = md.topk, topp = md.topp;
+    uint32_t K = md.K;
+    if (md.K_t > 0 && n < md.K_t) return false;
+    if ((topp || md.sample_all) && n == 0) return false;
+    const float m = key_value(kmax);
+    if (topp && m == -__builtin_inff()) {  // all -inf: keep one token
+        topp = false;
+        topk = true;
+        K = 1;
+    }
+    const bool all = !topk && !topp;
+    // every candidate (a: the first half of the sort region), then in rank
+    // order (s: its second half, which no sort path reads for sets of at most
+    // half the region): s[r] is the word of rank r
+    uint64_t* a = (uint64_t*)(dyn_lds() + T::SA_OFF);
+    uint64_t* s = a + T::CSORT / 2;
+    SortExt ex;
+    const uint32_t cnt = gather_words<NT>(lsrc, a, (uint32_t)T::CSORT / 2, 1ull, ~0ull, ex, sh, rb, kmax);
+    RankOut so{nullptr, 0u, nullptr, 0u, nullptr, nullptr, 0.0f, 0.0, s};
+    sort_words<T>(cnt, ex, so, sh, rb);
+    // ranks the masses run over: the top-k set, or every candidate
+    const uint32_t R = topk ? (K < cnt ? K : cnt) : cnt;
+    const uint32_t per = (R + NT - 1u) / NT;
+    const uint32_t r0 = threadIdx.x * per < R ? threadIdx.x * per : R;
+    const uint32_t r1 = r0 + per < R ? r0 + per : R;
+    const bool masses = topp || P.out_token || P.out_prob;
+    uint64_t before = 0, total = 0;
+    if (masses && m != -__builtin_inff()) {
+        uint64_t loc = 0;
+        for (uint32_t r = r0; r < r1; ++r) loc += mass_fx(cand_key(s[r]), m);
+        before = block_scan_u64<NT>(loc, total, sh, rb);
+    }
+    // the logits outside the candidates (top-p-only and keep-all rows), in
+    // the same fixed point
+    const double rest =
+        (!topk && rest_fx) ? (double)rest_fx * (double)mass_f32(f32_key(__float_as_uint(rest_ref)), m) : 0.0;
+    uint32_t Lk = topk ? K : V;
+    if (topp) {
+        uint64_t Tq = (uint64_t)ceil((double)md.p * ((double)total + rest));
+        Tq = Tq ? Tq : 1u;
+        if (!topk && total < Tq) return false;  // the candidates hold less than p of the mass
+        const uint32_t cut = first_reaching<NT>(s, r0, r1, before, Tq, m, R, sh, rb);
+        Lk = cut < R ? cut + 1u : R;
+    }
+    // the kept set's mass: the prefix through rank Lk - 1 (plus the outside
+    // mass for keep-all rows)
+    double s_kept = 0.0;
+    int32_t token = -1;
+    if (masses && m != -__builtin_inff()) {
+        const uint32_t lastr = (all ? R : (Lk < R ? Lk : R)) - 1u;
+        uint64_t mine = 0;
+        if (lastr >= r0 && lastr < r1) {
+            uint64_t run = before;
+            for (uint32_t r = r0; r <= lastr; ++r) run += mass_fx(cand_key(s[r]), m);
+            mine = run;
+        }
+        uint64_t got[1] = {wave_sum_u64(mine)};
+        comb_record<NT, 0, 1, 0>(nullptr, got, nullptr, sh, rb);
+        s_kept = (double)got[0] + (all ? rest : 0.0);
+        if (P.out_token) {
+            uint64_t Tu = (uint64_t)ceil(row_uniform(P.seed, P.offset, (uint64_t)(P.row0 + row)) * s_kept);
+            Tu = Tu ? Tu : 1u;
+            if (all && (double)Tu > (double)got[0]) return false;  // the draw falls outside the candidates
+            const uint32_t rt = first_reaching<NT>(s, r0, r1, before, Tu, m, R, sh, rb);
+            token = (int32_t)cand_idx(s[rt < R ? rt : R - 1u]);
+        }
+    } else if (P.out_token) {
+        token = (int32_t)cand_idx(s[0]);  // no finite logit: rank 0
+    }
+    const uint32_t L_ = all ? V : Lk;
+    const void* rowp = P.dtype != 0 ? (const void*)((const uint16_t*)P.logits + row * (int64_t)V)
+                                    : (const void*)((const float*)P.logits + row * (int64_t)V);
+    RowOut o{(P.out_idx && P.idx_cap > 0) ? P.out_idx + row * (int64_t)P.idx_cap : nullptr, (uint32_t)P.idx_cap,
+             (P.mask && !md.keep_all) ? P.mask + row * (int64_t)V : nullptr, P.bitmap != 0, V,
+             (P.out_prob && P.idx_cap > 0) ? P.out_prob + row * (int64_t)P.idx_cap : nullptr, m,
+             s_kept > 0.0 ? 1.0 / s_kept : 0.0, rowp, (int)P.dtype};
+    const uint32_t Lout = o.idx ? (L_ < o.idx_cap ? L_ : o.idx_cap) : 0u;
+    if (P.idx_order && !all) {
+        uint32_t* bm = (uint32_t*)(dyn_lds() + T::SB_OFF);
+        const uint32_t nw = (V + 31u) / 32u;
+        clear_words(bm, nw + 1u, NT);  // one word past the row: write_mask_row reads it
+        lds_sync();
+        for (uint32_t r = threadIdx.x; r < Lk; r += NT) {
+            const uint32_t i = cand_idx(s[r]);
+            atomicOr(&bm[i >> 5], 1u << (i & 31u));
+        }
+        lds_sync();
+        bitmap_outputs<NT>(bm, o, Lout, sh, rb);
+    } else if (P.idx_order) {  // keep-all row: 0, 1, ..., Lout - 1
+        for (uint32_t r = threadIdx.x; r < Lout; r += NT) {
+            o.idx[r] = (int32_t)r;
+            if (o.prob) o.prob[r] = prob_at(o, r);
+        }
+    } else {
+        for (uint32_t r = threadIdx.x; r < Lout; r += NT) {
+            const uint64_t w = s[r];
+            o.idx[r] = (int32_t)cand_idx(w);
+            if (o.prob) o.prob[r] = (float)((double)mass_fx(cand_key(w), m) * o.inv_s);
+        }
+        if (o.mrow && !all) {
+            if (o.bitmap) {
+                uint32_t* bm = (uint32_t*)(dyn_lds() + T::SB_OFF);
+                clear_words(bm, (V + 31u) / 32u + 1u, NT);
+                lds_sync();
+                for (uint32_t r = threadIdx.x; r < Lk; r += NT) {
+                    const uint32_t i = cand_idx(s[r]);
+                    atomicOr(&bm[i >> 5], 1u << (i & 31u));
+                }
+                lds_sync();
+                write_mask_row<NT>(o.mrow, bm, V);
+            } else {
+                for (uint32_t r = threadIdx.x; r < Lk; r += NT) o.mrow[cand_idx(s[r])] = 1;
+            }
+        }
+    }
+    if (P.out_count && threadIdx.x == 0) P.out_count[row] = (int32_t)L_;
+    if (P.out_token && threadIdx.x == 0) P.out_token[row] = token;
+    lds_sync();
     return true;
 }
 
@@ -1761,8 +2061,12 @@ __global__ __launch_bounds__(T::NT, T::WAVES_PER_SIMD) void tail_kernel(Params P
         }
         done = true;
     } else {
-        const bool in_lds = !overflow && nlist <= (uint32_t)P.tail_cap;
-        if (in_lds) {
+        const bool small = !overflow && nlist <= (uint32_t)P.small_max;
+        const bool in_lds = !small && !overflow && nlist <= (uint32_t)P.tail_cap;
+        if (small) {
+            const SrcList<NT> lsrc = list_source<NT>(P, row, S, (uint32_t)P.sub_cap, sh.cnt, nlist);
+            done = finish_small<T>(P, row, md, lsrc, nlist, kmax, rest, tc, t, sh, rb, dg);
+        } else if (in_lds) {
             // every candidate has z >= tc, so its key exceeds key(tc) - 1
             const int64_t key_lo = (int64_t)f32_key(__float_as_uint(tc)) - 1;
             uint32_t* a = (uint32_t*)(dyn_lds() + T::A_OFF);
@@ -1800,8 +2104,8 @@ __global__ __launch_bounds__(T::NT, T::WAVES_PER_SIMD) void tail_kernel(Params P
             done = finish_row<T>(P, row, md, src, lsrc, nlist, key_lo, kmax, rest, tc, t, sh, rb, dg);
         }
         if (!done) {
-            const TailOut o = tail_fallback<T>(P, row, md, t, tc, nlist, kmax, rest, overflow, in_lds, lambda, ns_h,
-                                               dg.n_t, sh, rb);
+            const TailOut o = tail_fallback<T>(P, row, md, t, tc, nlist, kmax, rest, overflow, in_lds || small,
+                                               lambda, ns_h, dg.n_t, sh, rb);
             done = o.done != 0;
             path = o.path;
             dg.n_t = o.n_t;
