@@ -61,8 +61,8 @@ bool dtype_ok(int d) { return d == QRITA_F32 || d == QRITA_BF16 || d == QRITA_F1
 // top-k range):
 //  - pass 1: 256-thread workgroups, at least 1024 of them (all resident
 //    together on 256 CUs); from 512 rows on, long rows get up to eight slices
-//    of about 64 KiB so several rounds of workgroups balance the CUs; slices of
-//    at least 8192 logits;
+//    of about 64 KiB (256 KiB from 2048 rows on) so several rounds of
+//    workgroups balance the CUs; slices of at least 8192 logits;
 //  - tail: the light tier (two rows per CU) for batches of 256 rows or more
 //    whose index output is at most 4096 ranks, else the heavy tier (one row
 //    per CU, twice the LDS capacities, kept sets up to 8192 sorted at once);
@@ -74,7 +74,11 @@ bool dtype_ok(int d) { return d == QRITA_F32 || d == QRITA_BF16 || d == QRITA_F1
 Plan choose_plan(int64_t B, int64_t V, int64_t esize, int64_t idx_cap, const qrita_options* o) {
     Plan t;
     int64_t S = std::max<int64_t>(1, (1024 + B - 1) / B);
-    if (B >= 512) S = std::max<int64_t>(S, std::min<int64_t>(8, (V * esize + 65535) / 65536));
+    // many rows: slices of about 64 KiB (512-2047 rows) or 256 KiB (2048
+    // rows and more; there every CU already holds several rows' slices, and
+    // each slice's threshold set-up is better spread over more logits)
+    const int64_t slice_bytes = B >= 2048 ? 262144 : 65536;
+    if (B >= 512) S = std::max<int64_t>(S, std::min<int64_t>(8, (V * esize + slice_bytes - 1) / slice_bytes));
     S = std::min<int64_t>(S, qrita::kMaxSlices);
     S = std::min<int64_t>(S, std::max<int64_t>(1, (V + 8191) / 8192));
     if (o && o->slices > 0) S = std::min<int64_t>(std::min<int64_t>(o->slices, qrita::kMaxSlices), std::max<int64_t>(1, V));
