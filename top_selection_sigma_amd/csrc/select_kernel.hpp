@@ -49,12 +49,11 @@ constexpr int kTailPre = 8;      // tail: list rows per thread read before the r
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kHistBins = 256;  // pass 1: sample histogram for the miss prediction
+constexpr int kHistBins = 1024;  // pass 1: sample histogram for the miss prediction (in the LDS stage)
 
 struct Shared {
     alignas(16) uint32_t slot[2][kMaxWaves][16];  // per-wave partial records, double-buffered
     alignas(16) uint32_t ties[kTieDirect + 4];
-    uint32_t hist[kHistBins];
     float fred[2 * kMaxWaves];
     uint32_t ncand;
     uint32_t flags;
@@ -232,7 +231,10 @@ QRITA_DEV Thresh compute_threshold(const Params& P, const RowMode& md, const voi
     if (!md.need_cand) return th;
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int32_t V = P.vocab;
-    for (int i = threadIdx.x; i < kHistBins; i += THREADS) sh.hist[i] = 0u;
+    // the candidate stage is free until the streaming pass: it holds the
+    // sample histogram meanwhile
+    uint32_t* hist = (uint32_t*)lds_cands();
+    for (int i = threadIdx.x; i < kHistBins; i += THREADS) hist[i] = 0u;
     // the table entries depend on K, p and V only: read them while the sample
     // is in flight
     const float cap = qrita_lut_k[lut_k_index(1.0f / (float)V)];
@@ -314,8 +316,8 @@ QRITA_DEV Thresh compute_threshold(const Params& P, const RowMode& md, const voi
     // table's factor-2 target about 2 * lambda values >= t. Fewer than
     // 1.25 * lambda + 2 suggests t lies above that logit (a truncation miss);
     // then collect down to about the r-th largest sample value instead
-    // (r = lambda + 5 sqrt(lambda) + 5), so the miss is served from the same
-    // single pass. That value is read off a 256-bin histogram of the sample
+    // (r = lambda + 4 sqrt(lambda) + 4), so the miss is served from the same
+    // single pass. That value is read off a 1024-bin histogram of the sample
     // over its range: the lower edge of the bin where the count from the top
     // reaches r, less half a bin, is at or below the r-th largest value.
     if (md.K_t > 0 && n >= 2 && __builtin_isfinite(t)) {
@@ -329,7 +331,7 @@ QRITA_DEV Thresh compute_threshold(const Params& P, const RowMode& md, const voi
             c += (ok && x[i] >= t) ? 1u : 0u;
             if (ok) {
                 const int b = (int)fminf(fmaxf((x[i] - lo) * inv, 0.0f), (float)(kHistBins - 1));
-                atomicAdd(&sh.hist[b], 1u);
+                atomicAdd(&hist[b], 1u);
             }
         }
         c = wave_sum_u32(c);
@@ -341,17 +343,26 @@ QRITA_DEV Thresh compute_threshold(const Params& P, const RowMode& md, const voi
         const float lam = (float)ns * (float)md.K_t / (float)V;
         th.lambda = lam;
         if (lam >= 4.0f && (float)ct < 1.25f * lam + 2.0f) {
-            const uint32_t r = min((uint32_t)ceilf(lam + 5.0f * sqrtf(lam) + 5.0f), ns);
+            const uint32_t r = min((uint32_t)ceilf(lam + 4.0f * sqrtf(lam) + 4.0f), ns);
             // every wave scans the histogram from the top: lane l holds bins
-            // 4l .. 4l+3, and the suffix counts come from a DPP scan
-            const uint32_t b0 = sh.hist[4 * lane], b1 = sh.hist[4 * lane + 1], b2 = sh.hist[4 * lane + 2],
-                           b3 = sh.hist[4 * lane + 3];
-            const uint32_t own = b0 + b1 + b2 + b3;
+            // 16l .. 16l+15, and the suffix counts come from a DPP scan
+            constexpr int BPL = kHistBins / kWave;
+            uint32_t bc[BPL];
+            uint32_t own = 0;
+#pragma unroll
+            for (int j = 0; j < BPL; ++j) {
+                bc[j] = hist[BPL * lane + j];
+                own += bc[j];
+            }
             const uint32_t above = wave_suffix_sum_excl(own);  // bins of higher lanes
             // highest bin whose count from the top reaches r
             int bin = -1;
-            const uint32_t c3 = above + b3, c2 = c3 + b2, c1 = c2 + b1, cz = c1 + b0;
-            bin = c3 >= r ? 4 * lane + 3 : (c2 >= r ? 4 * lane + 2 : (c1 >= r ? 4 * lane + 1 : (cz >= r ? 4 * lane : -1)));
+            uint32_t run = above;
+#pragma unroll
+            for (int j = BPL - 1; j >= 0; --j) {
+                run += bc[j];
+                bin = (bin < 0 && run >= r) ? BPL * lane + j : bin;
+            }
             const uint64_t has = __ballot(bin >= 0);
             // the reaching bin sits in the highest lane that has one
             const int src = has ? 63 - (int)__builtin_clzll(has) : 0;
