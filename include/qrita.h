@@ -150,8 +150,9 @@ int qrita_select(const void* logits, int64_t batch, int64_t vocab, int dtype,
  *                second stream of the library (one per device) while the
  *                streaming pass reads chunk c + 1; the caller's stream waits
  *                for the last tail before anything queued after the call.
- *   pivot_search_only  0 automatic: rows whose candidate set has at most 2048
- *                entries are sorted once and answered from the rank order;
+ *   pivot_search_only  0 automatic: rows whose candidate set has at most 4096
+ *                entries (2048 on the light tier) are sorted once and answered
+ *                from the rank order;
  *                1: every row takes the pivot searches (for the ablations).
  */
 typedef struct {

@@ -270,16 +270,19 @@ def test_chunked_tails_overlap_and_agree(chunks):
 @pytest.mark.parametrize("n_kind", ["gauss", "ties16", "smallint", "twolevel", "neginf", "zeros"])
 def test_small_sets_sorted_and_searched_agree(n_kind):
     """The sort-and-scan path and the pivot searches give identical outputs
-    (masks, indices, counts, diagnostics of the kept set) on rows whose
-    candidate sets straddle the 2048 limit."""
+    (masks, indices, counts) on rows whose candidate sets straddle the limits
+    of the sort-and-scan path (2048 candidates on the light tier, 4096 on the
+    heavy one)."""
     import top_selection_sigma_amd as q
 
-    x = w.make_rows(40, 60000, "f32", n_kind, seed=8)
-    x.k[:] = np.array([1, 5, 50, 500, 1500, 2047, 0, 0] * 5, np.int32)
-    x.p[:] = np.array([1.0, 0.9, 0.5, 1.0, 0.99, 1.0, 0.7, 0.999] * 5, np.float32)
-    ref = oracle_for(x, 2100)
-    a = run_gpu(x, 2100, options=q.Options(pivot_search_only=0))
-    b = run_gpu(x, 2100, options=q.Options(pivot_search_only=1))
-    check(x, a, ref, 2100, f"sorted {n_kind}")
-    check(x, b, ref, 2100, f"searched {n_kind}")
-    assert np.array_equal(a.count, b.count) and np.array_equal(a.mask, b.mask)
+    for B, tier in ((40, 2), (40, 1)):
+        x = w.make_rows(B, 60000, "f32", n_kind, seed=8 + tier)
+        x.k[:] = np.array([1, 5, 50, 500, 1500, 2047, 0, 0, 1000, 1900] * 4, np.int32)
+        x.p[:] = np.array([1.0, 0.9, 0.5, 1.0, 0.99, 1.0, 0.7, 0.999, 1.0, 1.0] * 4, np.float32)
+        ref = oracle_for(x, 2100)
+        a = run_gpu(x, 2100, options=q.Options(pivot_search_only=0, tier=tier))
+        b = run_gpu(x, 2100, options=q.Options(pivot_search_only=1, tier=tier))
+        check(x, a, ref, 2100, f"sorted {n_kind} tier {tier}")
+        check(x, b, ref, 2100, f"searched {n_kind} tier {tier}")
+        assert np.array_equal(a.count, b.count) and np.array_equal(a.mask, b.mask)
+        _say(f"{n_kind} tier {tier}: candidates {sorted(a.diag[:, 3].tolist())[::8]}")

@@ -18,7 +18,7 @@ using qrita::Params;
 
 constexpr int64_t kListMax = 32768;   // per-row candidate list (entries of 8 bytes)
 constexpr int kMaxChunks = 16;        // row chunks of one call
-constexpr int kSmallSet = 2048;       // candidate sets sorted and scanned instead of searched
+constexpr int kSmallSet = 4096;       // candidate sets sorted and scanned instead of searched
 constexpr int kPass1Threads = 256;
 constexpr int kSampleN = 2048;        // pass 1 sample (its LDS stage holds at least this many entries)
 constexpr int kStageCap = 2048;       // pass 1 LDS candidate stage
