@@ -955,7 +955,8 @@ struct SortExt {
 
 template <int NT, int NB>
 QRITA_DEV bool bucket_sort(const uint64_t* a, uint32_t cnt, const SortExt& ex, const RankOut& ro, uint64_t* bw,
-                           uint16_t* pos, uint16_t* binof, uint32_t* bins, uint32_t* hc, Shared& sh, int& rb) {
+                           uint16_t* pos, uint16_t* binof, uint32_t* bins, uint32_t* hc, Shared& sh, int& rb,
+                           bool* ordered) {
     const uint32_t t = threadIdx.x;
     const uint32_t kmn = ex.kmn, kmx = ex.kmx, lmn = ex.lmn, lmx = ex.lmx;
     const uint32_t nb = min((uint32_t)NB, 2u * next_pow2(cnt));
@@ -1050,6 +1051,9 @@ QRITA_DEV bool bucket_sort(const uint64_t* a, uint32_t cnt, const SortExt& ex, c
         lds_sync();
         return true;
     }
+    // below, ranking reads the words in place: no sorted copy over them
+    const bool keep_sorted = ro.sorted != a;
+    if (!keep_sorted) *ordered = false;
     {
         // runs of bins in proportion to the codes' sizes
         for (uint32_t i = t; i <= ncodes; i += NT) hc[i] = 0u;
@@ -1142,7 +1146,12 @@ QRITA_DEV bool bucket_sort(const uint64_t* a, uint32_t cnt, const SortExt& ex, c
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u)
-            if (p0 + (uint32_t)u * NT < cnt) ro.put(r[u], w[u]);
+            if (p0 + (uint32_t)u * NT < cnt) {
+                if (keep_sorted)
+                    ro.put(r[u], w[u]);
+                else
+                    RankOut{ro.out, ro.lout, ro.mrow, ro.lmask, ro.last, ro.prob, ro.mref, ro.inv_s, nullptr}.put(r[u], w[u]);
+            }
     }
     lds_sync();
     return true;
@@ -1151,9 +1160,11 @@ QRITA_DEV bool bucket_sort(const uint64_t* a, uint32_t cnt, const SortExt& ex, c
 // Rank order of the cnt <= CSORT words at the start of the sort region: a
 // handful by ranking, more by the bucket sort, sets it cannot split by the
 // bitonic sort. The words stay in the first region (the bitonic sort permutes
-// them).
+// them). Returns whether ro.sorted received the words in rank order (not when
+// it is the sort region itself and the bucket sort sized its bins in
+// proportion to the codes, which ranks the words in place).
 template <class T>
-QRITA_DEV void sort_words(uint32_t cnt, const SortExt& ex, RankOut ro, Shared& sh, int& rb) {
+QRITA_DEV bool sort_words(uint32_t cnt, const SortExt& ex, RankOut ro, Shared& sh, int& rb) {
     constexpr int NT = T::NT;
     uint64_t* a = (uint64_t*)(dyn_lds() + T::SA_OFF);
     uint16_t* pos = (uint16_t*)(dyn_lds() + T::SB_OFF);
@@ -1161,17 +1172,19 @@ QRITA_DEV void sort_words(uint32_t cnt, const SortExt& ex, RankOut ro, Shared& s
     uint32_t* bins = (uint32_t*)(dyn_lds() + T::BINS_OFF);
     uint32_t* hc = (uint32_t*)(dyn_lds() + T::HC_OFF);
     cnt = min(uni(cnt), (uint32_t)T::CSORT);  // more only for inputs outside the contract (NaN logits)
-    if (cnt == 0) return;
+    if (cnt == 0) return true;
     if (cnt <= (uint32_t)NT) {
         rank_sort<NT>(a, cnt, ro, bins);
-        return;
+        return true;
     }
     uint64_t* bw = (uint64_t*)(dyn_lds() + T::SB_OFF);
-    if (bucket_sort<NT, T::NB>(a, cnt, ex, ro, bw, pos, binof, bins, hc, sh, rb)) return;
+    bool ordered = true;
+    if (bucket_sort<NT, T::NB>(a, cnt, ex, ro, bw, pos, binof, bins, hc, sh, rb, &ordered)) return ordered;
     const uint32_t np = next_pow2(cnt);  // < 2 cnt: inside the fallback region
     for (uint32_t i = cnt + threadIdx.x; i < np; i += NT) a[i] = 0ull;
     lds_sync();
     bitonic_lds<NT>(a, np, cnt, ro);
+    return true;
 }
 
 // ---------------------------------------------------------------------------
@@ -1483,15 +1496,18 @@ QRITA_DEV void bitmap_outputs(const uint32_t* bm, const RowOut& o, uint32_t Lout
 // ranks go to the index output. When every candidate at or above the value
 // that bounds the index output fits one sort, the sort's rank order resolves
 // the duplicates and writes the outputs; otherwise the duplicates are
-// resolved by tie_boundary and the indices sorted in windows.
+// resolved by tie_boundary and the indices sorted in windows. With
+// keep_sorted, returns whether the one sort also left the kept set's words in
+// rank order at the start of the sort region.
 template <class T, class C, class L>
-QRITA_DEV void emit_row(C& c, const L& lsrc, const RowOut& o, bool all, uint32_t vf, uint32_t ngt, uint32_t needf,
-                        uint32_t Nf, uint32_t L_, int64_t key_lo, uint32_t n, uint32_t kmax, TailDiag& dg) {
+QRITA_DEV bool emit_row(C& c, const L& lsrc, const RowOut& o, bool all, uint32_t vf, uint32_t ngt, uint32_t needf,
+                        uint32_t Nf, uint32_t L_, int64_t key_lo, uint32_t n, uint32_t kmax, TailDiag& dg,
+                        bool keep_sorted = false) {
     constexpr int NT = T::NT;
     Shared& sh = *c.sh;
     const uint32_t Lout = o.idx ? (L_ < o.idx_cap ? L_ : o.idx_cap) : 0u;
     const bool mask = o.mrow != nullptr && !all;
-    if (!mask && Lout == 0) return;
+    if (!mask && Lout == 0) return false;
     // the boundary of the index output's last rank
     uint32_t vo = vf, ngo = ngt, needo = needf, No = Nf;
     if (Lout > 0 && (all || Lout < L_)) {
@@ -1512,26 +1528,27 @@ QRITA_DEV void emit_row(C& c, const L& lsrc, const RowOut& o, bool all, uint32_t
         const uint32_t cnt =
             gather_words<NT>(lsrc, a, T::CSORT, (uint64_t)(Lout > 0 ? vo : vf) << 32, ~0ull, ex, sh, c.rb);
         RankOut ro{o.idx, Lout, (mask && !o.bitmap) ? o.mrow : nullptr, mask ? L_ : 0u,
-                   (mask && o.bitmap) ? (uint64_t*)&sh.u32[0] : nullptr, o.prob, o.mref, o.inv_s};
-        sort_words<T>(cnt, ex, ro, sh, c.rb);
+                   (mask && o.bitmap) ? (uint64_t*)&sh.u32[0] : nullptr, o.prob, o.mref, o.inv_s,
+                   keep_sorted ? a : nullptr};
+        const bool ord = sort_words<T>(cnt, ex, ro, sh, c.rb);
         if (mask && o.bitmap) {
             lds_sync();
             const uint64_t B = uni(*(const uint64_t*)&sh.u32[0]);
             mask_from_sorted<T>(min(cnt, (uint32_t)T::CSORT), B, o);
         }
-        return;
+        return keep_sorted && ord;  // then the kept set is a[0 .. L) in rank order
     }
     // the kept set's boundary word, for the mask
     if (mask) {
         const uint64_t B = tie_boundary<T>(lsrc, vf, needf, Nf, o.V, c.mode, sh, c.rb, dg.iters);
         mask_from_boundary<T>(lsrc, B, o);
     }
-    if (Lout == 0) return;
+    if (Lout == 0) return false;
     if (Gi <= (uint32_t)T::CSORT) {
         SortExt ex;
         const uint32_t cnt = gather_words<NT>(lsrc, a, T::CSORT, (uint64_t)vo << 32, ~0ull, ex, sh, c.rb);
         sort_words<T>(cnt, ex, RankOut{o.idx, Lout, nullptr, 0u, nullptr, o.prob, o.mref, o.inv_s}, sh, c.rb);
-        return;
+        return false;
     }
     // windows of CSORT ranks, each bounded by its own boundary word. The
     // gathers and sorts reuse the LDS that may hold the search source's
@@ -1559,6 +1576,153 @@ QRITA_DEV void emit_row(C& c, const L& lsrc, const RowOut& o, bool all, uint32_t
         prev = Bn;
         done += cnt;
     }
+    return false;
+}
+
+// Exclusive prefix over the block of per-thread 64-bit values v (thread
+// order); total is the block's sum (uniform).
+template <int NT>
+QRITA_DEV uint64_t block_scan_u64(uint64_t v, uint64_t& total, Shared& sh, int& rb) {
+    constexpr int NW = NT / kWave;
+    const uint32_t lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    uint64_t x = v;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const uint32_t lo = (uint32_t)__shfl_up((int)(uint32_t)x, o, kWave);
+        const uint32_t hi = (uint32_t)__shfl_up((int)(uint32_t)(x >> 32), o, kWave);
+        if (lane >= (uint32_t)o) x += ((uint64_t)hi << 32) | lo;
+    }
+    const uint64_t wtot = ((uint64_t)readlane((uint32_t)(x >> 32), kWave - 1) << 32) | readlane((uint32_t)x, kWave - 1);
+    if (lane == 0) *(uint2*)&sh.slot[rb][wave][0] = make_uint2((uint32_t)wtot, (uint32_t)(wtot >> 32));
+    lds_sync();
+    uint64_t before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        const uint2 q = *(const uint2*)&sh.slot[rb][w][0];
+        const uint64_t t = ((uint64_t)q.y << 32) | q.x;
+        before += (uint32_t)w < wave ? t : 0ull;
+        all += t;
+    }
+    rb ^= 1;
+    total = uni(all);
+    return before + x - v;
+}
+
+// Smallest rank r < R whose running mass P_r (rank-order prefix of
+// mass_fx over s[0 .. R), starting from the thread's exclusive prefix) is at
+// least T, or R. Each thread walks its own run of ranks [r0, r1).
+template <int NT>
+QRITA_DEV uint32_t first_reaching(const uint64_t* s, uint32_t r0, uint32_t r1, uint64_t before, uint64_t T,
+                                  float m, uint32_t R, Shared& sh, int& rb) {
+    uint32_t hit = 0xFFFFFFFFu;
+    uint64_t run = before;
+    for (uint32_t r = r0; r < r1; ++r) {
+        run += mass_fx(cand_key(s[r]), m);
+        if (run >= T) {
+            hit = r;
+            break;
+        }
+    }
+    uint32_t mn[1] = {wave_min_u32(hit)};
+    comb_record<NT, 0, 0, 1>(nullptr, nullptr, mn, sh, rb);
+    return mn[0] < R ? mn[0] : R;
+}
+
+// Logit of vocabulary entry i of a row, as a key.
+QRITA_DEV uint32_t key_at(const void* rowp, int dtype, uint32_t i) {
+    uint32_t x;
+    if (dtype == 0) {
+        x = ((const uint32_t*)rowp)[i];
+    } else {
+        const uint32_t h = ((const uint16_t*)rowp)[i];
+        x = __float_as_uint(dtype == 1 ? lo16<1>(h) : lo16<2>(h));
+    }
+    return f32_key(x);
+}
+
+// The draw (and the probabilities) for a row whose kept set of L ranks the
+// index output already holds in rank order (idx[0 .. L)): the masses of the
+// kept logits in rank order go to LDS (free once the outputs are written;
+// coalesced index reads, eight gathers in flight per thread), then their
+// block prefix gives the first rank whose running mass reaches u * S. The
+// same integers as the mass search over the kept set. Returns the drawn index.
+template <int NT>
+QRITA_DEV int32_t draw_from_ranks(const int32_t* idx, float* prob, uint32_t L, uint32_t lprob, const void* rowp,
+                                  int dtype, float m, double u, Shared& sh, int& rb) {
+    // the index output is this workgroup's own global stores: a full
+    // workgroup barrier (release and acquire at workgroup scope) orders them
+    __syncthreads();
+    uint64_t* em = (uint64_t*)dyn_lds();
+    constexpr int U = 8;
+    for (uint32_t r0 = threadIdx.x; r0 < L; r0 += U * NT) {
+        uint32_t ix[U], key[U];
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            const uint32_t r = r0 + (uint32_t)j * NT;
+            ix[j] = (uint32_t)idx[r < L ? r : r0];
+        }
+#pragma unroll
+        for (int j = 0; j < U; ++j) key[j] = key_at(rowp, dtype, ix[j]);
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            const uint32_t r = r0 + (uint32_t)j * NT;
+            if (r < L) em[r] = mass_fx(key[j], m);
+        }
+    }
+    lds_sync();
+    const uint32_t per = (L + NT - 1u) / NT;
+    const uint32_t r0 = threadIdx.x * per < L ? threadIdx.x * per : L;
+    const uint32_t r1 = r0 + per < L ? r0 + per : L;
+    uint64_t loc = 0;
+    for (uint32_t r = r0; r < r1; ++r) loc += em[r];
+    uint64_t total = 0;
+    const uint64_t before = block_scan_u64<NT>(loc, total, sh, rb);
+    uint64_t T = (uint64_t)ceil(u * (double)total);
+    T = T ? T : 1u;
+    uint32_t hit = 0xFFFFFFFFu;
+    uint64_t run = before;
+    for (uint32_t r = r0; r < r1; ++r) {
+        run += em[r];
+        if (run >= T) {
+            hit = r;
+            break;
+        }
+    }
+    uint32_t mn[1] = {wave_min_u32(hit)};
+    comb_record<NT, 0, 0, 1>(nullptr, nullptr, mn, sh, rb);
+    if (prob) {
+        const double inv = total ? 1.0 / (double)total : 0.0;
+        for (uint32_t r = threadIdx.x; r < lprob; r += NT) prob[r] = (float)((double)em[r] * inv);
+    }
+    const uint32_t rt = mn[0] < L ? mn[0] : L - 1u;
+    const int32_t tok = idx[rt];
+    lds_sync();
+    return tok;
+}
+
+// The draw (and the probabilities) from the kept set's words in rank order
+// in LDS (s[0 .. L)): the block prefix of their masses and the first rank
+// whose running mass reaches u * S, as in the sort-and-scan path.
+template <int NT>
+QRITA_DEV int32_t draw_from_sorted(const uint64_t* s, float* prob, uint32_t L, float m, double u, Shared& sh,
+                                   int& rb) {
+    const uint32_t per = (L + NT - 1u) / NT;
+    const uint32_t r0 = threadIdx.x * per < L ? threadIdx.x * per : L;
+    const uint32_t r1 = r0 + per < L ? r0 + per : L;
+    uint64_t loc = 0;
+    for (uint32_t r = r0; r < r1; ++r) loc += mass_fx(cand_key(s[r]), m);
+    uint64_t total = 0;
+    const uint64_t before = block_scan_u64<NT>(loc, total, sh, rb);
+    uint64_t T = (uint64_t)ceil(u * (double)total);
+    T = T ? T : 1u;
+    const uint32_t rt = first_reaching<NT>(s, r0, r1, before, T, m, L, sh, rb);
+    if (prob) {
+        const double inv = total ? 1.0 / (double)total : 0.0;
+        for (uint32_t r = threadIdx.x; r < L; r += NT) prob[r] = (float)((double)mass_fx(cand_key(s[r]), m) * inv);
+    }
+    const int32_t tok = (int32_t)cand_idx(s[rt < L ? rt : L - 1u]);
+    lds_sync();
+    return tok;
 }
 
 // Steps a4-a7 on one candidate source holding n candidates, all with keys in
@@ -1654,7 +1818,13 @@ QRITA_DEV bool finish_row(const Params& P, int64_t row, const RowMode& md, const
     // its value and its position j among that value's duplicates
     double s_kept = 0.0;
     int32_t token = -1;
-    if (P.out_token) {
+    // the kept set sorted in one piece for the index output: the draw reads
+    // its words in rank order after the outputs are written (one pass instead
+    // of a mass search over the candidates); if the sort ranked them in place,
+    // from the index output
+    const bool draw_after = P.out_token && m != -__builtin_inff() && !all && !P.idx_order && P.out_idx &&
+                            Lk <= (uint32_t)P.idx_cap && ngt + Nf <= (uint32_t)T::CSORT;
+    if (P.out_token && !draw_after) {
         if (m == -__builtin_inff()) {
             // no finite logit: rank 0, the lowest index of the maximum
             const CountOut r0 = search_count<NT, 0>(c, 0u, 1u, key_lo, n, (int64_t)kmax, 0u);
@@ -1690,68 +1860,27 @@ QRITA_DEV bool finish_row(const Params& P, int64_t row, const RowMode& md, const
     }
     const void* rowp = P.dtype != 0 ? (const void*)((const uint16_t*)P.logits + row * (int64_t)V)
                                     : (const void*)((const float*)P.logits + row * (int64_t)V);
+    float* prow = (P.out_prob && P.idx_cap > 0) ? P.out_prob + row * (int64_t)P.idx_cap : nullptr;
     RowOut o{(P.out_idx && P.idx_cap > 0) ? P.out_idx + row * (int64_t)P.idx_cap : nullptr, (uint32_t)P.idx_cap,
              (P.mask && !md.keep_all) ? P.mask + row * (int64_t)V : nullptr, P.bitmap != 0, V,
-             (P.out_prob && P.idx_cap > 0) ? P.out_prob + row * (int64_t)P.idx_cap : nullptr, m,
-             s_kept > 0.0 ? 1.0 / s_kept : 0.0, rowp, (int)P.dtype};
+             draw_after ? nullptr : prow, m, s_kept > 0.0 ? 1.0 / s_kept : 0.0, rowp, (int)P.dtype};
+    bool sorted_kept = false;
     if (P.idx_order)
         emit_row_by_index<T>(c, lsrc, o, all, vf, needf, Nf, Lk, dg);
     else
-        emit_row<T>(c, lsrc, o, all, vf, ngt, needf, Nf, Lk, key_lo, n, kmax, dg);
+        sorted_kept = emit_row<T>(c, lsrc, o, all, vf, ngt, needf, Nf, Lk, key_lo, n, kmax, dg, draw_after);
+    if (draw_after) {
+        const double u = row_uniform(P.seed, P.offset, (uint64_t)(P.row0 + row));
+        // (Lk <= CSORT: its masses fit the dynamic LDS for draw_from_ranks)
+        token = sorted_kept
+                    ? draw_from_sorted<NT>((const uint64_t*)(dyn_lds() + T::SA_OFF), prow, Lk, m, u, sh, c.rb)
+                    : draw_from_ranks<NT>(o.idx, prow, Lk, Lk, rowp, (int)P.dtype, m, u, sh, c.rb);
+    }
     if (P.out_count && threadIdx.x == 0) P.out_count[row] = (int32_t)Lk;
     if (P.out_token && threadIdx.x == 0) P.out_token[row] = token;
     rb = c.rb;
     dg.iters += c.iters;
     return true;
-}
-
-// Exclusive prefix over the block of per-thread 64-bit values v (thread
-// order); total is the block's sum (uniform).
-template <int NT>
-QRITA_DEV uint64_t block_scan_u64(uint64_t v, uint64_t& total, Shared& sh, int& rb) {
-    constexpr int NW = NT / kWave;
-    const uint32_t lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-    uint64_t x = v;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const uint32_t lo = (uint32_t)__shfl_up((int)(uint32_t)x, o, kWave);
-        const uint32_t hi = (uint32_t)__shfl_up((int)(uint32_t)(x >> 32), o, kWave);
-        if (lane >= (uint32_t)o) x += ((uint64_t)hi << 32) | lo;
-    }
-    const uint64_t wtot = ((uint64_t)readlane((uint32_t)(x >> 32), kWave - 1) << 32) | readlane((uint32_t)x, kWave - 1);
-    if (lane == 0) *(uint2*)&sh.slot[rb][wave][0] = make_uint2((uint32_t)wtot, (uint32_t)(wtot >> 32));
-    lds_sync();
-    uint64_t before = 0, all = 0;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-        const uint2 q = *(const uint2*)&sh.slot[rb][w][0];
-        const uint64_t t = ((uint64_t)q.y << 32) | q.x;
-        before += (uint32_t)w < wave ? t : 0ull;
-        all += t;
-    }
-    rb ^= 1;
-    total = uni(all);
-    return before + x - v;
-}
-
-// Smallest rank r < R whose running mass P_r (rank-order prefix of
-// mass_fx over s[0 .. R), starting from the thread's exclusive prefix) is at
-// least T, or R. Each thread walks its own run of ranks [r0, r1).
-template <int NT>
-QRITA_DEV uint32_t first_reaching(const uint64_t* s, uint32_t r0, uint32_t r1, uint64_t before, uint64_t T,
-                                  float m, uint32_t R, Shared& sh, int& rb) {
-    uint32_t hit = 0xFFFFFFFFu;
-    uint64_t run = before;
-    for (uint32_t r = r0; r < r1; ++r) {
-        run += mass_fx(cand_key(s[r]), m);
-        if (run >= T) {
-            hit = r;
-            break;
-        }
-    }
-    uint32_t mn[1] = {wave_min_u32(hit)};
-    comb_record<NT, 0, 0, 1>(nullptr, nullptr, mn, sh, rb);
-    return mn[0] < R ? mn[0] : R;
 }
 
 // Steps a4-a7 for a row with few candidates (n <= CSORT / 2, all in the list
