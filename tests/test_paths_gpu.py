@@ -286,3 +286,21 @@ def test_small_sets_sorted_and_searched_agree(n_kind):
         check(x, b, ref, 2100, f"searched {n_kind} tier {tier}")
         assert np.array_equal(a.count, b.count) and np.array_equal(a.mask, b.mask)
         _say(f"{n_kind} tier {tier}: candidates {sorted(a.diag[:, 3].tolist())[::8]}")
+
+
+@pytest.mark.parametrize("tier,B", [(1, 700), (1, 1024), (2, 300), (2, 512)])
+def test_counted_rows_cover_every_row_once(tier, B):
+    """Batches of one to two rounds of resident tail workgroups take their rows
+    from a counter that pass 1 zeroes: every row is handled exactly once, on a
+    mix of cheap and expensive rows (k cycling over 1, 20, 1000, 3000 and top-p
+    rows), in two calls in a row."""
+    import top_selection_sigma_amd as q
+
+    ks = np.array([1, 20, 1000, 3000, 0], dtype=np.int32)[np.arange(B) % 5]
+    ps = np.where(np.arange(B) % 5 == 4, 0.9, 1.0)
+    x = w.make_rows(B, 6007, "bf16", "gauss_outliers", seed=B + 31 * tier, k=ks, p=ps)
+    ref = oracle_for(x, 3000)
+    for call in range(2):
+        _say(f"counted rows tier {tier} B {B} call {call}")
+        g = run_gpu(x, 3000, options=q.Options(tier=tier))
+        check(x, g, ref, 3000, f"counted rows tier {tier} B {B} call {call}")

@@ -37,13 +37,15 @@ struct Params {
     float* out_prob;     // sampling: [batch][idx_cap] probabilities beside out_idx, or null
     uint64_t seed;       // sampling: Philox key
     uint64_t offset;     // sampling: Philox counter word 1
-    int64_t row0;
-    int32_t small_max;   // rows with at most this many candidates take the sort-and-scan path (0: none)        // batch row of this launch's row 0 (the draw's counter uses batch rows)
+    int64_t row0;        // batch row of this launch's row 0 (the draw's counter uses batch rows)
+    int32_t small_max;   // rows with at most this many candidates take the sort-and-scan path (0: none)
+    uint32_t* queue;     // tail row counter (null: workgroup g takes row g)
 };
 
 // Records that pass 1 leaves for the tail. Every word is written by plain
-// stores in the call that reads it, so the workspace carries no state from one
-// call to the next (no word is expected to start at zero).
+// stores in the call that reads it (the tail's row counter is zeroed by pass
+// 1 and then counted up by the tail), so the workspace carries no state from
+// one call to the next (no word is expected to start at zero).
 enum : int {
     R_T = 0,       // row record: Gaussian threshold (float bits)
     R_TC = 1,      // collection threshold (float bits)

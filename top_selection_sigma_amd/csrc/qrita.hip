@@ -27,16 +27,17 @@ constexpr int kWaveSpill = 512;       // pass 1 per-wave spill buffer entries
 int64_t list_stride_for(int64_t vocab) { return std::min<int64_t>(vocab, kListMax); }
 int64_t round256(int64_t x) { return (x + 255) / 256 * 256; }
 
-// Workspace layout: row records, slice records, row lists. Nothing in it is
-// expected to hold any value when a call starts.
+// Workspace layout: row records, slice records, the tail's row counter, row
+// lists. Nothing in it is expected to hold any value when a call starts.
 struct WsLayout {
-    int64_t rowrec, slrec, lists, total;
+    int64_t rowrec, slrec, queue, lists, total;
 };
 WsLayout ws_layout(int64_t B, int64_t V) {
     WsLayout w;
     w.rowrec = 0;
     w.slrec = round256(B * qrita::R_WORDS * 4);
-    w.lists = w.slrec + round256(B * qrita::kMaxSlices * qrita::S_WORDS * 4);
+    w.queue = w.slrec + round256(B * qrita::kMaxSlices * qrita::S_WORDS * 4);
+    w.lists = w.queue + (B > 0 ? 256 : 0);
     w.total = w.lists + B * list_stride_for(V) * 8;
     return w;
 }
@@ -121,6 +122,7 @@ Plan choose_plan(int64_t B, int64_t V, int64_t esize, int64_t idx_cap, const qri
 // gfx950 check, once per device (kernels built for gfx950 cannot run elsewhere).
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_arch[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+std::atomic<int> g_cus[kMaxDevices];   // compute units (valid once g_arch is)
 
 bool device_supported() {
     int dev = 0;
@@ -131,6 +133,7 @@ bool device_supported() {
         hipDeviceProp_t prop;
         if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return false;
         s = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        g_cus[dev].store(prop.multiProcessorCount, std::memory_order_relaxed);
         g_arch[dev].store(s, std::memory_order_relaxed);
     }
     return s == 1;
@@ -240,6 +243,7 @@ int select_impl(const void* logits, int64_t batch, int64_t vocab, int dtype, con
     P.rowrec = (uint32_t*)((char*)workspace + w.rowrec);
     P.slrec = (uint32_t*)((char*)workspace + w.slrec);
     P.glist = (uint64_t*)((char*)workspace + w.lists);
+    P.queue = nullptr;
     P.diag = opt ? opt->diag : nullptr;
     P.batch = batch;
     P.vocab = (int32_t)vocab;
@@ -285,6 +289,18 @@ int select_impl(const void* logits, int64_t batch, int64_t vocab, int dtype, con
         sd = side_for(dev);  // no second stream: one chunk
     }
     if (!sd) {
+        // rows for more than one and at most two rounds of the tail
+        // workgroups resident at once: each tail workgroup takes the next row
+        // from a counter when it starts. (With more rounds, the counter's
+        // round trip at every start costs more than the balance gains.)
+        {
+            int dev = 0;
+            if (hipGetDevice(&dev) != hipSuccess) return QRITA_ELAUNCH;
+            const qrita::TierInfo ti = t.heavy ? qrita::tier_heavy() : qrita::tier_light();
+            const int64_t per_cu = std::max<int64_t>(1, (int64_t)(160 * 1024) / (int64_t)(ti.lds + 4096));
+            const int64_t resident = per_cu * std::max(1, g_cus[dev].load(std::memory_order_relaxed));
+            if (batch > resident && batch <= 2 * resident) P.queue = (uint32_t*)((char*)workspace + w.queue);
+        }
         if (pass1(P, s) != hipSuccess) return QRITA_ELAUNCH;
         if (opt && opt->mid_event) {
             if (hipEventRecord((hipEvent_t)opt->mid_event, s) != hipSuccess) return QRITA_ELAUNCH;

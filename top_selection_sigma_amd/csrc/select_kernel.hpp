@@ -63,6 +63,7 @@ struct Shared {
     uint32_t nsub;               // pass 1: entries reserved in the slice's sub-list
     uint32_t cnt[kMaxSlices];    // tail: candidates per slice
     uint32_t pre[kMaxSlices + 1];  // tail: prefix of cnt
+    uint32_t row;                  // tail: the row taken from the counter
 };
 
 extern __shared__ uint64_t qrita_dyn_lds[];
@@ -670,13 +671,15 @@ QRITA_DEV void stream_slice(const Params& P, int64_t row, uint64_t* sub, int64_t
 // Pass 1: one workgroup per (row, slice). Workgroup g runs on XCD g mod 8;
 // rows are dealt so that all slices of row r share XCD r mod 8 and therefore
 // one L2, which also holds the row list when the row's tail (workgroup r of
-// the next launch, on the same XCD) reads it. A slice writes only its own
-// sub-list and record: no global atomics, no state carried between calls.
+// the next launch, on the same XCD, unless rows are counted out) reads it. A
+// slice writes only its own sub-list and record: no global atomics, no state
+// carried between calls. Workgroup 0 also zeroes the tail's row counter.
 template <int THREADS, int DT>
 __global__ __launch_bounds__(THREADS, 4) void pass1_kernel(Params P) {
     __shared__ Shared sh;
     int rb = 0;
     const uint32_t g = blockIdx.x;
+    if (P.queue && g == 0 && threadIdx.x == 0) *P.queue = 0u;
     const uint32_t xcd = g & 7u, jj = g >> 3;
     const uint32_t rloc = jj / (uint32_t)P.slices, slice = jj % (uint32_t)P.slices;
     const int64_t row = (int64_t)rloc * 8 + xcd;

@@ -2140,14 +2140,27 @@ QRITA_DEV TailOut tail_fallback(const Params& P, int64_t row, RowMode md, float 
     return TailOut{done ? 1 : 0, path, dg.n_t, dg.iters, rb};
 }
 
-// Tail: one workgroup per row. The row's sub-lists are loaded into LDS when
-// they fit and did not overflow; everything else takes tail_fallback.
+// Tail: one workgroup per row. When the rows take about two rounds of the
+// workgroups resident at once, a workgroup takes its row from a counter
+// (zeroed by pass 1) when it starts, rather than row = workgroup index. Rows
+// are then handed out in the order the workgroups start, wherever they run,
+// instead of by the fixed placement of workgroup indices on XCDs and CUs,
+// which can put the expensive rows of a periodic pattern (a per-row k that
+// cycles) on the same XCDs; the rows of the second round then also go to
+// whichever workgroups start first. The grid has one workgroup per row, so
+// each takes one ticket below the row count. The row's sub-lists are loaded into LDS when they fit
+// and did not overflow; everything else takes tail_fallback.
 template <class T>
 __global__ __launch_bounds__(T::NT, T::WAVES_PER_SIMD) void tail_kernel(Params P) {
     constexpr int NT = T::NT;
     __shared__ Shared sh;
     int rb = 0;
-    const int64_t row = blockIdx.x;
+    int64_t row = blockIdx.x;
+    if (P.queue) {
+        if (threadIdx.x == 0) sh.row = atomicAdd(P.queue, 1u);
+        __syncthreads();
+        row = uni(sh.row);
+    }
     if (row >= P.batch) return;
     const int32_t V = P.vocab;
     const uint32_t S = (uint32_t)P.slices;
