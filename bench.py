@@ -393,6 +393,10 @@ def leg(r, ref, steps, warmup, opts):
 def ablations(index, r, ref, steps, warmup, base):
     """The ablation legs on this workload (each parity-checked against the oracle)."""
     a = {"default_us": round(base["ms_per_step"] * 1e3, 2)}
+    if index in (0, 1, 2):
+        # one launch: each row's tail workgroup streams its row itself,
+        # instead of the streaming pass's (row, slice) workgroups
+        a["one_launch"] = leg(r, ref, steps, warmup, dict(launches=1))
     if index in (0, 1, 2, 4):
         # truncation off: no survivors in pass 1, every row searches its full row
         a["truncation_off"] = leg(r, ref, steps, warmup, dict(force_miss=True))

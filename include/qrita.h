@@ -131,7 +131,8 @@ int qrita_select(const void* logits, int64_t batch, int64_t vocab, int dtype,
  *   diag         device int32 [batch][QRITA_DIAG_FIELDS] or NULL: per-row
  *                diagnostics, see QRITA_DIAG_* below.
  *   mid_event    a hipEvent_t or NULL: recorded on the stream between the
- *                streaming pass and the per-row tail, for per-stage timing.
+ *                streaming pass and the per-row tail, for per-stage timing
+ *                (with one launch: before it).
  *   tier         tail tier: 0 automatic, 1 light (two rows per CU),
  *                2 heavy (one row per CU, larger capacities).
  *   mask_mode    0 automatic; 1: pass 1 zero-fills the mask and the tail
@@ -154,6 +155,13 @@ int qrita_select(const void* logits, int64_t batch, int64_t vocab, int dtype,
  *                entries (2048 on the light tier) are sorted once and answered
  *                from the rank order;
  *                1: every row takes the pivot searches (for the ablations).
+ *   launches     0 automatic (two launches: the streaming pass over
+ *                (row, slice) workgroups, then the per-row tail);
+ *                1: one launch, in which each row's tail workgroup first
+ *                streams its whole row itself (slower at every measured
+ *                shape: one workgroup's ALUs bound the pass over a row; for
+ *                the ablation); 2: two launches. The outputs are the same
+ *                either way.
  */
 typedef struct {
     int32_t force_miss;
@@ -169,6 +177,7 @@ typedef struct {
     int32_t idx_order;
     int32_t chunks;
     int32_t pivot_search_only;
+    int32_t launches;
 } qrita_options;
 
 #define QRITA_DIAG_FIELDS 8

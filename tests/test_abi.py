@@ -100,7 +100,9 @@ def test_options_are_validated():
            q._Options(0, 0.0, 0, 0, 0, 0, None, None, 0, 0, -1),
            q._Options(0, 0.0, 0, 0, 0, 0, None, None, 0, 0, 0, 17),
            q._Options(0, 0.0, 0, 0, 0, 0, None, None, 0, 0, 0, -1),
-           q._Options(0, 0.0, 0, 0, 0, 0, None, None, 0, 0, 0, 0, 2)]
+           q._Options(0, 0.0, 0, 0, 0, 0, None, None, 0, 0, 0, 0, 2),
+           q._Options(0, 0.0, 0, 0, 0, 0, None, None, 0, 0, 0, 0, 0, 3),
+           q._Options(0, 0.0, 0, 0, 0, 0, None, None, 0, 0, 0, 0, 0, -1)]
     for o in bad:
         assert _call(opt=o) == q.QRITA_EINVAL
 

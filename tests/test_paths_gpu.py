@@ -304,3 +304,44 @@ def test_counted_rows_cover_every_row_once(tier, B):
         _say(f"counted rows tier {tier} B {B} call {call}")
         g = run_gpu(x, 3000, options=q.Options(tier=tier))
         check(x, g, ref, 3000, f"counted rows tier {tier} B {B} call {call}")
+
+
+@pytest.mark.parametrize("launches", [1, 2])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+def test_one_and_two_launches_all_kinds(launches, dtype):
+    """One launch (each row's tail workgroup streams the row itself) and two
+    launches (the streaming pass over (row, slice) workgroups, then the tail)
+    on every kind of row, against the oracle."""
+    import top_selection_sigma_amd as q
+
+    for i, kind in enumerate(KINDS):
+        x = w.make_rows(6, 7001, dtype, kind, seed=1300 + i)
+        _say(f"launches {launches} {kind} {dtype}")
+        g = run_gpu(x, 400, options=q.Options(launches=launches))
+        check(x, g, oracle_for(x, 400), 400, f"launches {launches} {kind} {dtype}")
+
+
+@pytest.mark.parametrize("case", ["bitmap", "misses", "overflow", "long_rows"])
+def test_one_launch_paths(case):
+    """One launch through the tail's other paths: whole-row bitmap masks (512
+    rows), forced truncation misses (re-collection and full-row search), a
+    list too small for the candidates, and rows long enough for several tiles
+    per thread with a ragged end."""
+    import top_selection_sigma_amd as q
+
+    if case == "bitmap":
+        x = w.make_rows(512, 3001, "bf16", "gauss_outliers", seed=77)
+        opts = q.Options(launches=1)
+    elif case == "misses":
+        x = w.make_rows(24, 20000, "bf16", "gauss_outliers", seed=78)
+        opts = q.Options(launches=1, force_miss=True)
+    elif case == "overflow":
+        x = w.make_rows(24, 20000, "f32", "ties16", seed=79)
+        opts = q.Options(launches=1, list_cap=64)
+    else:
+        x = w.make_rows(8, 262144 + 37, "bf16", "heavy", seed=80)
+        opts = q.Options(launches=1)
+    ref = oracle_for(x, 300)
+    _say(f"one launch {case}")
+    g = run_gpu(x, 300, options=opts)
+    check(x, g, ref, 300, f"one launch {case}")

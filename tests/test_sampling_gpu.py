@@ -87,16 +87,17 @@ KINDS = ["gauss", "gauss_outliers", "ties16", "uniform", "heavy", "equal", "twol
          "allneginf", "zeros", "spike", "flat"]
 
 
-@pytest.mark.parametrize("search", [0, 1])
+@pytest.mark.parametrize("search,launches", [(0, 1), (1, 1), (0, 2)])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_sample_all_kinds_mixed_controls(dtype, search):
+def test_sample_all_kinds_mixed_controls(dtype, search, launches):
     import top_selection_sigma_amd as q
 
     for i, kind in enumerate(KINDS):
         x = w.make_rows(24, 6007, dtype, kind, seed=300 + i)
-        _say(f"sample {kind} {dtype} search {search}")
-        got = run_sample(x, 6007, seed=1000 + i, offset=i, options=q.Options(pivot_search_only=search))
-        check_sample(x, 6007, 1000 + i, i, got, f"sample {kind} {dtype} search {search}")
+        _say(f"sample {kind} {dtype} search {search} launches {launches}")
+        got = run_sample(x, 6007, seed=1000 + i, offset=i,
+                         options=q.Options(pivot_search_only=search, launches=launches))
+        check_sample(x, 6007, 1000 + i, i, got, f"sample {kind} {dtype} search {search} launches {launches}")
 
 
 @pytest.mark.parametrize("search", [0, 1])

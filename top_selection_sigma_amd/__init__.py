@@ -56,6 +56,7 @@ class _Options(ctypes.Structure):
         ("idx_order", ctypes.c_int32),
         ("chunks", ctypes.c_int32),
         ("pivot_search_only", ctypes.c_int32),
+        ("launches", ctypes.c_int32),
     ]
 
 
@@ -76,13 +77,15 @@ class Options:
     idx_order: int = 0        # 0 rank order, 1 ascending vocabulary index
     chunks: int = 0           # 0 automatic, 1 no overlap, n row chunks overlapping tail and pass 1
     pivot_search_only: int = 0  # 1: no sort-and-scan path for small candidate sets
+    launches: int = 0         # 0 automatic (two), 1 one launch (the tail streams its row), 2 two launches
 
     def to_c(self) -> _Options:
         return _Options(int(self.force_miss), float(self.delta_scale), int(self.pivot_mode),
                         int(self.slices), int(self.lds_cap), int(self.list_cap),
                         None if self.diag is None else self.diag.data_ptr(),
                         None if self.mid_event is None else self.mid_event.cuda_event,
-                        int(self.tier), int(self.mask_mode), int(self.idx_order), int(self.chunks), int(self.pivot_search_only))
+                        int(self.tier), int(self.mask_mode), int(self.idx_order), int(self.chunks), int(self.pivot_search_only),
+                        int(self.launches))
 
 
 def lib() -> ctypes.CDLL:

@@ -40,6 +40,7 @@ struct Params {
     int64_t row0;        // batch row of this launch's row 0 (the draw's counter uses batch rows)
     int32_t small_max;   // rows with at most this many candidates take the sort-and-scan path (0: none)
     uint32_t* queue;     // tail row counter (null: workgroup g takes row g)
+    int32_t fused;       // 1: one launch, the tail streams each row itself (pass 1 with one slice)
 };
 
 // Records that pass 1 leaves for the tail. Every word is written by plain

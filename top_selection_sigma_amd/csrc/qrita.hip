@@ -52,6 +52,7 @@ struct Plan {
     int sub_cap;     // list entries per slice
     bool bitmap;     // the tail writes whole mask rows
     int chunks;      // row chunks whose tails overlap the next chunk's streaming pass
+    bool one_launch; // no pass-1 launch: the tail streams each row (one slice per row)
 };
 
 bool dtype_ok(int d) { return d == QRITA_F32 || d == QRITA_BF16 || d == QRITA_F16; }
@@ -83,12 +84,16 @@ Plan choose_plan(int64_t B, int64_t V, int64_t esize, int64_t idx_cap, const qri
     S = std::min<int64_t>(S, qrita::kMaxSlices);
     S = std::min<int64_t>(S, std::max<int64_t>(1, (V + 8191) / 8192));
     if (o && o->slices > 0) S = std::min<int64_t>(std::min<int64_t>(o->slices, qrita::kMaxSlices), std::max<int64_t>(1, V));
+    // on request, one launch: each row's tail workgroup streams its whole
+    // row (measured slower than two launches at every shape: ablation leg)
+    t.one_launch = o && o->launches == 1;
+    if (t.one_launch) S = 1;
     // slices are whole tiles of 16 logits per thread (only a row's last slice
     // ends in a part tile), and after the first they start 16-aligned
     const int64_t TB = (int64_t)kPass1Threads * 16;
     int64_t L = (V + S - 1) / S;
     L = ((L + TB - 1) / TB) * TB;
-    if (o && o->slices > 0) L = ((((V + S - 1) / S) + 15) / 16) * 16;
+    if (o && o->slices > 0 && !t.one_launch) L = ((((V + S - 1) / S) + 15) / 16) * 16;
     S = (V + L - 1) / L;
     t.slices = (int)S;
     t.slice_len = (int)L;
@@ -115,7 +120,7 @@ Plan choose_plan(int64_t B, int64_t V, int64_t esize, int64_t idx_cap, const qri
     int ch = 1;  // measured: overlapping on two streams was slower at every shape (ablation leg)
     if (o && o->chunks > 0) ch = o->chunks;
     ch = (int)std::min<int64_t>(ch, std::max<int64_t>(1, B / 8));
-    t.chunks = std::min(ch, kMaxChunks);
+    t.chunks = t.one_launch ? 1 : std::min(ch, kMaxChunks);
     return t;
 }
 
@@ -176,7 +181,8 @@ bool options_valid(const qrita_options* opt) {
                      opt->slices < 0 || opt->lds_cap < 0 || opt->list_cap < 0 || opt->tier < 0 ||
                      opt->tier > 2 || opt->mask_mode < 0 || opt->mask_mode > 1 || opt->idx_order < 0 ||
                      opt->idx_order > 1 || opt->chunks < 0 || opt->chunks > kMaxChunks ||
-                     opt->pivot_search_only < 0 || opt->pivot_search_only > 1 ||
+                     opt->pivot_search_only < 0 || opt->pivot_search_only > 1 || opt->launches < 0 ||
+                     opt->launches > 2 ||
                      !(opt->delta_scale == opt->delta_scale));
 }
 
@@ -244,6 +250,7 @@ int select_impl(const void* logits, int64_t batch, int64_t vocab, int dtype, con
     P.slrec = (uint32_t*)((char*)workspace + w.slrec);
     P.glist = (uint64_t*)((char*)workspace + w.lists);
     P.queue = nullptr;
+    P.fused = t.one_launch ? 1 : 0;
     P.diag = opt ? opt->diag : nullptr;
     P.batch = batch;
     P.vocab = (int32_t)vocab;
@@ -287,6 +294,12 @@ int select_impl(const void* logits, int64_t batch, int64_t vocab, int dtype, con
         int dev = 0;
         if (hipGetDevice(&dev) != hipSuccess) return QRITA_ELAUNCH;
         sd = side_for(dev);  // no second stream: one chunk
+    }
+    if (!sd && t.one_launch) {
+        if (opt && opt->mid_event) {  // no streaming pass: the whole call is the tail
+            if (hipEventRecord((hipEvent_t)opt->mid_event, s) != hipSuccess) return QRITA_ELAUNCH;
+        }
+        return tail(P, s) == hipSuccess ? QRITA_OK : QRITA_ELAUNCH;
     }
     if (!sd) {
         // rows for more than one and at most two rounds of the tail

@@ -674,16 +674,11 @@ QRITA_DEV void stream_slice(const Params& P, int64_t row, uint64_t* sub, int64_t
 // the next launch, on the same XCD, unless rows are counted out) reads it. A
 // slice writes only its own sub-list and record: no global atomics, no state
 // carried between calls. Workgroup 0 also zeroes the tail's row counter.
+//
+// pass1_slice is the work of one (row, slice); the tail's one-launch path
+// runs it for a whole row (one slice) before the row's selection.
 template <int THREADS, int DT>
-__global__ __launch_bounds__(THREADS, 4) void pass1_kernel(Params P) {
-    __shared__ Shared sh;
-    int rb = 0;
-    const uint32_t g = blockIdx.x;
-    if (P.queue && g == 0 && threadIdx.x == 0) *P.queue = 0u;
-    const uint32_t xcd = g & 7u, jj = g >> 3;
-    const uint32_t rloc = jj / (uint32_t)P.slices, slice = jj % (uint32_t)P.slices;
-    const int64_t row = (int64_t)rloc * 8 + xcd;
-    if (row >= P.batch) return;
+QRITA_DEV void pass1_slice(const Params& P, int64_t row, uint32_t slice, Shared& sh, int& rb) {
     const int32_t V = P.vocab;
     const int64_t roff = row * (int64_t)V;
     const void* rowp = row_ptr<DT>(P, row);
@@ -782,6 +777,19 @@ __global__ __launch_bounds__(THREADS, 4) void pass1_kernel(Params P) {
     if (threadIdx.x == 0)
         *(uint4*)(P.slrec + (row * kMaxSlices + slice) * S_WORDS) =
             make_uint4(gb + nst + wtot, kmax, (uint32_t)rest, (uint32_t)(rest >> 32));
+}
+
+template <int THREADS, int DT>
+__global__ __launch_bounds__(THREADS, 4) void pass1_kernel(Params P) {
+    __shared__ Shared sh;
+    int rb = 0;
+    const uint32_t g = blockIdx.x;
+    if (P.queue && g == 0 && threadIdx.x == 0) *P.queue = 0u;
+    const uint32_t xcd = g & 7u, jj = g >> 3;
+    const uint32_t rloc = jj / (uint32_t)P.slices, slice = jj % (uint32_t)P.slices;
+    const int64_t row = (int64_t)rloc * 8 + xcd;
+    if (row >= P.batch) return;
+    pass1_slice<THREADS, DT>(P, row, slice, sh, rb);
 }
 
 // Re-collect the row's candidates >= tr into the per-row list (full-row

@@ -2162,6 +2162,19 @@ __global__ __launch_bounds__(T::NT, T::WAVES_PER_SIMD) void tail_kernel(Params P
         row = uni(sh.row);
     }
     if (row >= P.batch) return;
+    if (P.fused) {
+        // one launch: this workgroup first streams the whole row as pass 1's
+        // only slice, leaving the row and slice records and the list that
+        // the rest reads back
+        if (P.dtype == 1)
+            pass1_slice<NT, 1>(P, row, 0u, sh, rb);
+        else if (P.dtype == 2)
+            pass1_slice<NT, 2>(P, row, 0u, sh, rb);
+        else
+            pass1_slice<NT, 0>(P, row, 0u, sh, rb);
+        __threadfence_block();
+        __syncthreads();
+    }
     const int32_t V = P.vocab;
     const uint32_t S = (uint32_t)P.slices;
     const RowMode md = row_mode(P, row);
