@@ -417,9 +417,16 @@ QRITA_DEV void wave_spill_flush(const Params& P, uint64_t* sub, const uint64_t* 
     }
 }
 
+// The candidate stage holds kSampleN entries as two arrays of words: the
+// logits' bits, then their vocabulary indices (a survivor is two 32-bit
+// writes at one address and a fixed offset).
+constexpr uint32_t kStageN = kSampleN;
+
 // Compact the survivors (f >= tc) of 16 logits per lane into the candidate
 // stage: wavefront ballots count them, one LDS atomic per wave reserves
-// space, mbcnt gives each lane its slot. Logit j of this lane has vocabulary
+// space, mbcnt gives each lane its slot. The lane masks come straight from
+// the comparisons (one per logit and lane, in scalar registers), so the
+// wave-uniform tests are scalar. Logit j of this lane has vocabulary
 // index idx0 + (j / VE) * vstride + (j % VE); bit j of `valid` marks it as
 // present. Survivors past the stage go to the wave's spill buffer (with their
 // key, for the list's max). For top-p-only rows (REST) the dropped logits'
@@ -431,12 +438,14 @@ QRITA_DEV void consume16(const Params& P, uint64_t* sub, const float f[16], uint
     const uint32_t lane = threadIdx.x & (kWave - 1);
     uint32_t tot = 0;
     float dropped = 0.0f;
+    // the survivors of logit j of every lane: wave-uniform (every lane takes
+    // both masks; valid differs by lane), in scalar registers
+    auto mask = [&](int j) { return __builtin_amdgcn_fcmpf(f[j], tc, 3) & __ballot((valid >> j) & 1u); };
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
         const bool v = (valid >> j) & 1u;
-        const bool s = v && f[j] >= tc;
-        tot += (uint32_t)__popcll(__ballot(s));
-        if (REST) dropped += (v && !s) ? __expf(f[j] - tc) : 0.0f;
+        tot += (uint32_t)__popcll(mask(j));
+        if (REST) dropped += (v && !(f[j] >= tc)) ? __expf(f[j] - tc) : 0.0f;
     }
     if (REST) rest += fx_from_unit_f32(fminf(dropped * 0x1p-5f, 1.0f)) << 5;
     if (tot == 0) return;
@@ -444,18 +453,19 @@ QRITA_DEV void consume16(const Params& P, uint64_t* sub, const float f[16], uint
     if (lane == 0) base = atomicAdd(&sh.ncand, tot);
     base = readlane(base, 0);
     const uint32_t cap = (uint32_t)P.stage_cap;
-    uint64_t* a = lds_cands();
+    uint32_t* a = (uint32_t*)lds_cands();
     uint32_t run = base;
     if (base + tot <= cap) {
         // the whole group fits the stage
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-            const bool s = ((valid >> j) & 1u) && f[j] >= tc;
-            const uint64_t b = __ballot(s);
+            const uint64_t b = mask(j);
             if (b) {
-                if (s)
-                    a[run + lanes_below(b)] = ((uint64_t)__float_as_uint(f[j]) << 32) |
-                                              (idx0 + (uint32_t)(j / VE) * vstride + (uint32_t)(j % VE));
+                if (((valid >> j) & 1u) && f[j] >= tc) {
+                    const uint32_t pos = run + lanes_below(b);
+                    a[pos] = __float_as_uint(f[j]);
+                    a[kStageN + pos] = idx0 + (uint32_t)(j / VE) * vstride + (uint32_t)(j % VE);
+                }
                 run += (uint32_t)__popcll(b);
             }
         }
@@ -476,15 +486,15 @@ QRITA_DEV void consume16(const Params& P, uint64_t* sub, const float f[16], uint
     }
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-        const bool s = ((valid >> j) & 1u) && f[j] >= tc;
-        const uint64_t b = __ballot(s);
+        const uint64_t b = mask(j);
         if (b) {
-            if (s) {
+            if (((valid >> j) & 1u) && f[j] >= tc) {
                 const uint32_t pos = run + lanes_below(b);
                 const uint32_t bits = __float_as_uint(f[j]);
                 const uint32_t idx = idx0 + (uint32_t)(j / VE) * vstride + (uint32_t)(j % VE);
                 if (pos < cap) {
-                    a[pos] = ((uint64_t)bits << 32) | idx;
+                    a[pos] = bits;
+                    a[kStageN + pos] = idx;
                 } else {
                     const uint32_t off = pos - spill_from;
                     const uint32_t key = f32_key(bits);
@@ -745,15 +755,14 @@ QRITA_DEV void pass1_slice(const Params& P, int64_t row, uint32_t slice, Shared&
     uint32_t kmax = sp.kmax;
     uint32_t gb = 0;
     if (threadIdx.x == 0) gb = atomicAdd(&sh.nsub, nst + wtot);
-    constexpr int PER = kSampleN / THREADS;  // stage entries per thread (stage_cap <= 2048)
-    const uint64_t* a = lds_cands();
+    constexpr int PER = kStageN / THREADS;  // stage entries per thread (stage_cap <= kStageN)
+    const uint32_t* a = (const uint32_t*)lds_cands();
     uint32_t keys[PER], lows[PER];
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
         const uint32_t i = (uint32_t)u * THREADS + threadIdx.x;
-        const uint64_t r = i < nst ? a[i] : 0ull;
-        keys[u] = i < nst ? f32_key((uint32_t)(r >> 32)) : 0u;
-        lows[u] = ~(uint32_t)r;
+        keys[u] = i < nst ? f32_key(a[i]) : 0u;
+        lows[u] = ~(i < nst ? a[kStageN + i] : 0u);
         kmax = keys[u] > kmax ? keys[u] : kmax;
     }
     if (threadIdx.x == 0) sh.u32[0] = gb;
