@@ -82,3 +82,17 @@ def test_noalloc_rejects_shapes_beyond_its_scratch():
     with pytest.raises(q.QritaError) as e:
         q.qrita_select_noalloc(logits, None, None, None, None, count, 0)
     assert e.value.status == q.QRITA_ESCRATCH
+
+
+def test_noalloc_matches_select_with_counted_tail_rows():
+    """700 rows take their tail rows from the counter in the scratch (zeroed by
+    pass 1 in the same call); then a smaller call on the same scratch."""
+    cases = [
+        (w.make_rows(700, 3001, "bf16", "gauss_outliers", seed=503), 200, "700 x 3001 bf16"),
+        (w.make_rows(20, 3001, "bf16", "ties16", seed=504), 200, "20 x 3001 bf16"),
+    ]
+    for x, cap, label in cases:
+        print(f"noalloc case {label}", flush=True)
+        ref = _call(x, cap, noalloc=False)
+        got = _call(x, cap, noalloc=True)
+        _same(ref, got, cap, label)
