@@ -127,19 +127,19 @@ Plan choose_plan(int64_t B, int64_t V, int64_t esize, int64_t idx_cap, const qri
 // gfx950 check, once per device (kernels built for gfx950 cannot run elsewhere).
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_arch[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
-std::atomic<int> g_cus[kMaxDevices];   // compute units (valid once g_arch is)
+std::atomic<int> g_cus[kMaxDevices];   // compute units (published before g_arch)
 
 bool device_supported() {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) return false;
     if (dev >= kMaxDevices) return false;
-    int s = g_arch[dev].load(std::memory_order_relaxed);
+    int s = g_arch[dev].load(std::memory_order_acquire);
     if (s == 0) {
         hipDeviceProp_t prop;
         if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return false;
         s = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
         g_cus[dev].store(prop.multiProcessorCount, std::memory_order_relaxed);
-        g_arch[dev].store(s, std::memory_order_relaxed);
+        g_arch[dev].store(s, std::memory_order_release);
     }
     return s == 1;
 }

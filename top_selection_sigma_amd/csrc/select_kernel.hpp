@@ -424,9 +424,9 @@ constexpr uint32_t kStageN = kSampleN;
 
 // Compact the survivors (f >= tc) of 16 logits per lane into the candidate
 // stage: wavefront ballots count them, one LDS atomic per wave reserves
-// space, mbcnt gives each lane its slot. The lane masks come straight from
-// the comparisons (one per logit and lane, in scalar registers), so the
-// wave-uniform tests are scalar. Logit j of this lane has vocabulary
+// space, mbcnt gives each lane its slot. For each of the 16 positions the
+// mask of lanes holding a survivor there comes straight from the comparison
+// (a scalar register pair), so the wave-uniform tests are scalar. Logit j of this lane has vocabulary
 // index idx0 + (j / VE) * vstride + (j % VE); bit j of `valid` marks it as
 // present. Survivors past the stage go to the wave's spill buffer (with their
 // key, for the list's max). For top-p-only rows (REST) the dropped logits'

@@ -2148,8 +2148,9 @@ QRITA_DEV TailOut tail_fallback(const Params& P, int64_t row, RowMode md, float 
 // which can put the expensive rows of a periodic pattern (a per-row k that
 // cycles) on the same XCDs; the rows of the second round then also go to
 // whichever workgroups start first. The grid has one workgroup per row, so
-// each takes one ticket below the row count. The row's sub-lists are loaded into LDS when they fit
-// and did not overflow; everything else takes tail_fallback.
+// each takes one ticket below the row count. The row's sub-lists are loaded
+// into LDS when they fit and did not overflow; everything else takes
+// tail_fallback.
 template <class T>
 __global__ __launch_bounds__(T::NT, T::WAVES_PER_SIMD) void tail_kernel(Params P) {
     constexpr int NT = T::NT;
