@@ -180,3 +180,16 @@ def test_sample_duplicate_heavy_rows_draw_lowest_kept_duplicates():
     token, idx, prob = got[0], got[1], got[2]
     assert np.all(token % 7 == 0) and np.all(token < 7 * 100)
     np.testing.assert_allclose(prob[:, :100], 0.01, rtol=1e-6)
+
+
+@pytest.mark.parametrize("tier,B", [(1, 700), (2, 400)])
+def test_sample_counted_tail_rows(tier, B):
+    """Batches whose tail workgroups take their rows from the counter: each
+    row's draw uses the uniform of its own batch row, whichever workgroup
+    handles it."""
+    import top_selection_sigma_amd as q
+
+    x = w.make_rows(B, 2003, "bf16", "gauss_outliers", seed=600 + tier)
+    _say(f"counted rows sample tier {tier} B {B}")
+    got = run_sample(x, 2003, seed=11, offset=4, options=q.Options(tier=tier))
+    check_sample(x, 2003, 11, 4, got, f"counted rows sample tier {tier} B {B}")
